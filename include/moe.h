@@ -1,0 +1,249 @@
+/*
+ * moe.h: C ABI of the MI355X (gfx950) top-k Mixture-of-Experts layer forward.
+ *
+ * The library computes, on one GPU with every expert resident, the forward pass of a
+ * top-k MoE FFN layer: fp32 router logits, softmax, top-k selection with gate
+ * renormalisation modes, the per-expert load histogram and capacity slots, the
+ * permutation of tokens into expert-contiguous buffers, the gated expert FFN as two
+ * grouped GEMMs, and the gate-weighted combine back to token order.
+ *
+ * Sources (the pages the method is taken from; cited below by their short key):
+ *   [GROK5]  "第 5 章 model.py 精读·中：MoE 路由与专家" (Grok-1 中文精读, chapter 5),
+ *            https://yingwang.github.io/grok-1/05-model-2/
+ *   [BOOK12] "第 12 章 MoE：路由、专家与负载" (LLMs from scratch, chapter 12),
+ *            https://book.ozine.me/llm/llms-from-scratch/chapters/12_moe.html
+ *   [SERIES] "8.1 MoE 系列：从 GShard 到 Mixtral，再到 Switch Transformer",
+ *            https://gitcode.csdn.net/69b8cfc40a2f6a37c5980bb1.html
+ *   [GROKIX] "Grok-1 中文精读" (book index page), https://yingwang.github.io/grok-1/
+ *   [F2C]    "MoE 公式到源码对照",
+ *            https://jerryiiii.gitbook.io/llm-review/notes/distributed/moe-formula-to-code-walkthrough
+ *
+ * Conventions shared by every entry point
+ *  - Tensor arguments are DEVICE pointers to caller-owned memory, row-major, densely
+ *    packed, 16-byte aligned. The library never frees, retains or allocates them.
+ *  - `desc` is a HOST pointer; it is read during the call only.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream). Every compute
+ *    entry point only enqueues work on that stream and returns; none allocates memory
+ *    or synchronises, except moe_read_stats, which synchronises the stream.
+ *  - Every call validates all sizes and pointers on the host BEFORE enqueuing anything;
+ *    on an error nothing is launched and the outputs are untouched.
+ *  - Index work (selection, histogram, slots, drop mask) is deterministic and exact.
+ *    Floating-point reductions run in a fixed order, so results are bit-identical
+ *    from run to run. No kernel uses global atomics.
+ *  - Inputs must be finite; behaviour on NaN/Inf inputs is unspecified.
+ *  - The layer returns the FFN increment only; the residual add belongs to the caller
+ *    ([SERIES] §2.2 case B: a token that overflows every expert gets increment 0).
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes --------------------------------------------------------------- */
+enum {
+  MOE_OK = 0,
+  MOE_E_INVAL = -1,       /* invalid size, enum, or NULL/misaligned required pointer   */
+  MOE_E_UNSUPPORTED = -2, /* valid but outside what the kernels implement (see below)  */
+  MOE_E_WORKSPACE = -3,   /* workspace/scratch pointer NULL or smaller than required   */
+  MOE_E_HIP = -4          /* a HIP runtime call failed (launch error, no device, ...)  */
+};
+
+/* ---- enums carried in moe_desc ------------------------------------------------- */
+/* Element type of x, W1, W2, W3, h, y_perm and y. W_r, logits, probs and gates are always fp32. */
+enum { MOE_DT_F32 = 0, MOE_DT_BF16 = 1 };
+
+/* Gate rule ([GROK5] §5.2.3 "softmax 在 top-k 之前还是之后"):
+ *  SOFTMAX_TOPK: softmax over all E experts, the k selected probabilities are the gates
+ *                unnormalised (sum < 1), the Grok-1 rule.
+ *  TOPK_SOFTMAX: softmax over the k selected logits only (sum = 1), the Mixtral rule;
+ *                equal to renormalising the selected probabilities ([F2C] §1.2,
+ *                [BOOK12] §12.1). */
+enum { MOE_ROUTE_SOFTMAX_TOPK = 0, MOE_ROUTE_TOPK_SOFTMAX = 1 };
+
+/* Selection of slots 1..k-1 ([SERIES] §3, GShard random routing):
+ *  TOPK : all k slots are the k largest clean logits.
+ *  NOISY: slot 0 is the clean argmax; slot j>=1 is the argmax, over experts not yet
+ *         chosen, of fl32(logit + noise) where noise[N,E] is supplied by the caller.
+ *         Gates always use the clean probabilities. */
+enum { MOE_SECOND_TOPK = 0, MOE_SECOND_NOISY = 1 };
+
+/* Activation of the W1 branch: f_e(x) = [act(x W1_e) * (x W2_e)] W3_e
+ * ([BOOK12] §12.1 gated FFN with SiLU; [GROK5] §5.3.5 GELU(x W_g) * (x W_v), exact erf
+ * GELU, tanh form in §5.3.5.1). */
+enum { MOE_ACT_SILU = 0, MOE_ACT_GELU_ERF = 1, MOE_ACT_GELU_TANH = 2 };
+
+/* Expert buffer layout and capacity:
+ *  NONE  : ragged expert-sorted rows, no capacity limit, nothing dropped; rows = N*k.
+ *  PADDED: zero-padded [E, C, D] buffers with capacity C ([SERIES] §2.1, §2.3);
+ *          rows = E*C; records beyond C are dropped ([F2C] §3.2). */
+enum { MOE_CAP_NONE = 0, MOE_CAP_PADDED = 1 };
+
+typedef struct moe_desc {
+  int64_t N;              /* tokens (B*T flattened, [BOOK12] §12.2)                      */
+  int64_t D;              /* model width                                                 */
+  int64_t F;              /* expert FFN width                                            */
+  int32_t E;              /* experts                                                     */
+  int32_t k;              /* experts selected per token                                  */
+  int32_t dtype;          /* MOE_DT_*                                                    */
+  int32_t routing_mode;   /* MOE_ROUTE_*                                                 */
+  int32_t second_choice;  /* MOE_SECOND_*                                                */
+  int32_t activation;     /* MOE_ACT_*                                                   */
+  int32_t capacity_mode;  /* MOE_CAP_*                                                   */
+  int32_t min_capacity;   /* PADDED: lower bound on C (>= 0)                             */
+  double capacity_factor; /* PADDED: CF > 0                                              */
+} moe_desc;
+
+/* Limits of this implementation (MOE_E_UNSUPPORTED beyond them, MOE_E_INVAL below 1):
+ *   1 <= E <= 64, 1 <= k <= min(E, 8), D and F multiples of 128,
+ *   N*k, E*C and every row index fit in int32. */
+
+/* Statistics of the last route+dispatch that used a given scratch buffer. */
+typedef struct moe_stats {
+  int64_t routed_slots;    /* N*k dispatch records ([BOOK12] §12.2)                      */
+  int64_t dropped_slots;   /* records over capacity ([F2C] §3.3 numerator)               */
+  int64_t dropped_tokens;  /* tokens with every slot dropped ([SERIES] §2.2 case B)      */
+  int64_t capacity;        /* C used by the dispatch (N when capacity_mode is NONE)      */
+  double drop_rate;        /* dropped_slots / (N*k), slot level ([F2C] §3.3)              */
+  double token_drop_rate;  /* dropped_tokens / N                                         */
+  double balance_loss;     /* E * sum_e f_e P_e, f_e = load_e/(N*k), P_e = mean_t p_te    */
+  double balance_loss_div_n; /* E * sum_e (load_e/N) P_e, the ÷N form of [F2C] §2.3       */
+} moe_stats;
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* moe_status_string(int status);
+
+/* ---- host-only queries (no GPU work; safe without a device) ---------------------- */
+
+/* Expert capacity ([F2C] §3.1; [SERIES] §2.1 with min_capacity):
+ *   PADDED: C = max(ceil(CF * N * k / E), min_capacity), evaluated in double as
+ *           ceil(((CF*N)*k)/E). Worked example [SERIES] §2.1: N=8, E=4, k=2, CF=1 -> 4.
+ *   NONE  : C = N (no expert can receive more than N records, so nothing drops).
+ * Errors: MOE_E_INVAL for NULL pointers, N<1, E<1, k<1, k>E, or CF<=0 in PADDED mode
+ * (the invalid-input rule of [F2C] §3.1). */
+int moe_capacity(const moe_desc* desc, int64_t* capacity);
+
+/* Number of rows of the expert buffers x_perm/h/y_perm: N*k (NONE) or E*C (PADDED). */
+int moe_rows(const moe_desc* desc, int64_t* rows);
+
+/* Bytes of scratch used by moe_route, moe_dispatch, moe_expert_ffn and moe_read_stats
+ * (per-block partial counts and sums; O(N*k/256*E) bytes). */
+int moe_scratch_size(const moe_desc* desc, size_t* bytes);
+
+/* Bytes of workspace for moe_forward: the scratch region followed by every
+ * intermediate (topk ids/gates, slots, x_perm, h, y_perm). */
+int moe_workspace_size(const moe_desc* desc, size_t* bytes);
+
+/* Byte offsets of the intermediates inside a moe_forward workspace, so that a caller
+ * can inspect them after moe_forward returns (the workspace keeps the last call's
+ * contents). Layout of each is as in the step functions below. */
+typedef struct moe_ws_layout {
+  size_t scratch;        /* moe_scratch_size bytes                                      */
+  size_t topk_idx;       /* int32 [N,k]                                                 */
+  size_t topk_gate;      /* fp32  [N,k]                                                 */
+  size_t load;           /* int32 [E]                                                   */
+  size_t counts;         /* int32 [E]                                                   */
+  size_t offsets;        /* int32 [E+1]                                                 */
+  size_t row_of;         /* int32 [N,k]                                                 */
+  size_t dropped;        /* uint8 [N,k]                                                 */
+  size_t gate_eff;       /* fp32  [N,k]                                                 */
+  size_t token_of_row;   /* int32 [rows]                                                */
+  size_t x_perm;         /* dtype [rows,D]                                              */
+  size_t h;              /* dtype [rows,F]                                              */
+  size_t y_perm;         /* dtype [rows,D]                                              */
+  size_t total;          /* == moe_workspace_size                                       */
+} moe_ws_layout;
+int moe_workspace_layout(const moe_desc* desc, moe_ws_layout* layout);
+
+/* ---- compute entry points (asynchronous on `stream`) ----------------------------- */
+
+/* Router: steps "router linear in fp32 -> softmax -> top-k -> gates"
+ * ([GROK5] §5.2, §5.2.1, §5.2.3; [F2C] §1.1-1.2; [SERIES] §1.1, §3).
+ *   logits[t,e] = sum_d fp32(x[t,d]) * w_r[d,e] (+ logit_bias[e]), fp32 accumulation.
+ *   Selection compares fp32 logits (equal to comparing probabilities, softmax being
+ *   monotone per token); ties go to the LOWER expert index; slot 0 holds the largest.
+ *   Gates per routing_mode / second_choice (see the enums).
+ * Arguments:
+ *   x          [N,D] dtype       required unless logits_in is given (then ignored)
+ *   w_r        [D,E] fp32        required unless logits_in is given (then ignored)
+ *   logit_bias [E]   fp32        optional additive per-expert logit bias (NULL = none)
+ *   noise      [N,E] fp32        required iff second_choice == NOISY, else ignored
+ *   logits_in  [N,E] fp32        optional: route these logits and skip the GEMM
+ *   logits_out [N,E] fp32        optional output of the logits
+ *   probs_out  [N,E] fp32        optional output of softmax over all E
+ *   topk_idx   [N,k] int32       required output, expert of each slot
+ *   topk_gate  [N,k] fp32        required output, gate of each slot
+ *   scratch    moe_scratch_size  optional (NULL = skip); receives per-block partial sums
+ *                                of the probabilities for the balance statistic. */
+int moe_route(const moe_desc* desc, const void* x, const float* w_r, const float* logit_bias,
+              const float* noise, const float* logits_in, float* logits_out, float* probs_out,
+              int32_t* topk_idx, float* topk_gate, void* scratch, size_t scratch_bytes,
+              void* stream);
+
+/* Dispatch: load histogram, capacity slots, drop rule and gather
+ * ([F2C] §1.3 load, §3.1-3.2 capacity and dropped mask; [SERIES] §2.2 overflow cases,
+ *  §2.3 zero padding; [BOOK12] §12.2 expert-grouped buffers).
+ *   load[e]   = #{(t,j): topk_idx[t,j] = e}   (before capacity)
+ *   Slot positions are assigned slot-major: every slot-0 record (tokens ascending)
+ *   before every slot-1 record, and so on; a record is kept iff its position < C.
+ *   counts[e] = min(load[e], C) rows filled; offsets[e] = first row of expert e
+ *   (NONE: exclusive scan of counts; PADDED: e*C); offsets[E] = rows.
+ *   row_of[t,j] = row of the record, or -1 if dropped; dropped[t,j] = 1 if dropped.
+ *   gate_eff: all slots kept -> the gates; none kept -> 0; otherwise each kept slot
+ *   gets g_j * (sum of all gates) / (sum of kept gates) and dropped slots 0 (for two
+ *   renormalised gates with the 2nd dropped this is (1,0), [SERIES] §2.2 case A).
+ *   token_of_row[r] = token of row r, -1 for padding rows.
+ *   x_perm[r,:] = x[token_of_row[r],:], zero for padding rows.
+ * Arguments: x [N,D] dtype; topk_idx, topk_gate as produced by moe_route; outputs
+ *   load [E], counts [E], offsets [E+1] int32; row_of [N,k] int32; dropped [N,k] uint8;
+ *   gate_eff [N,k] fp32; token_of_row [rows] int32; x_perm [rows,D] dtype.
+ *   scratch (moe_scratch_size bytes) is required. Every pointer is required.
+ *   topk_idx entries must lie in [0,E) and be distinct per token (as moe_route makes). */
+int moe_dispatch(const moe_desc* desc, const void* x, const int32_t* topk_idx,
+                 const float* topk_gate, int32_t* load, int32_t* counts, int32_t* offsets,
+                 int32_t* row_of, uint8_t* dropped, float* gate_eff, int32_t* token_of_row,
+                 void* x_perm, void* scratch, size_t scratch_bytes, void* stream);
+
+/* Expert FFN as two grouped GEMMs over the expert buffers ([BOOK12] §12.1 gated FFN;
+ * [GROK5] §5.3.5):
+ *   h[r,:]      = act(x_perm[r,:] W1_e) * (x_perm[r,:] W2_e)      (stored in dtype)
+ *   y_perm[r,:] = h[r,:] W3_e
+ * for every row r in [offsets[e], offsets[e] + counts[e]). Rows outside those ranges
+ * (padding rows of the PADDED layout) are left unspecified.
+ * Arguments: x_perm [rows,D], w1 and w2 [E,D,F], w3 [E,F,D], h [rows,F], y_perm [rows,D],
+ *   all dtype; offsets [E+1], counts [E] int32 as produced by moe_dispatch.
+ *   scratch (moe_scratch_size bytes) is required. Accumulation is fp32. */
+int moe_expert_ffn(const moe_desc* desc, const void* x_perm, const int32_t* offsets,
+                   const int32_t* counts, const void* w1, const void* w2, const void* w3,
+                   void* h, void* y_perm, void* scratch, size_t scratch_bytes, void* stream);
+
+/* Combine ([GROK5] §5.3.5 gate-weighted sum, §5.8; [BOOK12] §12.2 accumulate, not
+ * overwrite): y[t,:] = sum over kept slots j, in slot order, of
+ * gate_eff[t,j] * y_perm[row_of[t,j],:], accumulated in fp32 and rounded once to dtype;
+ * exactly 0 for a token with every slot dropped.
+ * Arguments: y_perm [rows,D] dtype; row_of [N,k] int32; gate_eff [N,k] fp32; y [N,D]. */
+int moe_combine(const moe_desc* desc, const void* y_perm, const int32_t* row_of,
+                const float* gate_eff, void* y, void* stream);
+
+/* The whole layer: moe_route -> moe_dispatch -> moe_expert_ffn -> moe_combine with every
+ * intermediate in `workspace` (moe_workspace_size bytes, laid out as
+ * moe_workspace_layout reports). Arguments as in the step functions; y [N,D] dtype. */
+int moe_forward(const moe_desc* desc, const void* x, const float* w_r, const float* logit_bias,
+                const float* noise, const void* w1, const void* w2, const void* w3, void* y,
+                void* workspace, size_t workspace_bytes, void* stream);
+
+/* Reduces the statistics left in `scratch` (or in a moe_forward workspace, whose first
+ * moe_scratch_size bytes are the scratch) by the last moe_route + moe_dispatch on it,
+ * copies them to *out and SYNCHRONISES `stream`. balance_loss fields are 0 if moe_route
+ * ran without scratch. */
+int moe_read_stats(const moe_desc* desc, const void* scratch, size_t scratch_bytes,
+                   moe_stats* out, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_MI355X_H */

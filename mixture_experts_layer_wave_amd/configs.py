@@ -1,0 +1,89 @@
+"""The five synthetic MoE-layer workloads (shapes, dtypes, routing options, distributions).
+
+Pure data: no arithmetic of the method. Distributions follow one convention per
+symbol: "var" is a variance (std = sqrt(var)), "std" is a standard deviation.
+
+Shapes come from the pages: Mixtral-shaped D=4096, F=14336, E=8, k=2; Grok-1-shaped
+D=6144, F=32768, E=8, k=2 ("Grok-1 中文精读" index page, writing conventions; chapter 5
+§5.2.1 router shape [6144, 8]); GShard capacity routing with a noisy second choice and
+zero-padded buffers ("8.1 MoE 系列" §2-§3).
+"""
+from __future__ import annotations
+
+import copy
+
+# Keys of one workload:
+#   N, D, F, E, k         sizes
+#   dtype                 "f32" | "bf16" (x, W1..W3, h, y); router and gates are fp32
+#   routing_mode          "softmax_topk" (Grok-1, unnormalised) | "topk_softmax" (Mixtral)
+#   second_choice         "topk" | "noisy" (GShard random routing of slots >= 1)
+#   activation            "silu" | "gelu_erf" | "gelu_tanh"
+#   capacity_mode         "none" (ragged, no drops) | "padded" ([E,C,D], drops)
+#   capacity_factor, min_capacity
+#   x_std, wr_var, w_std (W1,W2), w3_std   input distributions (zero mean normal)
+#   zipf_s, zipf_beta     per-expert logit bias -beta*s*ln(rank), ranks a seeded
+#                         permutation of 1..E (None = no bias)
+#   noise_std             std of the GShard noise [N,E] (None = no noise)
+#   seed                  generator seed
+
+CONFIGS = {
+    "tiny_fp32": dict(
+        N=64, D=128, F=256, E=4, k=2, dtype="f32",
+        routing_mode="topk_softmax", second_choice="topk", activation="silu",
+        capacity_mode="none", capacity_factor=0.0, min_capacity=0,
+        x_std=1.0, wr_var=1.0 / 128, w_std=(1.0 / 128) ** 0.5, w3_std=(1.0 / 256) ** 0.5,
+        zipf_s=None, zipf_beta=None, noise_std=None, seed=1001,
+    ),
+    "mixtral_prefill": dict(
+        N=4096, D=4096, F=14336, E=8, k=2, dtype="bf16",
+        routing_mode="topk_softmax", second_choice="topk", activation="silu",
+        capacity_mode="none", capacity_factor=0.0, min_capacity=0,
+        x_std=1.0, wr_var=1.0 / 4096, w_std=0.02, w3_std=0.02,
+        zipf_s=None, zipf_beta=None, noise_std=None, seed=1002,
+    ),
+    "grok1_layer": dict(
+        N=8192, D=6144, F=32768, E=8, k=2, dtype="bf16",
+        routing_mode="softmax_topk", second_choice="topk", activation="gelu_erf",
+        capacity_mode="none", capacity_factor=0.0, min_capacity=0,
+        x_std=1.0, wr_var=1.0 / 6144, w_std=0.02, w3_std=0.02,
+        zipf_s=None, zipf_beta=None, noise_std=None, seed=1003,
+    ),
+    "mixtral_decode": dict(
+        N=64, D=4096, F=14336, E=8, k=2, dtype="bf16",
+        routing_mode="topk_softmax", second_choice="topk", activation="silu",
+        capacity_mode="none", capacity_factor=0.0, min_capacity=0,
+        x_std=1.0, wr_var=1.0 / 4096, w_std=0.02, w3_std=0.02,
+        zipf_s=1.0, zipf_beta=4.0, noise_std=None, seed=1004,
+    ),
+    "gshard_capacity": dict(
+        N=16384, D=2048, F=8192, E=64, k=2, dtype="bf16",
+        routing_mode="topk_softmax", second_choice="noisy", activation="silu",
+        capacity_mode="padded", capacity_factor=1.25, min_capacity=4,
+        x_std=1.0, wr_var=1.0 / 2048, w_std=0.02, w3_std=0.02,
+        zipf_s=1.2, zipf_beta=1.0, noise_std=1.0, seed=1005,
+    ),
+}
+
+# Order of the workloads as they are numbered in the documentation (1..5).
+ORDER = ["tiny_fp32", "mixtral_prefill", "grok1_layer", "mixtral_decode", "gshard_capacity"]
+
+
+def get_config(name: str, **overrides) -> dict:
+    """A copy of a named workload, with any field overridden (e.g. a smaller N)."""
+    cfg = copy.deepcopy(CONFIGS[name])
+    cfg.update(overrides)
+    cfg["name"] = overrides.get("name", name)
+    return cfg
+
+
+def scaled_config(name: str, N: int, D: int, F: int, **overrides) -> dict:
+    """The routing/dtype recipe of a named workload at smaller sizes, with the weight
+    distributions rescaled the same way (var 1/D for the router)."""
+    base = CONFIGS[name]
+    cfg = get_config(name, N=N, D=D, F=F, **overrides)
+    cfg["wr_var"] = 1.0 / D
+    if base["dtype"] == "f32":
+        cfg["w_std"] = (1.0 / D) ** 0.5
+        cfg["w3_std"] = (1.0 / F) ** 0.5
+    cfg["name"] = overrides.get("name", f"{name}@N{N}D{D}F{F}")
+    return cfg

@@ -1,0 +1,92 @@
+"""Seeded synthetic inputs for the MoE-layer workloads.
+
+This module is the one piece shared by the GPU path's callers and the oracle: it draws
+random numbers and rounds them to the stored element types, and holds none of the
+method's arithmetic. Every tensor comes from its own numpy PCG64 stream, keyed by
+(seed, tensor id[, expert]), so results do not depend on thread count or draw order.
+fp32 -> bf16 rounding is round-to-nearest-even (torch's conversion).
+"""
+from __future__ import annotations
+
+import os
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+import torch
+
+_TENSOR_ID = {"x": 1, "w_r": 2, "w1": 3, "w2": 4, "w3": 5, "rank": 6, "noise": 7, "logits": 8}
+
+
+def _rng(seed: int, name: str, sub: int = 0) -> np.random.Generator:
+    return np.random.Generator(np.random.PCG64(np.random.SeedSequence([int(seed), _TENSOR_ID[name], int(sub)])))
+
+
+def _normal(seed: int, name: str, shape, std: float, sub: int = 0) -> np.ndarray:
+    a = _rng(seed, name, sub).standard_normal(size=shape, dtype=np.float32)
+    if std != 1.0:
+        a *= np.float32(std)
+    return a
+
+
+def _store(a: np.ndarray, dtype: str) -> torch.Tensor:
+    t = torch.from_numpy(a)
+    return t.to(torch.bfloat16) if dtype == "bf16" else t
+
+
+def _threads() -> int:
+    return max(1, min(16, os.cpu_count() or 1))
+
+
+def _expert_stack(seed: int, name: str, E: int, shape, std: float, dtype: str) -> torch.Tensor:
+    out = torch.empty((E, *shape), dtype=torch.bfloat16 if dtype == "bf16" else torch.float32)
+
+    def one(e):
+        out[e].copy_(_store(_normal(seed, name, shape, std, sub=e), dtype))
+
+    with ThreadPoolExecutor(_threads()) as ex:
+        list(ex.map(one, range(E)))
+    return out
+
+
+def zipf_bias(cfg: dict) -> torch.Tensor | None:
+    """Per-expert logit bias b_e = -beta * s * ln(r_e), ranks r a seeded permutation."""
+    if cfg.get("zipf_s") is None:
+        return None
+    E = cfg["E"]
+    ranks = _rng(cfg["seed"], "rank").permutation(E) + 1
+    b = -float(cfg["zipf_beta"]) * float(cfg["zipf_s"]) * np.log(ranks.astype(np.float64))
+    return torch.from_numpy(b.astype(np.float32))
+
+
+def make_inputs(cfg: dict, weights: bool = True) -> dict:
+    """Host tensors of one workload: x, w_r, logit_bias, noise, and (if weights) w1, w2, w3."""
+    N, D, F, E = cfg["N"], cfg["D"], cfg["F"], cfg["E"]
+    s, dt = cfg["seed"], cfg["dtype"]
+    out = {"cfg": dict(cfg)}
+    out["x"] = _store(_normal(s, "x", (N, D), cfg["x_std"]), dt)
+    out["w_r"] = torch.from_numpy(_normal(s, "w_r", (D, E), float(cfg["wr_var"]) ** 0.5))
+    if weights:
+        out["w1"] = _expert_stack(s, "w1", E, (D, F), cfg["w_std"], dt)
+        out["w2"] = _expert_stack(s, "w2", E, (D, F), cfg["w_std"], dt)
+        out["w3"] = _expert_stack(s, "w3", E, (F, D), cfg["w3_std"], dt)
+    out["logit_bias"] = zipf_bias(cfg)
+    out["noise"] = (torch.from_numpy(_normal(s, "noise", (N, E), cfg["noise_std"]))
+                    if cfg.get("noise_std") is not None else None)
+    return out
+
+
+def make_logits(N: int, E: int, seed: int, std: float = 1.0, zipf_s=None, zipf_beta=None,
+                quantum: float | None = None, hot_expert: int | None = None) -> torch.Tensor:
+    """fp32 router logits drawn directly (for routing tests fed identical logits).
+
+    quantum: round logits to multiples of it, which makes exact ties frequent.
+    hot_expert: add +50 to that expert, so every token selects it first."""
+    a = _normal(seed, "logits", (N, E), std).astype(np.float64)
+    if zipf_s is not None:
+        ranks = _rng(seed, "rank").permutation(E) + 1
+        a += -float(zipf_beta) * float(zipf_s) * np.log(ranks.astype(np.float64))[None, :]
+    if quantum is not None:
+        a = np.round(a / quantum) * quantum
+    if hot_expert is not None:
+        a[:, hot_expert] += 50.0
+    return torch.from_numpy(a.astype(np.float32))

@@ -1,0 +1,267 @@
+"""ctypes front end of the fp64 CPU oracle (``moe_oracle.c``).
+
+TEST INFRASTRUCTURE ONLY (see the package docstring).
+
+Each method converts its arguments to contiguous host arrays and calls one C
+function; the C file holds every step of the arithmetic. Inputs are the exact stored
+values: fp32 arrays, or bf16 tensors passed as their raw 16-bit patterns.
+
+Sources (short keys):
+  [GROK5]  "第 5 章 model.py 精读·中：MoE 路由与专家" (yingwang.github.io/grok-1/05-model-2/)
+  [BOOK12] "第 12 章 MoE：路由、专家与负载" (book.ozine.me ... 12_moe.html)
+  [SERIES] "8.1 MoE 系列：从 GShard 到 Mixtral，再到 Switch Transformer" (gitcode.csdn.net)
+  [F2C]    "MoE 公式到源码对照" (jerryiiii.gitbook.io ... moe-formula-to-code-walkthrough)
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from dataclasses import dataclass
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ORACLE_SOURCE = os.path.join(HERE, "moe_oracle.c")
+ORACLE_LIB = os.path.join(HERE, "libmoe_oracle.so")
+
+ACT = {"silu": 0, "gelu_erf": 1, "gelu_tanh": 2}
+MODE = {"softmax_topk": 0, "topk_softmax": 1}
+
+_i64 = ctypes.c_int64
+_i32 = ctypes.c_int32
+_int = ctypes.c_int
+_dbl = ctypes.c_double
+_vp = ctypes.c_void_p
+
+
+def build_oracle(source: str = ORACLE_SOURCE, out: str = ORACLE_LIB, extra_flags=()) -> str:
+    """Compile the oracle with gcc (-O2 -fopenmp) into a shared library; returns its path."""
+    cmd = ["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c11", *extra_flags,
+           "-o", out + ".tmp", source, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(out + ".tmp", out)
+    return out
+
+
+def _ptr(a: np.ndarray | None):
+    return None if a is None else a.ctypes.data_as(_vp)
+
+
+def _host(a, dtype=None):
+    """Contiguous numpy view of a numpy array or CPU torch tensor; bf16 -> uint16 bits."""
+    if a is None:
+        return None
+    try:
+        import torch
+        if isinstance(a, torch.Tensor):
+            a = a.detach()
+            if a.device.type != "cpu":
+                raise ValueError("the oracle takes host arrays only")
+            if a.dtype == torch.bfloat16:
+                a = a.contiguous().view(torch.int16).numpy().view(np.uint16)
+            else:
+                a = a.contiguous().numpy()
+    except ImportError:  # pragma: no cover - torch is always present here
+        pass
+    a = np.ascontiguousarray(a)
+    if dtype is not None and a.dtype != dtype:
+        a = np.ascontiguousarray(a.astype(dtype))
+    return a
+
+
+def _dtype_code(a: np.ndarray) -> int:
+    if a.dtype == np.uint16:
+        return 1
+    if a.dtype == np.float32:
+        return 0
+    raise TypeError(f"oracle element type must be fp32 or bf16, got {a.dtype}")
+
+
+@dataclass
+class Routing:
+    logits: np.ndarray      # [N,E] float64 (the fp32 logits, widened)
+    probs: np.ndarray       # [N,E] float64
+    idx: np.ndarray         # [N,k] int32
+    gate: np.ndarray        # [N,k] float64
+    margin: np.ndarray      # [N]   float64
+
+
+@dataclass
+class Dispatch:
+    capacity: int           # -1 when unlimited
+    load: np.ndarray        # [E] int64
+    counts: np.ndarray      # [E] int64
+    offsets: np.ndarray     # [E+1] int64
+    row_of: np.ndarray      # [N,k] int64
+    dropped: np.ndarray     # [N,k] uint8
+    gate_eff: np.ndarray    # [N,k] float64
+
+
+class Oracle:
+    """One loaded copy of the oracle library (a path lets tests load a mutated build)."""
+
+    def __init__(self, lib_path: str = ORACLE_LIB):
+        self.path = lib_path
+        L = ctypes.CDLL(lib_path)
+        L.oracle_act.restype = _dbl
+        L.oracle_act.argtypes = [_int, _dbl]
+        L.oracle_router_logits.restype = None
+        L.oracle_router_logits.argtypes = [_i64, _i64, _i32, _int, _vp, _vp, _vp, _vp]
+        L.oracle_route.restype = _int
+        L.oracle_route.argtypes = [_i64, _i32, _i32, _int, _int, _vp, _vp, _vp, _vp, _vp, _vp]
+        L.oracle_capacity.restype = _int
+        L.oracle_capacity.argtypes = [_i64, _i32, _i32, _dbl, _i32, ctypes.POINTER(_i64)]
+        L.oracle_dispatch.restype = _int
+        L.oracle_dispatch.argtypes = [_i64, _i32, _i32, _vp, _i64, _int, _vp, _vp, _vp, _vp, _vp]
+        L.oracle_drop_rule.restype = None
+        L.oracle_drop_rule.argtypes = [_i64, _i32, _vp, _vp, _vp]
+        L.oracle_expert_ffn.restype = _int
+        L.oracle_expert_ffn.argtypes = [_i64, _i64, _int, _int, _vp, _vp, _vp, _vp, _i32, _vp]
+        L.oracle_layer_tokens.restype = _int
+        L.oracle_layer_tokens.argtypes = [_i64, _vp, _i64, _i64, _i64, _i32, _i32, _int, _int,
+                                          _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
+        L.oracle_balance.restype = None
+        L.oracle_balance.argtypes = [_i64, _i32, _i32, _vp, _vp, _vp, _vp, _vp]
+        self.lib = L
+
+    # -- activations -------------------------------------------------------------------
+    def act(self, kind: str, z: float) -> float:
+        return self.lib.oracle_act(ACT[kind], float(z))
+
+    # -- router ------------------------------------------------------------------------
+    def router_logits(self, x, w_r, bias=None) -> np.ndarray:
+        """fp64 logits x W_r (+ bias), [GROK5] §5.2.1."""
+        xh = _host(x)
+        wr = _host(w_r, np.float32)
+        b = _host(bias, np.float32)
+        N, D = xh.shape
+        E = wr.shape[1]
+        assert wr.shape[0] == D
+        out = np.empty((N, E), np.float64)
+        self.lib.oracle_router_logits(N, D, E, _dtype_code(xh), _ptr(xh), _ptr(wr), _ptr(b), _ptr(out))
+        return out
+
+    def route(self, logits, k: int, mode: str, noise=None) -> Routing:
+        """Softmax, selection and gates from logits (rounded to fp32 for the decisions)."""
+        lg = _host(logits, np.float64)
+        N, E = lg.shape
+        nz = _host(noise, np.float32)
+        idx = np.empty((N, k), np.int32)
+        gate = np.empty((N, k), np.float64)
+        probs = np.empty((N, E), np.float64)
+        margin = np.empty((N,), np.float64)
+        rc = self.lib.oracle_route(N, E, k, MODE[mode], 1 if nz is not None else 0, _ptr(lg), _ptr(nz),
+                                   _ptr(idx), _ptr(gate), _ptr(probs), _ptr(margin))
+        if rc != 0:
+            raise ValueError("oracle_route: invalid inputs")
+        l32 = lg.astype(np.float32).astype(np.float64)
+        return Routing(l32, probs, idx, gate, margin)
+
+    # -- capacity / dispatch -------------------------------------------------------------
+    def capacity(self, N: int, E: int, k: int, cf: float, min_capacity: int = 0) -> int:
+        c = _i64(0)
+        rc = self.lib.oracle_capacity(N, E, k, float(cf), int(min_capacity), ctypes.byref(c))
+        if rc != 0:
+            raise ValueError("invalid capacity inputs")
+        return c.value
+
+    def dispatch(self, idx, gate, E: int, capacity: int | None, padded: bool) -> Dispatch:
+        ih = _host(idx, np.int32)
+        gh = _host(gate, np.float64)
+        N, k = ih.shape
+        C = -1 if capacity is None else int(capacity)
+        load = np.empty(E, np.int64)
+        counts = np.empty(E, np.int64)
+        offsets = np.empty(E + 1, np.int64)
+        row_of = np.empty((N, k), np.int64)
+        dropped = np.empty((N, k), np.uint8)
+        rc = self.lib.oracle_dispatch(N, E, k, _ptr(ih), C, 1 if padded else 0, _ptr(load), _ptr(counts),
+                                      _ptr(offsets), _ptr(row_of), _ptr(dropped))
+        if rc != 0:
+            raise ValueError("oracle_dispatch: invalid inputs")
+        gate_eff = np.empty((N, k), np.float64)
+        self.lib.oracle_drop_rule(N, k, _ptr(gh), _ptr(dropped), _ptr(gate_eff))
+        return Dispatch(C, load, counts, offsets, row_of, dropped, gate_eff)
+
+    # -- experts / layer ------------------------------------------------------------------
+    def expert_ffn(self, x_row, w1, w2, w3, e: int, act: str) -> np.ndarray:
+        xr = _host(x_row, np.float64)
+        a, b, c = _host(w1), _host(w2), _host(w3)
+        E, D, F = a.shape
+        out = np.empty(D, np.float64)
+        rc = self.lib.oracle_expert_ffn(D, F, _dtype_code(a), ACT[act], _ptr(xr), _ptr(a), _ptr(b), _ptr(c),
+                                        int(e), _ptr(out))
+        if rc != 0:
+            raise ValueError("oracle_expert_ffn failed")
+        return out
+
+    def layer_tokens(self, tokens, x, w1, w2, w3, idx, dropped, gate_eff, act: str) -> np.ndarray:
+        """y rows of the listed tokens (fp64)."""
+        toks = np.ascontiguousarray(np.asarray(tokens, np.int64))
+        xh = _host(x)
+        a, b, c = _host(w1), _host(w2), _host(w3)
+        ih = _host(idx, np.int32)
+        dh = _host(dropped, np.uint8)
+        gh = _host(gate_eff, np.float64)
+        N, D = xh.shape
+        E, D2, F = a.shape
+        assert D2 == D and c.shape == (E, F, D)
+        k = ih.shape[1]
+        if _dtype_code(xh) != _dtype_code(a):
+            raise TypeError("x and expert weights must share one element type")
+        y = np.empty((len(toks), D), np.float64)
+        rc = self.lib.oracle_layer_tokens(len(toks), _ptr(toks), N, D, F, E, k, _dtype_code(a), ACT[act],
+                                          _ptr(xh), _ptr(a), _ptr(b), _ptr(c), _ptr(ih), _ptr(dh), _ptr(gh),
+                                          _ptr(y))
+        if rc != 0:
+            raise ValueError("oracle_layer_tokens failed")
+        return y
+
+    def balance(self, probs, load, k: int):
+        """(P[E], E*sum f P with f = load/(N k), E*sum (load/N) P)."""
+        ph = _host(probs, np.float64)
+        lh = _host(load, np.int64)
+        N, E = ph.shape
+        P = np.empty(E, np.float64)
+        b = _dbl(0.0)
+        bn = _dbl(0.0)
+        self.lib.oracle_balance(N, E, k, _ptr(ph), _ptr(lh), _ptr(P), ctypes.byref(b), ctypes.byref(bn))
+        return P, b.value, bn.value
+
+    # -- whole layer ------------------------------------------------------------------------
+    def forward(self, inputs: dict, tokens=None, logits=None):
+        """Run every step for the workload dict produced by the input generator.
+
+        Routing and dispatch cover all N tokens; the expert FFN and combine run for
+        ``tokens`` (all tokens when None). ``logits`` overrides the router GEMM (used when
+        both sides are fed the same logits). Returns a dict of every intermediate."""
+        cfg = inputs["cfg"]
+        if logits is None:
+            logits = self.router_logits(inputs["x"], inputs["w_r"], inputs.get("logit_bias"))
+        r = self.route(logits, cfg["k"], cfg["routing_mode"],
+                       inputs.get("noise") if cfg["second_choice"] == "noisy" else None)
+        padded = cfg["capacity_mode"] == "padded"
+        C = self.capacity(cfg["N"], cfg["E"], cfg["k"], cfg["capacity_factor"], cfg["min_capacity"]) if padded else None
+        d = self.dispatch(r.idx, r.gate, cfg["E"], C, padded)
+        if tokens is None:
+            tokens = np.arange(cfg["N"])
+        y = self.layer_tokens(tokens, inputs["x"], inputs["w1"], inputs["w2"], inputs["w3"], r.idx, d.dropped,
+                              d.gate_eff, cfg["activation"])
+        P, bal, bal_n = self.balance(r.probs, d.load, cfg["k"])
+        return {"routing": r, "dispatch": d, "tokens": np.asarray(tokens), "y": y,
+                "P": P, "balance_loss": bal, "balance_loss_div_n": bal_n}
+
+
+_DEFAULT: Oracle | None = None
+
+
+def default_oracle() -> Oracle:
+    """The oracle built from ``moe_oracle.c`` (compiled on first use if missing or stale)."""
+    global _DEFAULT
+    if _DEFAULT is None:
+        if (not os.path.exists(ORACLE_LIB)
+                or os.path.getmtime(ORACLE_LIB) < os.path.getmtime(ORACLE_SOURCE)):
+            build_oracle()
+        _DEFAULT = Oracle(ORACLE_LIB)
+    return _DEFAULT

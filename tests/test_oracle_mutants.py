@@ -1,0 +1,60 @@
+"""Plants plausible mistakes in a copy of the oracle (on the CPU) and checks that the pins
+catch every one: a dropped term, a wrong sign or index, a transposed operand, a wrong
+loop order. Each mutant is a single textual replacement in moe_oracle.c, compiled with
+gcc into a temporary library."""
+import os
+
+import pytest
+
+import oracle_pins
+from oracle import ORACLE_SOURCE, Oracle, build_oracle
+
+MUTANTS = {
+    "gate_from_slot0": ("const double g = gate_eff[t * k + j];", "const double g = gate_eff[t * k + 0];"),
+    "overwrite_not_accumulate": ("y[i * D + d] += g * fo[d];", "y[i * D + d] = g * fo[d];"),
+    "softmax_sign": ("probs[t * E + e] = exp((double)l32[e] - m) / z;", "probs[t * E + e] = exp(m - (double)l32[e]) / z;"),
+    "tie_to_higher_index": ("if (!chosen[e] && (best < 0 || val[e] > val[best])) best = e;",
+                            "if (!chosen[e] && (best < 0 || val[e] >= val[best])) best = e;"),
+    "token_major_capacity": ("  for (int32_t j = 0; j < k; ++j)\n    for (int64_t t = 0; t < N; ++t) {\n      int32_t e = idx[t * k + j];\n      if (C < 0",
+                             "  for (int64_t t = 0; t < N; ++t)\n    for (int32_t j = 0; j < k; ++j) {\n      int32_t e = idx[t * k + j];\n      if (C < 0"),
+    "no_drop_renormalisation": ("else gate_eff[t * k + j] = g * all / kept;", "else gate_eff[t * k + j] = g;"),
+    "capacity_without_k": ("double c = ceil(((cf * (double)N) * (double)k) / (double)E);",
+                           "double c = ceil((cf * (double)N) / (double)E);"),
+    "capacity_floor": ("double c = ceil(((cf * (double)N) * (double)k) / (double)E);",
+                       "double c = floor(((cf * (double)N) * (double)k) / (double)E);"),
+    "w3_transposed": ("out[d] += u * elem(w3, w_dtype, base_dn + f * D + d);",
+                      "out[d] += u * elem(w3, w_dtype, base_dn + d * F + f);"),
+    "silu_sign": ("if (kind == ACT_SILU) return z / (1.0 + exp(-z));", "if (kind == ACT_SILU) return z / (1.0 + exp(z));"),
+    "gelu_scale": ("return 0.5 * z * (1.0 + erf(z / sqrt(2.0)));", "return 0.5 * z * (1.0 + erf(z));"),
+    "act_on_w2_branch": ("const double u = oracle_act(act, h1[f]) * h2[f];", "const double u = h1[f] * oracle_act(act, h2[f]);"),
+    "noise_on_slot0": ("val[e] = (j > 0 && noisy) ?", "val[e] = (noisy) ?"),
+    "balance_f_div_n": ("b += ((double)load[e] / ((double)N * (double)k)) * P[e];", "b += ((double)load[e] / (double)N) * P[e];"),
+    "mode_b_uses_probs": ("for (int32_t j = 0; j < k; ++j) gate[t * k + j] = exp((double)l32[idx[t * k + j]] - ref) / s;",
+                          "for (int32_t j = 0; j < k; ++j) gate[t * k + j] = probs[t * E + idx[t * k + j]];"),
+    "bias_dropped": ("if (bias) s += (double)bias[e];", ";"),
+    "logits_transposed_w": ("s += elem(x, x_dtype, t * D + d) * (double)w_r[d * E + e];",
+                            "s += elem(x, x_dtype, t * D + d) * (double)w_r[e * D + d];"),
+    "padded_offsets_ragged": ("offsets[e] = padded ? (int64_t)e * C : run;", "offsets[e] = run;"),
+    "drop_case_b_keeps_gates": ("if (nk == k) gate_eff[t * k + j] = g;",
+                                "if (nk == k || nk == 0) gate_eff[t * k + j] = g;"),
+    "bf16_truncated_shift": ("uint32_t u = (uint32_t)bits << 16;", "uint32_t u = (uint32_t)bits << 15;"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(tmp_path, name):
+    old, new = MUTANTS[name]
+    src = open(ORACLE_SOURCE).read()
+    assert src.count(old) == 1, f"mutation site of {name} not found exactly once"
+    mpath = os.path.join(tmp_path, "moe_oracle_mut.c")
+    with open(mpath, "w") as f:
+        f.write(src.replace(old, new))
+    lib = build_oracle(mpath, os.path.join(tmp_path, "libmut.so"))
+    orc = Oracle(lib)
+    failed = []
+    for pin in oracle_pins.ALL_PINS:
+        try:
+            pin(orc)
+        except (AssertionError, ValueError):
+            failed.append(pin.__name__)
+    assert failed, f"mutant {name} passed every pin"
