@@ -1,0 +1,205 @@
+"""Benchmark of the MoE-layer forward on one MI355X.
+
+A step is one pass of the whole hot path over one batch of seeded synthetic input that
+is already resident in HBM: router (fp32 logits, softmax, top-k, gates) -> dispatch
+(histogram, capacity slots, drop rule, gather) -> gated up-projection grouped GEMM ->
+down-projection grouped GEMM -> combine. W untimed warm-up steps, then exactly K timed
+steps between two device synchronisations. HIP events recorded on the launch stream
+between the stages give each stage's average duration inside the timed region.
+
+Prints one JSON line: tokens/s, the roofline of the dominant kernel, and the fp64 CPU
+oracle timed on a bounded sample of the same workload on the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "MoE-layer tokens/s + grouped-GEMM TFLOP/s (% bf16 MFMA peak), Mixtral-shaped"
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PEAK_F32_TFLOPS = 157.3       # MI355X fp32
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+RIDGE = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
+STAGES = ["route", "dispatch", "expert_up", "expert_down", "combine"]
+KERNEL_OF_STAGE = {"expert_up": "k_gemm_bf16 (gated up-projection)", "expert_down": "k_gemm_bf16 (down-projection)"}
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--workload", default="mixtral_prefill")
+    p.add_argument("--cpu-sample", type=int, default=768, help="tokens in the oracle's timed FFN sample")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    return p.parse_args()
+
+
+def source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "mixture_experts_layer_wave_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profiles(workload: str, kernel_stage: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it was taken
+    on the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("source_hash") != source_hash():
+        return None
+    st = t.get("stages", {}).get(kernel_stage)
+    return None if st is None else st.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(cfg, inp, sample: int):
+    """The fp64 oracle (as it stands) on a bounded sample of the same workload."""
+    import numpy as np
+    from oracle import default_oracle
+    orc = default_oracle()
+    N = cfg["N"]
+    t0 = time.perf_counter()
+    logits = orc.router_logits(inp["x"], inp["w_r"], inp["logit_bias"])
+    r = orc.route(logits, cfg["k"], cfg["routing_mode"],
+                  inp["noise"] if cfg["second_choice"] == "noisy" else None)
+    padded = cfg["capacity_mode"] == "padded"
+    C = orc.capacity(N, cfg["E"], cfg["k"], cfg["capacity_factor"], cfg["min_capacity"]) if padded else None
+    o = orc.dispatch(r.idx, r.gate, cfg["E"], C, padded)
+    t1 = time.perf_counter()
+    toks = np.linspace(0, N - 1, min(sample, N)).astype(np.int64)
+    orc.layer_tokens(toks, inp["x"], inp["w1"], inp["w2"], inp["w3"], r.idx, o.dropped, o.gate_eff,
+                     cfg["activation"])
+    t2 = time.perf_counter()
+    n = len(toks)
+    per_tok = (t1 - t0) / N + (t2 - t1) / n
+    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    return {"value": 1.0 / per_tok, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"router+softmax+top-k+dispatch of all {N} tokens ({t1 - t0:.2f} s), expert FFN + combine "
+                      f"of {n} evenly spaced tokens ({t2 - t1:.2f} s); rate = 1 / (route time per token + "
+                      f"FFN time per token)"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (this build has no multi-GPU path); got --gpus {args.gpus}",
+              file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+    from mixture_experts_layer_wave_amd import binding as B
+    from mixture_experts_layer_wave_amd import configs, inputs
+
+    cfg = configs.get_config(args.workload)
+    inp = inputs.make_inputs(cfg)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    layer = B.MoELayer(cfg, inp, device=dev)
+    d = layer.desc
+    N, D, F, E, k = cfg["N"], cfg["D"], cfg["F"], cfg["E"], cfg["k"]
+    rows = B.moe_rows(d)
+    v = layer.views()
+    sc = v["scratch"]
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        B.moe_route(d, layer.x, layer.w_r, layer.bias, layer.noise, None, None, None, v["topk_idx"], v["topk_gate"],
+                    sc)
+        if ev is not None:
+            ev[1].record(stream)
+        B.moe_dispatch(d, layer.x, v["topk_idx"], v["topk_gate"], v["load"], v["counts"], v["offsets"], v["row_of"],
+                       v["dropped"], v["gate_eff"], v["token_of_row"], v["x_perm"], sc)
+        if ev is not None:
+            ev[2].record(stream)
+        B.moe_expert_up(d, v["x_perm"], v["offsets"], v["counts"], layer.w1, layer.w2, v["h"], sc)
+        if ev is not None:
+            ev[3].record(stream)
+        B.moe_expert_down(d, v["h"], v["offsets"], v["counts"], layer.w3, v["y_perm"], sc)
+        if ev is not None:
+            ev[4].record(stream)
+        B.moe_combine(d, v["y_perm"], v["row_of"], v["gate_eff"], layer.y)
+        if ev is not None:
+            ev[5].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    elapsed = t1 - t0
+
+    stage_ms = {s: float(np.mean([events[i][j].elapsed_time(events[i][j + 1]) for i in range(args.steps)]))
+                for j, s in enumerate(STAGES)}
+    counts = v["counts"].cpu().numpy().astype(np.int64)
+    A = int(counts.sum())
+    active = int((counts > 0).sum())
+    es = 2 if cfg["dtype"] == "bf16" else 4
+    work = {
+        "expert_up": dict(flops=4.0 * A * D * F, bytes=es * (2.0 * active * D * F + A * D + A * F)),
+        "expert_down": dict(flops=2.0 * A * F * D, bytes=es * (1.0 * active * D * F + A * F + A * D)),
+    }
+    gemm_ms = stage_ms["expert_up"] + stage_ms["expert_down"]
+    gemm_tflops = (work["expert_up"]["flops"] + work["expert_down"]["flops"]) / (gemm_ms * 1e-3) / 1e12
+    dom = max(("expert_up", "expert_down"), key=lambda s: stage_ms[s])
+    w = work[dom]
+    sec = stage_ms[dom] * 1e-3
+    peak_f = PEAK_BF16_TFLOPS if cfg["dtype"] == "bf16" else PEAK_F32_TFLOPS
+    if w["flops"] / w["bytes"] >= RIDGE or cfg["dtype"] == "f32":
+        roof = {"bound": "mfma", "achieved": w["flops"] / sec / 1e12, "peak": peak_f, "unit": "TFLOP/s"}
+    else:
+        roof = {"bound": "hbm", "achieved": w["bytes"] / sec / 1e9, "peak": PEAK_HBM_GBS, "unit": "GB/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = traffic_from_profiles(args.workload, dom)
+    roof["kernel"] = KERNEL_OF_STAGE[dom]
+    roof["per_launch"] = {"flops": w["flops"], "algorithmic_bytes": w["bytes"], "avg_ms": stage_ms[dom]}
+
+    out = {
+        "metric": METRIC,
+        "value": N * args.steps / elapsed,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": elapsed / args.steps * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg["dtype"],
+        "data": "synthetic (seeded normal inputs and random-init expert weights of the workload's shapes)",
+        "config": {"workload": cfg["name"], "N": N, "D": D, "F": F, "E": E, "k": k, "routing": cfg["routing_mode"],
+                   "second_choice": cfg["second_choice"], "activation": cfg["activation"],
+                   "capacity": cfg["capacity_mode"], "parallelism": "single GPU, all experts resident"},
+        "grouped_gemm": {"tflops": gemm_tflops, "frac_bf16_peak": gemm_tflops / PEAK_BF16_TFLOPS,
+                         "useful_flops": work["expert_up"]["flops"] + work["expert_down"]["flops"],
+                         "accepted_rows": A, "active_experts": active},
+        "stages_ms": stage_ms,
+        "roofline": roof,
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_sample)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

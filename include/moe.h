@@ -44,6 +44,13 @@
 extern "C" {
 #endif
 
+/* Every entry point below is exported from the shared library. */
+#if defined(__GNUC__) || defined(__clang__)
+#define MOE_API __attribute__((visibility("default")))
+#else
+#define MOE_API
+#endif
+
 /* ---- status codes --------------------------------------------------------------- */
 enum {
   MOE_OK = 0,
@@ -115,7 +122,7 @@ typedef struct moe_stats {
 } moe_stats;
 
 /* Human-readable name of a status code (static string, never NULL). */
-const char* moe_status_string(int status);
+MOE_API const char* moe_status_string(int status);
 
 /* ---- host-only queries (no GPU work; safe without a device) ---------------------- */
 
@@ -125,18 +132,18 @@ const char* moe_status_string(int status);
  *   NONE  : C = N (no expert can receive more than N records, so nothing drops).
  * Errors: MOE_E_INVAL for NULL pointers, N<1, E<1, k<1, k>E, or CF<=0 in PADDED mode
  * (the invalid-input rule of [F2C] §3.1). */
-int moe_capacity(const moe_desc* desc, int64_t* capacity);
+MOE_API int moe_capacity(const moe_desc* desc, int64_t* capacity);
 
 /* Number of rows of the expert buffers x_perm/h/y_perm: N*k (NONE) or E*C (PADDED). */
-int moe_rows(const moe_desc* desc, int64_t* rows);
+MOE_API int moe_rows(const moe_desc* desc, int64_t* rows);
 
 /* Bytes of scratch used by moe_route, moe_dispatch, moe_expert_ffn and moe_read_stats
  * (per-block partial counts and sums; O(N*k/256*E) bytes). */
-int moe_scratch_size(const moe_desc* desc, size_t* bytes);
+MOE_API int moe_scratch_size(const moe_desc* desc, size_t* bytes);
 
 /* Bytes of workspace for moe_forward: the scratch region followed by every
  * intermediate (topk ids/gates, slots, x_perm, h, y_perm). */
-int moe_workspace_size(const moe_desc* desc, size_t* bytes);
+MOE_API int moe_workspace_size(const moe_desc* desc, size_t* bytes);
 
 /* Byte offsets of the intermediates inside a moe_forward workspace, so that a caller
  * can inspect them after moe_forward returns (the workspace keeps the last call's
@@ -157,7 +164,7 @@ typedef struct moe_ws_layout {
   size_t y_perm;         /* dtype [rows,D]                                              */
   size_t total;          /* == moe_workspace_size                                       */
 } moe_ws_layout;
-int moe_workspace_layout(const moe_desc* desc, moe_ws_layout* layout);
+MOE_API int moe_workspace_layout(const moe_desc* desc, moe_ws_layout* layout);
 
 /* ---- compute entry points (asynchronous on `stream`) ----------------------------- */
 
@@ -179,7 +186,7 @@ int moe_workspace_layout(const moe_desc* desc, moe_ws_layout* layout);
  *   topk_gate  [N,k] fp32        required output, gate of each slot
  *   scratch    moe_scratch_size  optional (NULL = skip); receives per-block partial sums
  *                                of the probabilities for the balance statistic. */
-int moe_route(const moe_desc* desc, const void* x, const float* w_r, const float* logit_bias,
+MOE_API int moe_route(const moe_desc* desc, const void* x, const float* w_r, const float* logit_bias,
               const float* noise, const float* logits_in, float* logits_out, float* probs_out,
               int32_t* topk_idx, float* topk_gate, void* scratch, size_t scratch_bytes,
               void* stream);
@@ -203,7 +210,7 @@ int moe_route(const moe_desc* desc, const void* x, const float* w_r, const float
  *   gate_eff [N,k] fp32; token_of_row [rows] int32; x_perm [rows,D] dtype.
  *   scratch (moe_scratch_size bytes) is required. Every pointer is required.
  *   topk_idx entries must lie in [0,E) and be distinct per token (as moe_route makes). */
-int moe_dispatch(const moe_desc* desc, const void* x, const int32_t* topk_idx,
+MOE_API int moe_dispatch(const moe_desc* desc, const void* x, const int32_t* topk_idx,
                  const float* topk_gate, int32_t* load, int32_t* counts, int32_t* offsets,
                  int32_t* row_of, uint8_t* dropped, float* gate_eff, int32_t* token_of_row,
                  void* x_perm, void* scratch, size_t scratch_bytes, void* stream);
@@ -217,22 +224,33 @@ int moe_dispatch(const moe_desc* desc, const void* x, const int32_t* topk_idx,
  * Arguments: x_perm [rows,D], w1 and w2 [E,D,F], w3 [E,F,D], h [rows,F], y_perm [rows,D],
  *   all dtype; offsets [E+1], counts [E] int32 as produced by moe_dispatch.
  *   scratch (moe_scratch_size bytes) is required. Accumulation is fp32. */
-int moe_expert_ffn(const moe_desc* desc, const void* x_perm, const int32_t* offsets,
+MOE_API int moe_expert_ffn(const moe_desc* desc, const void* x_perm, const int32_t* offsets,
                    const int32_t* counts, const void* w1, const void* w2, const void* w3,
                    void* h, void* y_perm, void* scratch, size_t scratch_bytes, void* stream);
+
+/* The two halves of moe_expert_ffn, for callers that schedule or time them apart:
+ *   moe_expert_up  : h = act(x_perm W1_e) * (x_perm W2_e)   (the gated up-projection)
+ *   moe_expert_down: y_perm = h W3_e                          (the down-projection)
+ * Arguments, row ranges and errors as for moe_expert_ffn. */
+MOE_API int moe_expert_up(const moe_desc* desc, const void* x_perm, const int32_t* offsets,
+                  const int32_t* counts, const void* w1, const void* w2, void* h, void* scratch,
+                  size_t scratch_bytes, void* stream);
+MOE_API int moe_expert_down(const moe_desc* desc, const void* h, const int32_t* offsets,
+                    const int32_t* counts, const void* w3, void* y_perm, void* scratch,
+                    size_t scratch_bytes, void* stream);
 
 /* Combine ([GROK5] §5.3.5 gate-weighted sum, §5.8; [BOOK12] §12.2 accumulate, not
  * overwrite): y[t,:] = sum over kept slots j, in slot order, of
  * gate_eff[t,j] * y_perm[row_of[t,j],:], accumulated in fp32 and rounded once to dtype;
  * exactly 0 for a token with every slot dropped.
  * Arguments: y_perm [rows,D] dtype; row_of [N,k] int32; gate_eff [N,k] fp32; y [N,D]. */
-int moe_combine(const moe_desc* desc, const void* y_perm, const int32_t* row_of,
+MOE_API int moe_combine(const moe_desc* desc, const void* y_perm, const int32_t* row_of,
                 const float* gate_eff, void* y, void* stream);
 
 /* The whole layer: moe_route -> moe_dispatch -> moe_expert_ffn -> moe_combine with every
  * intermediate in `workspace` (moe_workspace_size bytes, laid out as
  * moe_workspace_layout reports). Arguments as in the step functions; y [N,D] dtype. */
-int moe_forward(const moe_desc* desc, const void* x, const float* w_r, const float* logit_bias,
+MOE_API int moe_forward(const moe_desc* desc, const void* x, const float* w_r, const float* logit_bias,
                 const float* noise, const void* w1, const void* w2, const void* w3, void* y,
                 void* workspace, size_t workspace_bytes, void* stream);
 
@@ -240,7 +258,7 @@ int moe_forward(const moe_desc* desc, const void* x, const float* w_r, const flo
  * moe_scratch_size bytes are the scratch) by the last moe_route + moe_dispatch on it,
  * copies them to *out and SYNCHRONISES `stream`. balance_loss fields are 0 if moe_route
  * ran without scratch. */
-int moe_read_stats(const moe_desc* desc, const void* scratch, size_t scratch_bytes,
+MOE_API int moe_read_stats(const moe_desc* desc, const void* scratch, size_t scratch_bytes,
                    moe_stats* out, void* stream);
 
 #ifdef __cplusplus

@@ -1,0 +1,246 @@
+// dispatch.hip: expert load histogram, slot-major capacity positions, drop rule,
+// gather into expert-contiguous buffers, and the statistics reduction, for gfx950.
+//
+// Method ("MoE 公式到源码对照" §1.3 load histogram, §3.1-3.3 capacity, dropped mask and drop
+// rate; "8.1 MoE 系列" §2.1-2.3 capacity, overflow cases A/B and zero-padded buffers;
+// "第 12 章 MoE：路由、专家与负载" §12.2 expert-grouped buffers, N*k records):
+//   load[e] counts the (token, slot) records of expert e. Positions inside an expert are
+//   assigned slot-major: all slot-0 records in token order, then slot 1, ...; a record
+//   is kept iff its position is below the capacity C. A token whose kept slots are a
+//   strict subset keeps the whole gate mass on them; a token with none kept contributes 0.
+//
+// Design: deterministic by construction, with no global atomics. Three passes:
+//   count  : each 256-token workgroup builds, per slot, its expert histogram with one
+//            wave ballot per expert (rank = popcount of lower lanes with equal expert);
+//   scan   : one wave scans the block histograms in (slot, block) order per expert,
+//            giving each block's base position, the loads, counts and offsets;
+//   assign : the same ballots give each record's rank inside its block; position =
+//            base + rank. Rows, drop mask and gates after the drop rule are written.
+// The gather then copies token rows into the expert buffers with 16-byte vector moves.
+#include "moe_device.h"
+#include "moe_internal.h"
+
+namespace moe {
+namespace {
+
+constexpr int kTB = kDispatchTokens;
+
+// Per-wave match of expert ids: on return rank = number of lower lanes of this wave with
+// the same expert, and cnt_s[w][x] = lanes of wave w holding expert x (x < E).
+__device__ __forceinline__ void wave_match(int e, int E, int (*cnt_s)[kMaxE], int& rank) {
+  const int w = threadIdx.x >> 6;
+  const int lane = lane_id();
+  const uint64_t lt = lanemask_lt();
+  rank = 0;
+  for (int x = 0; x < E; ++x) {
+    const uint64_t m = __ballot(e == x);
+    if (e == x) rank = __popcll(m & lt);
+    if (lane == 0) cnt_s[w][x] = __popcll(m);
+  }
+}
+
+__global__ __launch_bounds__(256) void k_dispatch_count(const DispatchArgs a) {
+  __shared__ int cnt_s[4][kMaxE];
+  const int tid = threadIdx.x;
+  const int64_t t = (int64_t)blockIdx.x * kTB + tid;
+  const bool valid = t < a.N;
+  for (int j = 0; j < a.k; ++j) {
+    int e = valid ? a.topk_idx[t * a.k + j] : -1;
+    if (e >= a.E) e = -1;  // out-of-range ids are ignored (they never index LDS or scratch)
+    int rank;
+    wave_match(e, a.E, cnt_s, rank);
+    __syncthreads();
+    if (tid < a.E)
+      a.blockcnt[((int64_t)j * a.nblk + blockIdx.x) * a.E + tid] =
+          cnt_s[0][tid] + cnt_s[1][tid] + cnt_s[2][tid] + cnt_s[3][tid];
+    __syncthreads();
+  }
+}
+
+__global__ __launch_bounds__(64) void k_dispatch_scan(const DispatchArgs a) {
+  __shared__ int cnt_s[kMaxE];
+  const int e = threadIdx.x;
+  if (e < a.E) {
+    int run = 0;
+    for (int j = 0; j < a.k; ++j) {
+      for (int b = 0; b < a.nblk; ++b) {
+        const int64_t i = ((int64_t)j * a.nblk + b) * a.E + e;
+        a.base[i] = run;
+        run += a.blockcnt[i];
+      }
+    }
+    a.load[e] = run;
+    a.load_copy[e] = run;
+    const int c = (a.C < 0 || run < a.C) ? run : (int)a.C;
+    a.counts[e] = c;
+    cnt_s[e] = c;
+  }
+  __syncthreads();
+  if (e == 0) {
+    int off = 0;
+    for (int x = 0; x < a.E; ++x) {
+      a.offsets[x] = a.padded ? (int)((int64_t)x * a.C) : off;
+      off += cnt_s[x];
+    }
+    a.offsets[a.E] = a.padded ? (int)((int64_t)a.E * a.C) : off;
+  }
+}
+
+__global__ __launch_bounds__(256) void k_dispatch_assign(const DispatchArgs a) {
+  __shared__ int cnt_s[4][kMaxE];
+  __shared__ int drop_s[4];
+  const int tid = threadIdx.x;
+  const int w = tid >> 6;
+  const int64_t t = (int64_t)blockIdx.x * kTB + tid;
+  const bool valid = t < a.N;
+
+  int row[kMaxK];
+  bool kept[kMaxK];
+#pragma unroll
+  for (int j = 0; j < kMaxK; ++j) { row[j] = -1; kept[j] = false; }
+
+  for (int j = 0; j < a.k; ++j) {
+    int e = valid ? a.topk_idx[t * a.k + j] : -1;
+    if (e >= a.E) e = -1;  // out-of-range ids are treated as dropped records
+    int rank;
+    wave_match(e, a.E, cnt_s, rank);
+    __syncthreads();
+    if (e >= 0) {
+      int prefix = 0;
+      for (int ww = 0; ww < w; ++ww) prefix += cnt_s[ww][e];
+      const int64_t pos = (int64_t)a.base[((int64_t)j * a.nblk + blockIdx.x) * a.E + e] + prefix + rank;
+      const bool k_ok = (a.C < 0) || (pos < a.C);
+      int r = -1;
+      if (k_ok) {
+        const int off = a.padded ? (int)((int64_t)e * a.C) : a.offsets[e];
+        r = off + (int)pos;
+      }
+#pragma unroll
+      for (int jj = 0; jj < kMaxK; ++jj)
+        if (jj == j) { row[jj] = r; kept[jj] = k_ok; }
+    }
+    __syncthreads();
+  }
+
+  bool all_dropped = false;
+  if (valid) {
+    float g[kMaxK];
+    float all = 0.f, ksum = 0.f;
+    int nk = 0;
+#pragma unroll
+    for (int j = 0; j < kMaxK; ++j) {
+      g[j] = (j < a.k) ? a.topk_gate[t * a.k + j] : 0.f;
+      if (j < a.k) {
+        all += g[j];
+        if (kept[j]) { ksum += g[j]; nk += 1; }
+      }
+    }
+    all_dropped = (nk == 0);
+#pragma unroll
+    for (int j = 0; j < kMaxK; ++j) {
+      if (j < a.k) {
+        float ge;
+        if (nk == a.k) ge = g[j];
+        else if (nk == 0 || !kept[j]) ge = 0.f;
+        else ge = g[j] * all / ksum;
+        a.row_of[t * a.k + j] = row[j];
+        a.dropped[t * a.k + j] = kept[j] ? 0 : 1;
+        a.gate_eff[t * a.k + j] = ge;
+        if (kept[j]) a.token_of_row[row[j]] = (int32_t)t;
+      }
+    }
+  }
+  const uint64_t m = __ballot(all_dropped);
+  if ((tid & 63) == 0) drop_s[w] = __popcll(m);
+  __syncthreads();
+  if (tid == 0) a.tokdrop[blockIdx.x] = drop_s[0] + drop_s[1] + drop_s[2] + drop_s[3];
+}
+
+// One wave per expert-buffer row: copy the token's row or write zeros for padding.
+template <int VB>  // bytes per vector move
+__global__ __launch_bounds__(256) void k_gather(const GatherArgs a) {
+  const int w = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int64_t r = (int64_t)blockIdx.x * 4 + w;
+  if (r >= a.rows) return;
+  bool valid = true;
+  if (a.padded) {
+    const int64_t e = r / a.C;
+    valid = (r - e * a.C) < a.counts[e];
+  }
+  const int64_t row_bytes = (int64_t)a.D * a.elem_bytes;
+  const int nvec = (int)(row_bytes / VB);
+  u32x4* dst = reinterpret_cast<u32x4*>(reinterpret_cast<char*>(a.x_perm) + r * row_bytes);
+  const int64_t t = valid ? (int64_t)a.token_of_row[r] : -1;
+  if (t >= 0 && t < a.N) {
+    const u32x4* src = reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(a.x) + t * row_bytes);
+    for (int i = lane; i < nvec; i += 64) dst[i] = src[i];
+  } else {
+    const u32x4 z = {0u, 0u, 0u, 0u};
+    for (int i = lane; i < nvec; i += 64) dst[i] = z;
+    if (lane == 0) a.token_of_row[r] = -1;
+  }
+}
+
+// Statistics of the last route + dispatch, reduced in a fixed order (double precision).
+struct DevStats {
+  int64_t routed_slots, dropped_slots, dropped_tokens, capacity;
+  double drop_rate, token_drop_rate, balance_loss, balance_loss_div_n;
+};
+
+__global__ __launch_bounds__(64) void k_stats(const StatsArgs a) {
+  __shared__ double P_s[kMaxE];
+  const int e = threadIdx.x;
+  const bool have_p = *a.psum_magic == kPsumMagic;
+  if (e < a.E) {
+    double s = 0.0;
+    if (have_p)
+      for (int b = 0; b < a.nblk_r; ++b) s += (double)a.psum[(int64_t)b * a.E + e];
+    P_s[e] = s / (double)a.N;
+  }
+  __syncthreads();
+  if (e == 0) {
+    DevStats st;
+    int64_t dslots = 0;
+    double bal = 0.0, baln = 0.0;
+    for (int x = 0; x < a.E; ++x) {
+      const int64_t l = a.load[x];
+      if (a.C >= 0 && l > a.C) dslots += l - a.C;
+      bal += ((double)l / ((double)a.N * (double)a.k)) * P_s[x];
+      baln += ((double)l / (double)a.N) * P_s[x];
+    }
+    int64_t dtok = 0;
+    for (int b = 0; b < a.nblk_d; ++b) dtok += a.tokdrop[b];
+    st.routed_slots = a.N * a.k;
+    st.dropped_slots = dslots;
+    st.dropped_tokens = dtok;
+    st.capacity = a.C < 0 ? a.N : a.C;
+    st.drop_rate = (double)dslots / ((double)a.N * (double)a.k);
+    st.token_drop_rate = (double)dtok / (double)a.N;
+    st.balance_loss = have_p ? (double)a.E * bal : 0.0;
+    st.balance_loss_div_n = have_p ? (double)a.E * baln : 0.0;
+    *reinterpret_cast<DevStats*>(a.out) = st;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL(k_dispatch_count, dim3(a.nblk), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(k_dispatch_scan, dim3(1), dim3(64), 0, s, a);
+  hipLaunchKernelGGL(k_dispatch_assign, dim3(a.nblk), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_gather(const GatherArgs& a, hipStream_t s) {
+  const dim3 grid((unsigned)((a.rows + 3) / 4));
+  hipLaunchKernelGGL(k_gather<16>, grid, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_stats(const StatsArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL(k_stats, dim3(1), dim3(64), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace moe

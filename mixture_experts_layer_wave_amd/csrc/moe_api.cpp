@@ -1,0 +1,363 @@
+// moe_api.cpp: the C ABI of include/moe.h. Validates every argument on the host, then
+// enqueues the gfx950 kernels on the caller's stream. Allocates nothing.
+#include "../../include/moe.h"
+
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+#include "moe_internal.h"
+
+using namespace moe;
+
+namespace {
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+int status_of(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_E_HIP; }
+
+// Size/enum validation shared by every entry point.
+int check_desc(const moe_desc* d) {
+  if (!d) return MOE_E_INVAL;
+  if (d->N < 1 || d->D < 1 || d->F < 1 || d->E < 1 || d->k < 1 || d->k > d->E) return MOE_E_INVAL;
+  if (d->dtype != MOE_DT_F32 && d->dtype != MOE_DT_BF16) return MOE_E_INVAL;
+  if (d->routing_mode != MOE_ROUTE_SOFTMAX_TOPK && d->routing_mode != MOE_ROUTE_TOPK_SOFTMAX) return MOE_E_INVAL;
+  if (d->second_choice != MOE_SECOND_TOPK && d->second_choice != MOE_SECOND_NOISY) return MOE_E_INVAL;
+  if (d->activation < MOE_ACT_SILU || d->activation > MOE_ACT_GELU_TANH) return MOE_E_INVAL;
+  if (d->capacity_mode != MOE_CAP_NONE && d->capacity_mode != MOE_CAP_PADDED) return MOE_E_INVAL;
+  if (d->capacity_mode == MOE_CAP_PADDED && (!(d->capacity_factor > 0.0) || d->min_capacity < 0)) return MOE_E_INVAL;
+  if (d->E > kMaxE || d->k > kMaxK) return MOE_E_UNSUPPORTED;
+  if (d->D % 128 != 0 || d->F % 128 != 0) return MOE_E_UNSUPPORTED;
+  if (d->D > (1 << 20) || d->F > (1 << 20)) return MOE_E_UNSUPPORTED;
+  if (d->N * (int64_t)d->k > INT32_MAX) return MOE_E_UNSUPPORTED;
+  return MOE_OK;
+}
+
+int capacity_of(const moe_desc* d, int64_t* C) {
+  if (d->capacity_mode == MOE_CAP_NONE) { *C = d->N; return MOE_OK; }
+  const double c = ceil(((d->capacity_factor * (double)d->N) * (double)d->k) / (double)d->E);
+  if (!(c < 4.0e18)) return MOE_E_UNSUPPORTED;
+  int64_t ci = (int64_t)c;
+  if (ci < d->min_capacity) ci = d->min_capacity;
+  *C = ci;
+  return MOE_OK;
+}
+
+int rows_of(const moe_desc* d, int64_t* rows) {
+  int64_t C;
+  int st = capacity_of(d, &C);
+  if (st) return st;
+  const int64_t r = d->capacity_mode == MOE_CAP_PADDED ? C * d->E : d->N * d->k;
+  if (r > INT32_MAX) return MOE_E_UNSUPPORTED;
+  *rows = r;
+  return MOE_OK;
+}
+
+size_t esize(const moe_desc* d) { return d->dtype == MOE_DT_BF16 ? 2 : 4; }
+
+moe_ws_layout layout_of(const moe_desc* d, int64_t rows) {
+  moe_ws_layout L;
+  const ScratchLayout s = scratch_layout(d->N, d->E, d->k);
+  const size_t nk = (size_t)d->N * d->k;
+  size_t o = 0;
+  L.scratch = o; o = align_up(o + s.total, 256);
+  L.topk_idx = o; o = align_up(o + 4 * nk, 256);
+  L.topk_gate = o; o = align_up(o + 4 * nk, 256);
+  L.load = o; o = align_up(o + 4 * (size_t)d->E, 256);
+  L.counts = o; o = align_up(o + 4 * (size_t)d->E, 256);
+  L.offsets = o; o = align_up(o + 4 * ((size_t)d->E + 1), 256);
+  L.row_of = o; o = align_up(o + 4 * nk, 256);
+  L.dropped = o; o = align_up(o + nk, 256);
+  L.gate_eff = o; o = align_up(o + 4 * nk, 256);
+  L.token_of_row = o; o = align_up(o + 4 * (size_t)rows, 256);
+  L.x_perm = o; o = align_up(o + esize(d) * (size_t)rows * d->D, 256);
+  L.h = o; o = align_up(o + esize(d) * (size_t)rows * d->F, 256);
+  L.y_perm = o; o = align_up(o + esize(d) * (size_t)rows * d->D, 256);
+  L.total = o;
+  return L;
+}
+
+template <typename T>
+T* at(void* base, size_t off) { return reinterpret_cast<T*>(reinterpret_cast<char*>(base) + off); }
+
+// ---- step bodies (arguments already validated) ----------------------------------------
+
+int do_route(const moe_desc* d, const void* x, const float* w_r, const float* bias, const float* noise,
+             const float* logits_in, float* logits_out, float* probs_out, int32_t* idx, float* gate,
+             void* scratch, hipStream_t st) {
+  RouterArgs a{};
+  a.x = x; a.w_r = w_r; a.bias = bias;
+  a.noise = d->second_choice == MOE_SECOND_NOISY ? noise : nullptr;
+  a.logits_in = logits_in; a.logits_out = logits_out; a.probs_out = probs_out;
+  a.topk_idx = idx; a.topk_gate = gate;
+  if (scratch) {
+    const ScratchLayout s = scratch_layout(d->N, d->E, d->k);
+    a.psum = at<float>(scratch, s.psum);
+    a.psum_magic = at<uint32_t>(scratch, s.header + 64);
+  }
+  a.N = d->N; a.D = (int)d->D; a.E = d->E; a.k = d->k;
+  a.mode = d->routing_mode; a.noisy = d->second_choice == MOE_SECOND_NOISY;
+  return status_of(launch_router(a, d->dtype == MOE_DT_BF16, st));
+}
+
+int do_dispatch(const moe_desc* d, const void* x, const int32_t* idx, const float* gate, int32_t* load,
+                int32_t* counts, int32_t* offsets, int32_t* row_of, uint8_t* dropped, float* gate_eff,
+                int32_t* token_of_row, void* x_perm, void* scratch, hipStream_t st) {
+  int64_t C, rows;
+  int rc = capacity_of(d, &C);
+  if (rc) return rc;
+  rc = rows_of(d, &rows);
+  if (rc) return rc;
+  const ScratchLayout s = scratch_layout(d->N, d->E, d->k);
+  DispatchArgs a{};
+  a.topk_idx = idx; a.topk_gate = gate;
+  a.blockcnt = at<int32_t>(scratch, s.blockcnt);
+  a.base = at<int32_t>(scratch, s.base);
+  a.tokdrop = at<int32_t>(scratch, s.tokdrop);
+  a.load_copy = at<int32_t>(scratch, s.load);
+  a.load = load; a.counts = counts; a.offsets = offsets; a.row_of = row_of; a.dropped = dropped;
+  a.gate_eff = gate_eff; a.token_of_row = token_of_row;
+  a.N = d->N; a.E = d->E; a.k = d->k; a.nblk = s.nblk_d;
+  const bool padded = d->capacity_mode == MOE_CAP_PADDED;
+  a.C = padded ? C : -1;
+  a.padded = padded;
+  hipError_t e = launch_dispatch(a, st);
+  if (e != hipSuccess) return MOE_E_HIP;
+  GatherArgs g{};
+  g.x = x; g.token_of_row = token_of_row; g.counts = counts; g.x_perm = x_perm;
+  g.rows = rows; g.N = d->N; g.D = (int)d->D; g.elem_bytes = (int)esize(d);
+  g.C = padded ? C : -1; g.padded = padded;
+  return status_of(launch_gather(g, st));
+}
+
+FfnArgs ffn_args(const moe_desc* d, int64_t C, int64_t rows, const void* x_perm, const int32_t* offsets,
+                 const int32_t* counts, const void* w1, const void* w2, const void* w3, void* h, void* y_perm) {
+  FfnArgs a{};
+  a.x_perm = x_perm; a.offsets = offsets; a.counts = counts; a.w1 = w1; a.w2 = w2; a.w3 = w3;
+  a.h = h; a.y_perm = y_perm; a.rows = rows;
+  a.max_rows_per_expert = d->capacity_mode == MOE_CAP_PADDED ? (C < d->N ? C : d->N) : d->N;
+  a.D = (int)d->D; a.F = (int)d->F; a.E = d->E; a.act = d->activation;
+  return a;
+}
+
+// which: 1 = up only, 2 = down only, 3 = both
+int do_ffn(const moe_desc* d, const void* x_perm, const int32_t* offsets, const int32_t* counts, const void* w1,
+           const void* w2, const void* w3, void* h, void* y_perm, int which, hipStream_t st) {
+  int64_t C, rows;
+  int rc = capacity_of(d, &C);
+  if (rc) return rc;
+  rc = rows_of(d, &rows);
+  if (rc) return rc;
+  const FfnArgs a = ffn_args(d, C, rows, x_perm, offsets, counts, w1, w2, w3, h, y_perm);
+  const bool bf = d->dtype == MOE_DT_BF16;
+  if (which & 1) {
+    if (launch_expert_up(a, bf, st) != hipSuccess) return MOE_E_HIP;
+  }
+  if (which & 2) {
+    if (launch_expert_down(a, bf, st) != hipSuccess) return MOE_E_HIP;
+  }
+  return MOE_OK;
+}
+
+int do_combine(const moe_desc* d, const void* y_perm, const int32_t* row_of, const float* gate_eff, void* y,
+               hipStream_t st) {
+  CombineArgs a{};
+  a.y_perm = y_perm; a.row_of = row_of; a.gate_eff = gate_eff; a.y = y;
+  int64_t rows;
+  int rc = rows_of(d, &rows);
+  if (rc) return rc;
+  a.N = d->N; a.rows = rows; a.D = (int)d->D; a.k = d->k;
+  return status_of(launch_combine(a, d->dtype == MOE_DT_BF16, st));
+}
+
+#define REQUIRE(p) do { if (!(p) || !aligned16(p)) return MOE_E_INVAL; } while (0)
+#define OPTIONAL(p) do { if ((p) && !aligned16(p)) return MOE_E_INVAL; } while (0)
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_status_string(int status) {
+  switch (status) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_E_INVAL: return "MOE_E_INVAL: invalid argument";
+    case MOE_E_UNSUPPORTED: return "MOE_E_UNSUPPORTED: valid but not supported by these kernels";
+    case MOE_E_WORKSPACE: return "MOE_E_WORKSPACE: workspace or scratch missing or too small";
+    case MOE_E_HIP: return "MOE_E_HIP: HIP runtime error";
+    default: return "unknown moe status";
+  }
+}
+
+int moe_capacity(const moe_desc* d, int64_t* capacity) {
+  if (!d || !capacity) return MOE_E_INVAL;
+  if (d->N < 1 || d->E < 1 || d->k < 1 || d->k > d->E) return MOE_E_INVAL;
+  if (d->capacity_mode == MOE_CAP_PADDED && (!(d->capacity_factor > 0.0) || d->min_capacity < 0)) return MOE_E_INVAL;
+  return capacity_of(d, capacity);
+}
+
+int moe_rows(const moe_desc* d, int64_t* rows) {
+  if (!rows) return MOE_E_INVAL;
+  int rc = check_desc(d);
+  if (rc) return rc;
+  return rows_of(d, rows);
+}
+
+int moe_scratch_size(const moe_desc* d, size_t* bytes) {
+  if (!bytes) return MOE_E_INVAL;
+  int rc = check_desc(d);
+  if (rc) return rc;
+  *bytes = scratch_layout(d->N, d->E, d->k).total;
+  return MOE_OK;
+}
+
+int moe_workspace_layout(const moe_desc* d, moe_ws_layout* layout) {
+  if (!layout) return MOE_E_INVAL;
+  int rc = check_desc(d);
+  if (rc) return rc;
+  int64_t rows;
+  rc = rows_of(d, &rows);
+  if (rc) return rc;
+  *layout = layout_of(d, rows);
+  return MOE_OK;
+}
+
+int moe_workspace_size(const moe_desc* d, size_t* bytes) {
+  if (!bytes) return MOE_E_INVAL;
+  moe_ws_layout L;
+  int rc = moe_workspace_layout(d, &L);
+  if (rc) return rc;
+  *bytes = L.total;
+  return MOE_OK;
+}
+
+int moe_route(const moe_desc* d, const void* x, const float* w_r, const float* logit_bias, const float* noise,
+              const float* logits_in, float* logits_out, float* probs_out, int32_t* topk_idx, float* topk_gate,
+              void* scratch, size_t scratch_bytes, void* stream) {
+  int rc = check_desc(d);
+  if (rc) return rc;
+  if (!logits_in) { REQUIRE(x); REQUIRE(w_r); OPTIONAL(logit_bias); } else { REQUIRE(logits_in); }
+  if (d->second_choice == MOE_SECOND_NOISY) REQUIRE(noise);
+  OPTIONAL(logits_out); OPTIONAL(probs_out);
+  REQUIRE(topk_idx); REQUIRE(topk_gate);
+  if (scratch) {
+    OPTIONAL(scratch);
+    if (scratch_bytes < scratch_layout(d->N, d->E, d->k).total) return MOE_E_WORKSPACE;
+  }
+  return do_route(d, x, w_r, logit_bias, noise, logits_in, logits_out, probs_out, topk_idx, topk_gate, scratch,
+                  (hipStream_t)stream);
+}
+
+int moe_dispatch(const moe_desc* d, const void* x, const int32_t* topk_idx, const float* topk_gate, int32_t* load,
+                 int32_t* counts, int32_t* offsets, int32_t* row_of, uint8_t* dropped, float* gate_eff,
+                 int32_t* token_of_row, void* x_perm, void* scratch, size_t scratch_bytes, void* stream) {
+  int rc = check_desc(d);
+  if (rc) return rc;
+  int64_t rows;
+  rc = rows_of(d, &rows);
+  if (rc) return rc;
+  REQUIRE(x); REQUIRE(topk_idx); REQUIRE(topk_gate); REQUIRE(load); REQUIRE(counts); REQUIRE(offsets);
+  REQUIRE(row_of); REQUIRE(dropped); REQUIRE(gate_eff); REQUIRE(token_of_row); REQUIRE(x_perm);
+  if (!scratch || !aligned16(scratch)) return MOE_E_WORKSPACE;
+  if (scratch_bytes < scratch_layout(d->N, d->E, d->k).total) return MOE_E_WORKSPACE;
+  return do_dispatch(d, x, topk_idx, topk_gate, load, counts, offsets, row_of, dropped, gate_eff, token_of_row,
+                     x_perm, scratch, (hipStream_t)stream);
+}
+
+int moe_expert_ffn(const moe_desc* d, const void* x_perm, const int32_t* offsets, const int32_t* counts,
+                   const void* w1, const void* w2, const void* w3, void* h, void* y_perm, void* scratch,
+                   size_t scratch_bytes, void* stream) {
+  int rc = check_desc(d);
+  if (rc) return rc;
+  REQUIRE(x_perm); REQUIRE(offsets); REQUIRE(counts); REQUIRE(w1); REQUIRE(w2); REQUIRE(w3); REQUIRE(h);
+  REQUIRE(y_perm);
+  if (!scratch || !aligned16(scratch)) return MOE_E_WORKSPACE;
+  if (scratch_bytes < scratch_layout(d->N, d->E, d->k).total) return MOE_E_WORKSPACE;
+  return do_ffn(d, x_perm, offsets, counts, w1, w2, w3, h, y_perm, 3, (hipStream_t)stream);
+}
+
+int moe_expert_up(const moe_desc* d, const void* x_perm, const int32_t* offsets, const int32_t* counts,
+                  const void* w1, const void* w2, void* h, void* scratch, size_t scratch_bytes, void* stream) {
+  int rc = check_desc(d);
+  if (rc) return rc;
+  REQUIRE(x_perm); REQUIRE(offsets); REQUIRE(counts); REQUIRE(w1); REQUIRE(w2); REQUIRE(h);
+  if (!scratch || !aligned16(scratch)) return MOE_E_WORKSPACE;
+  if (scratch_bytes < scratch_layout(d->N, d->E, d->k).total) return MOE_E_WORKSPACE;
+  return do_ffn(d, x_perm, offsets, counts, w1, w2, nullptr, h, nullptr, 1, (hipStream_t)stream);
+}
+
+int moe_expert_down(const moe_desc* d, const void* h, const int32_t* offsets, const int32_t* counts,
+                    const void* w3, void* y_perm, void* scratch, size_t scratch_bytes, void* stream) {
+  int rc = check_desc(d);
+  if (rc) return rc;
+  REQUIRE(h); REQUIRE(offsets); REQUIRE(counts); REQUIRE(w3); REQUIRE(y_perm);
+  if (!scratch || !aligned16(scratch)) return MOE_E_WORKSPACE;
+  if (scratch_bytes < scratch_layout(d->N, d->E, d->k).total) return MOE_E_WORKSPACE;
+  return do_ffn(d, nullptr, offsets, counts, nullptr, nullptr, w3, const_cast<void*>(h), y_perm, 2,
+                (hipStream_t)stream);
+}
+
+int moe_combine(const moe_desc* d, const void* y_perm, const int32_t* row_of, const float* gate_eff, void* y,
+                void* stream) {
+  int rc = check_desc(d);
+  if (rc) return rc;
+  REQUIRE(y_perm); REQUIRE(row_of); REQUIRE(gate_eff); REQUIRE(y);
+  return do_combine(d, y_perm, row_of, gate_eff, y, (hipStream_t)stream);
+}
+
+int moe_forward(const moe_desc* d, const void* x, const float* w_r, const float* logit_bias, const float* noise,
+                const void* w1, const void* w2, const void* w3, void* y, void* workspace, size_t workspace_bytes,
+                void* stream) {
+  int rc = check_desc(d);
+  if (rc) return rc;
+  REQUIRE(x); REQUIRE(w_r); OPTIONAL(logit_bias); REQUIRE(w1); REQUIRE(w2); REQUIRE(w3); REQUIRE(y);
+  if (d->second_choice == MOE_SECOND_NOISY) REQUIRE(noise);
+  int64_t rows;
+  rc = rows_of(d, &rows);
+  if (rc) return rc;
+  if (!workspace || !aligned16(workspace)) return MOE_E_WORKSPACE;
+  const moe_ws_layout L = layout_of(d, rows);
+  if (workspace_bytes < L.total) return MOE_E_WORKSPACE;
+  hipStream_t st = (hipStream_t)stream;
+  void* ws = workspace;
+  rc = do_route(d, x, w_r, logit_bias, noise, nullptr, nullptr, nullptr, at<int32_t>(ws, L.topk_idx),
+                at<float>(ws, L.topk_gate), at<void>(ws, L.scratch), st);
+  if (rc) return rc;
+  rc = do_dispatch(d, x, at<int32_t>(ws, L.topk_idx), at<float>(ws, L.topk_gate), at<int32_t>(ws, L.load),
+                   at<int32_t>(ws, L.counts), at<int32_t>(ws, L.offsets), at<int32_t>(ws, L.row_of),
+                   at<uint8_t>(ws, L.dropped), at<float>(ws, L.gate_eff), at<int32_t>(ws, L.token_of_row),
+                   at<void>(ws, L.x_perm), at<void>(ws, L.scratch), st);
+  if (rc) return rc;
+  rc = do_ffn(d, at<void>(ws, L.x_perm), at<int32_t>(ws, L.offsets), at<int32_t>(ws, L.counts), w1, w2, w3,
+              at<void>(ws, L.h), at<void>(ws, L.y_perm), 3, st);
+  if (rc) return rc;
+  return do_combine(d, at<void>(ws, L.y_perm), at<int32_t>(ws, L.row_of), at<float>(ws, L.gate_eff), y, st);
+}
+
+int moe_read_stats(const moe_desc* d, const void* scratch, size_t scratch_bytes, moe_stats* out, void* stream) {
+  int rc = check_desc(d);
+  if (rc) return rc;
+  if (!out) return MOE_E_INVAL;
+  const ScratchLayout s = scratch_layout(d->N, d->E, d->k);
+  if (!scratch || !aligned16(scratch) || scratch_bytes < s.total) return MOE_E_WORKSPACE;
+  int64_t C;
+  rc = capacity_of(d, &C);
+  if (rc) return rc;
+  void* sc = const_cast<void*>(scratch);
+  StatsArgs a{};
+  a.psum = at<float>(sc, s.psum);
+  a.psum_magic = at<uint32_t>(sc, s.header + 64);
+  a.load = at<int32_t>(sc, s.load);
+  a.tokdrop = at<int32_t>(sc, s.tokdrop);
+  a.out = at<void>(sc, s.header);
+  a.N = d->N; a.C = d->capacity_mode == MOE_CAP_PADDED ? C : -1;
+  a.E = d->E; a.k = d->k; a.nblk_r = s.nblk_r; a.nblk_d = s.nblk_d;
+  hipStream_t st = (hipStream_t)stream;
+  if (launch_stats(a, st) != hipSuccess) return MOE_E_HIP;
+  if (hipMemcpyAsync(out, at<void>(sc, s.header), sizeof(moe_stats), hipMemcpyDeviceToHost, st) != hipSuccess)
+    return MOE_E_HIP;
+  if (hipStreamSynchronize(st) != hipSuccess) return MOE_E_HIP;
+  return MOE_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,138 @@
+// moe_internal.h: host-side launchers of the gfx950 kernels and the scratch layout.
+// (Internal header of the HIP library; the public C ABI is include/moe.h.)
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moe {
+
+constexpr int kRouterTokens = 64;     // tokens per router workgroup
+constexpr int kDispatchTokens = 256;  // tokens per dispatch workgroup
+constexpr int kMaxE = 64;
+constexpr int kMaxK = 8;
+constexpr uint32_t kPsumMagic = 0x5053554du;  // marks valid router partial sums
+
+inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+// Scratch (moe_scratch_size bytes) carved into regions, each 256-byte aligned:
+//   header    : moe_stats (64 B) + magic word
+//   psum      : fp32 [nblk_r][E]   per-router-block sums of the probabilities
+//   blockcnt  : int32 [k][nblk_d][E] per-dispatch-block expert histogram of each slot
+//   base      : int32 [k][nblk_d][E] exclusive slot-major scan of blockcnt
+//   tokdrop   : int32 [nblk_d]     tokens with every slot dropped, per block
+//   load      : int32 [E]          copy of the pre-capacity histogram
+struct ScratchLayout {
+  size_t header, psum, blockcnt, base, tokdrop, load, total;
+  int nblk_r, nblk_d;
+};
+
+inline ScratchLayout scratch_layout(int64_t N, int E, int k) {
+  ScratchLayout s;
+  s.nblk_r = (int)((N + kRouterTokens - 1) / kRouterTokens);
+  s.nblk_d = (int)((N + kDispatchTokens - 1) / kDispatchTokens);
+  size_t o = 0;
+  s.header = o; o = align_up(o + 128, 256);
+  s.psum = o; o = align_up(o + sizeof(float) * (size_t)s.nblk_r * E, 256);
+  s.blockcnt = o; o = align_up(o + sizeof(int32_t) * (size_t)k * s.nblk_d * E, 256);
+  s.base = o; o = align_up(o + sizeof(int32_t) * (size_t)k * s.nblk_d * E, 256);
+  s.tokdrop = o; o = align_up(o + sizeof(int32_t) * (size_t)s.nblk_d, 256);
+  s.load = o; o = align_up(o + sizeof(int32_t) * (size_t)E, 256);
+  s.total = o;
+  return s;
+}
+
+// ---- router -------------------------------------------------------------------------
+struct RouterArgs {
+  const void* x;          // [N,D] fp32 or bf16
+  const float* w_r;       // [D,E]
+  const float* bias;      // [E] or null
+  const float* noise;     // [N,E] or null
+  const float* logits_in; // [N,E] or null
+  float* logits_out;      // [N,E] or null
+  float* probs_out;       // [N,E] or null
+  int32_t* topk_idx;      // [N,k]
+  float* topk_gate;       // [N,k]
+  float* psum;            // [nblk_r][E] or null
+  uint32_t* psum_magic;   // or null
+  int64_t N;
+  int D, E, k, mode, noisy;
+};
+hipError_t launch_router(const RouterArgs& a, bool bf16_x, hipStream_t s);
+
+// ---- dispatch -----------------------------------------------------------------------
+struct DispatchArgs {
+  const int32_t* topk_idx;  // [N,k]
+  const float* topk_gate;   // [N,k]
+  int32_t* blockcnt;        // scratch
+  int32_t* base;            // scratch
+  int32_t* tokdrop;         // scratch
+  int32_t* load_copy;       // scratch
+  int32_t* load;            // [E]
+  int32_t* counts;          // [E]
+  int32_t* offsets;         // [E+1]
+  int32_t* row_of;          // [N,k]
+  uint8_t* dropped;         // [N,k]
+  float* gate_eff;          // [N,k]
+  int32_t* token_of_row;    // [rows]
+  int64_t N;
+  int E, k, nblk;
+  int64_t C;                // -1: no capacity
+  int padded;
+};
+hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t s);
+
+struct GatherArgs {
+  const void* x;            // [N,D]
+  int32_t* token_of_row;    // [rows] (padding rows set to -1 here)
+  const int32_t* counts;    // [E]
+  void* x_perm;             // [rows,D]
+  int64_t rows, N;
+  int D, elem_bytes;
+  int64_t C;
+  int padded;
+};
+hipError_t launch_gather(const GatherArgs& a, hipStream_t s);
+
+struct StatsArgs {
+  const float* psum;
+  const uint32_t* psum_magic;
+  const int32_t* load;      // scratch copy
+  const int32_t* tokdrop;
+  void* out;                // moe_stats in the scratch header
+  int64_t N, C;
+  int E, k, nblk_r, nblk_d;
+};
+hipError_t launch_stats(const StatsArgs& a, hipStream_t s);
+
+// ---- expert FFN -----------------------------------------------------------------------
+struct FfnArgs {
+  const void* x_perm;       // [rows,D]
+  const int32_t* offsets;   // [E+1]
+  const int32_t* counts;    // [E]
+  const void* w1;           // [E,D,F]
+  const void* w2;           // [E,D,F]
+  const void* w3;           // [E,F,D]
+  void* h;                  // [rows,F]
+  void* y_perm;             // [rows,D]
+  int64_t rows;             // rows of the expert buffers
+  int64_t max_rows_per_expert;  // host bound on counts[e] (N, or C when padded)
+  int D, F, E, act;
+};
+// Gated up-projection (h) and down-projection (y_perm) of every expert's rows.
+hipError_t launch_expert_up(const FfnArgs& a, bool bf16, hipStream_t s);
+hipError_t launch_expert_down(const FfnArgs& a, bool bf16, hipStream_t s);
+
+// ---- combine --------------------------------------------------------------------------
+struct CombineArgs {
+  const void* y_perm;       // [rows,D]
+  const int32_t* row_of;    // [N,k]
+  const float* gate_eff;    // [N,k]
+  void* y;                  // [N,D]
+  int64_t N, rows;
+  int D, k;
+};
+hipError_t launch_combine(const CombineArgs& a, bool bf16, hipStream_t s);
+
+}  // namespace moe

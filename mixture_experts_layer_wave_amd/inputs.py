@@ -90,3 +90,24 @@ def make_logits(N: int, E: int, seed: int, std: float = 1.0, zipf_s=None, zipf_b
     if hot_expert is not None:
         a[:, hot_expert] += 50.0
     return torch.from_numpy(a.astype(np.float32))
+
+
+def make_topk(N: int, E: int, k: int, seed: int, skew: float = 0.0):
+    """Random routing records for dispatch tests fed identical inputs: k distinct experts
+    per token (drawn with probabilities proportional to rank^-skew over a seeded expert
+    order) and positive gates in decreasing order that sum to at most 1."""
+    rng = _rng(seed, "logits", 1)
+    order = rng.permutation(E)
+    w = (np.arange(1, E + 1, dtype=np.float64) ** -float(skew))
+    p = np.empty(E)
+    p[order] = w / w.sum()
+    idx = np.stack([rng.choice(E, size=k, replace=False, p=p) for _ in range(N)]).astype(np.int32)
+    g = rng.random((N, k)) + 0.05
+    g = -np.sort(-g, axis=1)
+    g = g / (g.sum(axis=1, keepdims=True) * (1.0 + rng.random((N, 1))))
+    return torch.from_numpy(idx.reshape(N, k)), torch.from_numpy(g.astype(np.float32))
+
+
+def make_rows(rows: int, D: int, seed: int, dtype: str, std: float = 1.0) -> torch.Tensor:
+    """Random expert-buffer rows [rows, D] in the stored element type."""
+    return _store(_normal(seed, "x", (rows, D), std, sub=7), dtype)

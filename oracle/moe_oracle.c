@@ -247,10 +247,9 @@ void oracle_drop_rule(int64_t N, int32_t k, const double* gate, const uint8_t* d
 
 /* ---- step 8: one expert on one token ([BOOK12] §12.1; [GROK5] §5.3.5) ----------------- */
 
-/* out[d] = sum_f act(h1_f) * h2_f * W3[e,f,d], h1_f = sum_d x_d W1[e,d,f],
- * h2_f = sum_d x_d W2[e,d,f]. Weights are [E,D,F] (W1, W2) and [E,F,D] (W3). */
-int oracle_expert_ffn(int64_t D, int64_t F, int w_dtype, int act, const double* x,
-                      const void* w1, const void* w2, const void* w3, int32_t e, double* out) {
+/* h[f] = act(sum_d x_d W1[e,d,f]) * (sum_d x_d W2[e,d,f]); W1, W2 are [E,D,F]. */
+int oracle_expert_hidden(int64_t D, int64_t F, int w_dtype, int act, const double* x,
+                         const void* w1, const void* w2, int32_t e, double* h) {
   double* h1 = (double*)calloc((size_t)F, sizeof(double));
   double* h2 = (double*)calloc((size_t)F, sizeof(double));
   if (!h1 || !h2) { free(h1); free(h2); return ORACLE_EINVAL; }
@@ -262,14 +261,55 @@ int oracle_expert_ffn(int64_t D, int64_t F, int w_dtype, int act, const double* 
       h2[f] += xd * elem(w2, w_dtype, base_up + d * F + f);
     }
   }
+  for (int64_t f = 0; f < F; ++f) h[f] = oracle_act(act, h1[f]) * h2[f];
+  free(h1); free(h2);
+  return ORACLE_OK;
+}
+
+/* out[d] = sum_f h_f W3[e,f,d] with h from oracle_expert_hidden; W3 is [E,F,D]. */
+int oracle_expert_ffn(int64_t D, int64_t F, int w_dtype, int act, const double* x,
+                      const void* w1, const void* w2, const void* w3, int32_t e, double* out) {
+  double* h = (double*)malloc(sizeof(double) * (size_t)F);
+  if (!h) return ORACLE_EINVAL;
+  if (oracle_expert_hidden(D, F, w_dtype, act, x, w1, w2, e, h) != ORACLE_OK) { free(h); return ORACLE_EINVAL; }
   for (int64_t d = 0; d < D; ++d) out[d] = 0.0;
   const int64_t base_dn = (int64_t)e * F * D;
   for (int64_t f = 0; f < F; ++f) {
-    const double u = oracle_act(act, h1[f]) * h2[f];
+    const double u = h[f];
     for (int64_t d = 0; d < D; ++d) out[d] += u * elem(w3, w_dtype, base_dn + f * D + d);
   }
-  free(h1); free(h2);
+  free(h);
   return ORACLE_OK;
+}
+
+/* Expert outputs for a list of expert-buffer rows: out[i,:] = f_{e_i}(xrows[i,:]) and
+ * hid[i,:] = the hidden vector h (either output may be NULL). */
+int oracle_expert_rows(int64_t n, int64_t D, int64_t F, int w_dtype, int act, const double* xrows,
+                       const int32_t* experts, const void* w1, const void* w2, const void* w3,
+                       double* hid, double* out) {
+  int bad = 0;
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : bad)
+  for (int64_t i = 0; i < n; ++i) {
+    if (hid && oracle_expert_hidden(D, F, w_dtype, act, xrows + i * D, w1, w2, experts[i], hid + i * F) != ORACLE_OK)
+      bad = 1;
+    if (out && oracle_expert_ffn(D, F, w_dtype, act, xrows + i * D, w1, w2, w3, experts[i], out + i * D) != ORACLE_OK)
+      bad = 1;
+  }
+  return bad ? ORACLE_EINVAL : ORACLE_OK;
+}
+
+/* ---- step 9 (combine alone): y[t,:] = sum over slots j with row_of[t,j] >= 0, in slot
+ * order, of gate_eff[t,j] * y_perm[row_of[t,j],:] ([GROK5] §5.3.5; [BOOK12] §12.2). */
+void oracle_combine(int64_t N, int64_t D, int32_t k, const double* y_perm, const int64_t* row_of,
+                    const double* gate_eff, double* y) {
+  for (int64_t t = 0; t < N; ++t) {
+    for (int64_t d = 0; d < D; ++d) y[t * D + d] = 0.0;
+    for (int32_t j = 0; j < k; ++j) {
+      const int64_t r = row_of[t * k + j];
+      if (r < 0) continue;
+      for (int64_t d = 0; d < D; ++d) y[t * D + d] += gate_eff[t * k + j] * y_perm[r * D + d];
+    }
+  }
 }
 
 /* ---- step 9: layer output for a list of tokens ([GROK5] §5.3.5, §5.8; [BOOK12] §12.2) */

@@ -118,6 +118,10 @@ class Oracle:
         L.oracle_drop_rule.argtypes = [_i64, _i32, _vp, _vp, _vp]
         L.oracle_expert_ffn.restype = _int
         L.oracle_expert_ffn.argtypes = [_i64, _i64, _int, _int, _vp, _vp, _vp, _vp, _i32, _vp]
+        L.oracle_expert_rows.restype = _int
+        L.oracle_expert_rows.argtypes = [_i64, _i64, _i64, _int, _int, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
+        L.oracle_combine.restype = None
+        L.oracle_combine.argtypes = [_i64, _i64, _i32, _vp, _vp, _vp, _vp]
         L.oracle_layer_tokens.restype = _int
         L.oracle_layer_tokens.argtypes = [_i64, _vp, _i64, _i64, _i64, _i32, _i32, _int, _int,
                                           _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
@@ -195,6 +199,31 @@ class Oracle:
         if rc != 0:
             raise ValueError("oracle_expert_ffn failed")
         return out
+
+    def expert_rows(self, xrows, experts, w1, w2, w3, act: str, want_hidden=True, want_out=True):
+        """(h, f) for expert-buffer rows: h[i] = act(x_i W1_e) * (x_i W2_e), f[i] = h[i] W3_e."""
+        xr = _host(xrows, np.float64)
+        ex = _host(experts, np.int32)
+        a, b, c = _host(w1), _host(w2), _host(w3)
+        n, D = xr.shape
+        F = a.shape[2]
+        hid = np.empty((n, F), np.float64) if want_hidden else None
+        out = np.empty((n, D), np.float64) if want_out else None
+        rc = self.lib.oracle_expert_rows(n, D, F, _dtype_code(a), ACT[act], _ptr(xr), _ptr(ex), _ptr(a), _ptr(b),
+                                         _ptr(c), _ptr(hid), _ptr(out))
+        if rc != 0:
+            raise ValueError("oracle_expert_rows failed")
+        return hid, out
+
+    def combine(self, y_perm, row_of, gate_eff) -> np.ndarray:
+        yp = _host(y_perm, np.float64)
+        ro = _host(row_of, np.int64)
+        ge = _host(gate_eff, np.float64)
+        N, k = ro.shape
+        D = yp.shape[1]
+        y = np.empty((N, D), np.float64)
+        self.lib.oracle_combine(N, D, k, _ptr(yp), _ptr(ro), _ptr(ge), _ptr(y))
+        return y
 
     def layer_tokens(self, tokens, x, w1, w2, w3, idx, dropped, gate_eff, act: str) -> np.ndarray:
         """y rows of the listed tokens (fp64)."""

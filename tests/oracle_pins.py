@@ -400,4 +400,37 @@ def pin_router_logits_library(orc):
     _close(orc.router_logits(xb, w), xb.double().numpy() @ w.astype(np.float64), rtol=1e-13, atol=1e-14)
 
 
+def pin_combine_scatter_matrix(orc):
+    """combine(y_perm, row_of, gate_eff) equals S @ y_perm with S[t, row] = gate, a sparse
+    matrix formulation of the gate-weighted sum ([GROK5] §5.8; [BOOK12] §12.2)."""
+    rng = np.random.default_rng(81)
+    N, k, D, rows = 12, 3, 5, 40
+    y_perm = rng.standard_normal((rows, D))
+    row_of = np.stack([rng.choice(rows, k, replace=False) for _ in range(N)]).astype(np.int64)
+    gate = rng.random((N, k))
+    row_of[2, 1] = -1
+    row_of[5, :] = -1
+    S = np.zeros((N, rows))
+    for t in range(N):
+        for j in range(k):
+            if row_of[t, j] >= 0:
+                S[t, row_of[t, j]] += gate[t, j]
+    y = orc.combine(y_perm, row_of, gate)
+    _close(y, S @ y_perm, rtol=1e-13, atol=1e-14)
+    assert np.all(y[5] == 0.0)
+
+
+def pin_expert_rows_library(orc):
+    """Row-wise expert evaluation (hidden vector and output) equals numpy matmuls."""
+    x, _, w1, w2, w3 = _tiny_case(91, N=6, D=8, F=16, E=3)
+    experts = np.array([2, 0, 1, 1, 2, 0], np.int32)
+    hid, out = orc.expert_rows(x, experts, w1, w2, w3, "gelu_tanh")
+    for i, e in enumerate(experts):
+        h1 = x[i].astype(np.float64) @ w1[e].astype(np.float64)
+        h2 = x[i].astype(np.float64) @ w2[e].astype(np.float64)
+        h = 0.5 * h1 * (1.0 + np.tanh(np.sqrt(2.0 / np.pi) * (h1 + 0.044715 * h1 ** 3))) * h2
+        _close(hid[i], h, rtol=1e-12, atol=1e-14)
+        _close(out[i], h @ w3[e].astype(np.float64), rtol=1e-12, atol=1e-14)
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_") and callable(v)]

@@ -1,0 +1,437 @@
+"""GPU parity of the HIP path against the fp64 oracle, through the C ABI.
+
+Every stage is checked on identical inputs (both sides fed the same logits, the same
+routing records, the same expert rows): indices, loads, slots and the drop mask must be
+bit-exact; floating-point results within the stated tolerances. The whole layer is then
+checked end to end on the five workloads (full sizes, sampled tokens where the oracle
+is slow) and on mid-size variants that span several tiles with ragged tails.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+from mixture_experts_layer_wave_amd import binding as B
+from mixture_experts_layer_wave_amd import configs, inputs
+from parity_util import (MARGIN, TOL_Y, affected_experts, ambiguous_tokens, assert_rows_close, host)
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _dev(t):
+    return None if t is None else t.to(DEV)
+
+
+def _routing_cfg(N, E, k, mode="topk_softmax", noisy=False, dtype="bf16", D=128, F=128, **kw):
+    c = dict(N=N, D=D, F=F, E=E, k=k, dtype=dtype, routing_mode=mode, second_choice="noisy" if noisy else "topk",
+             activation="silu", capacity_mode="none", capacity_factor=0.0, min_capacity=0)
+    c.update(kw)
+    return c
+
+
+# ---------------------------------------------------------------------------------------
+# Router: selection and gates from identical fp32 logits
+# ---------------------------------------------------------------------------------------
+
+ROUTE_CASES = [
+    # N, E, k, dist
+    (1, 8, 2, "normal"), (63, 8, 2, "normal"), (65, 8, 1, "normal"), (1000, 8, 2, "ties"),
+    (1000, 8, 8, "normal"), (777, 4, 2, "zipf"), (300, 16, 4, "ties"), (4097, 64, 2, "zipf"),
+    (513, 64, 8, "normal"), (200, 33, 3, "hot"), (129, 1, 1, "normal"), (640, 64, 2, "ties"),
+]
+
+
+@pytest.mark.parametrize("N,E,k,dist", ROUTE_CASES)
+@pytest.mark.parametrize("mode", ["softmax_topk", "topk_softmax"])
+@pytest.mark.parametrize("noisy", [False, True])
+def test_route_from_identical_logits(orc, N, E, k, dist, mode, noisy):
+    if noisy and k < 2:
+        pytest.skip("noisy second choice needs k >= 2")
+    seed = 10 * N + E + k
+    kw = {}
+    if dist == "ties":
+        kw["quantum"] = 0.25
+    elif dist == "zipf":
+        kw.update(zipf_s=1.2, zipf_beta=1.0)
+    elif dist == "hot":
+        kw["hot_expert"] = E // 2
+    logits = inputs.make_logits(N, E, seed, **kw)
+    noise = inputs.make_logits(N, E, seed + 1, quantum=0.25 if dist == "ties" else None) if noisy else None
+    d = B.make_desc(_routing_cfg(N, E, k, mode, noisy))
+    idx = torch.empty((N, k), dtype=torch.int32, device=DEV)
+    gate = torch.empty((N, k), dtype=torch.float32, device=DEV)
+    probs = torch.empty((N, E), dtype=torch.float32, device=DEV)
+    lout = torch.empty((N, E), dtype=torch.float32, device=DEV)
+    B.moe_route(d, None, None, None, _dev(noise), _dev(logits), lout, probs, idx, gate)
+    torch.cuda.synchronize()
+    r = orc.route(logits, k, mode, noise=noise)
+    assert np.array_equal(host(idx), r.idx), "selection differs from the oracle on identical logits"
+    assert np.array_equal(host(lout), logits.numpy())
+    np.testing.assert_allclose(host(gate), r.gate, rtol=2e-6, atol=1e-7)
+    np.testing.assert_allclose(host(probs), r.probs, rtol=2e-6, atol=1e-7)
+
+
+# ---------------------------------------------------------------------------------------
+# Router GEMM: fp32 logits against the exact (fp64) logits
+# ---------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("name,N,D", [("tiny_fp32", 64, 128), ("mixtral_prefill", 333, 4096),
+                                      ("grok1_layer", 129, 6144), ("gshard_capacity", 1000, 2048),
+                                      ("mixtral_decode", 64, 4096)])
+def test_router_logits(orc, name, N, D):
+    cfg = configs.scaled_config(name, N=N, D=D, F=128)
+    inp = inputs.make_inputs(cfg, weights=False)
+    d = B.make_desc(cfg)
+    E, k = cfg["E"], cfg["k"]
+    lout = torch.empty((N, E), dtype=torch.float32, device=DEV)
+    idx = torch.empty((N, k), dtype=torch.int32, device=DEV)
+    gate = torch.empty((N, k), dtype=torch.float32, device=DEV)
+    B.moe_route(d, _dev(inp["x"]), _dev(inp["w_r"]), _dev(inp["logit_bias"]), _dev(inp["noise"]), None, lout, None,
+                idx, gate)
+    torch.cuda.synchronize()
+    exact = orc.router_logits(inp["x"], inp["w_r"], inp["logit_bias"])
+    x64 = inp["x"].double().numpy()
+    mag = np.abs(x64) @ np.abs(inp["w_r"].double().numpy())   # sum_d |x_d w_de|
+    err = np.abs(host(lout).astype(np.float64) - exact)
+    tol = 4e-6 * mag + 1e-6
+    assert np.all(err <= tol), f"max |dlogit| {err.max():.3e}, worst ratio {(err / tol).max():.2f}"
+
+
+# ---------------------------------------------------------------------------------------
+# Dispatch + gather from identical routing records
+# ---------------------------------------------------------------------------------------
+
+DISPATCH_CASES = [
+    # N, E, k, skew, capacity_mode, cf, min_cap
+    (1, 8, 2, 0.0, "none", 0.0, 0), (255, 8, 2, 0.0, "none", 0.0, 0), (257, 8, 2, 1.0, "none", 0.0, 0),
+    (1000, 64, 2, 1.2, "padded", 1.25, 4), (4096, 8, 2, 0.5, "padded", 1.0, 0),
+    (700, 16, 4, 2.0, "padded", 0.5, 1), (513, 4, 4, 0.0, "padded", 0.3, 0), (300, 64, 8, 1.0, "none", 0.0, 0),
+    (999, 8, 1, 3.0, "padded", 2.0, 0), (128, 2, 2, 0.0, "padded", 0.01, 1), (50, 64, 2, 0.0, "padded", 10.0, 0),
+]
+
+
+def _run_dispatch(d, x, idx, gate):
+    N, k, E, D = d.N, d.k, d.E, d.D
+    rows = B.moe_rows(d)
+    out = dict(load=torch.empty(E, dtype=torch.int32, device=DEV), counts=torch.empty(E, dtype=torch.int32, device=DEV),
+               offsets=torch.empty(E + 1, dtype=torch.int32, device=DEV),
+               row_of=torch.empty((N, k), dtype=torch.int32, device=DEV),
+               dropped=torch.empty((N, k), dtype=torch.uint8, device=DEV),
+               gate_eff=torch.empty((N, k), dtype=torch.float32, device=DEV),
+               token_of_row=torch.full((rows,), -7, dtype=torch.int32, device=DEV),
+               x_perm=torch.full((rows, D), 7.0, dtype=x.dtype, device=DEV))
+    scratch = torch.empty(B.moe_scratch_size(d), dtype=torch.uint8, device=DEV)
+    B.moe_dispatch(d, x, idx, gate, out["load"], out["counts"], out["offsets"], out["row_of"], out["dropped"],
+                   out["gate_eff"], out["token_of_row"], out["x_perm"], scratch)
+    torch.cuda.synchronize()
+    return out, scratch
+
+
+@pytest.mark.parametrize("N,E,k,skew,cap,cf,minc", DISPATCH_CASES)
+def test_dispatch_from_identical_records(orc, N, E, k, skew, cap, cf, minc):
+    cfg = _routing_cfg(N, E, k, capacity_mode=cap, capacity_factor=cf, min_capacity=minc, D=128)
+    d = B.make_desc(cfg)
+    idx, gate = inputs.make_topk(N, E, k, seed=N * 7 + E, skew=skew)
+    x = inputs.make_rows(N, 128, seed=N, dtype="bf16")
+    out, _ = _run_dispatch(d, x.to(DEV), idx.to(DEV), gate.to(DEV))
+    padded = cap == "padded"
+    C = orc.capacity(N, E, k, cf, minc) if padded else None
+    o = orc.dispatch(idx, gate.double(), E, C, padded)
+    assert np.array_equal(host(out["load"]), o.load)
+    assert np.array_equal(host(out["counts"]), o.counts)
+    assert np.array_equal(host(out["offsets"]), o.offsets)
+    assert np.array_equal(host(out["row_of"]), o.row_of)
+    assert np.array_equal(host(out["dropped"]), o.dropped)
+    np.testing.assert_allclose(host(out["gate_eff"]), o.gate_eff, rtol=1e-6, atol=1e-7)
+    gone = np.all(o.dropped == 1, axis=1)
+    assert np.all(host(out["gate_eff"])[gone] == 0.0)
+    # gather: every kept record's row holds its token; padding rows are -1 and zero
+    tor = host(out["token_of_row"])
+    xp = out["x_perm"].cpu()
+    kept = o.row_of >= 0
+    tok = np.broadcast_to(np.arange(N)[:, None], o.row_of.shape)
+    assert np.array_equal(tor[o.row_of[kept]], tok[kept])
+    assert torch.equal(xp[torch.from_numpy(o.row_of[kept])], x[torch.from_numpy(tok[kept].copy())])
+    filled = np.zeros(len(tor), bool)
+    filled[o.row_of[kept]] = True
+    assert np.all(tor[~filled] == -1)
+    assert torch.all(xp[torch.from_numpy(~filled)] == 0)
+
+
+# ---------------------------------------------------------------------------------------
+# Expert FFN from identical expert rows
+# ---------------------------------------------------------------------------------------
+
+FFN_CASES = [
+    # dtype, act, D, F, E, counts
+    ("bf16", "silu", 256, 384, 4, [130, 0, 257, 1]),
+    ("bf16", "gelu_erf", 384, 256, 3, [64, 200, 129]),
+    ("bf16", "gelu_tanh", 128, 512, 2, [5, 300]),
+    ("bf16", "silu", 4096, 1024, 2, [40, 131]),
+    ("f32", "silu", 128, 256, 4, [30, 33, 0, 65]),
+    ("f32", "gelu_erf", 256, 128, 3, [64, 1, 100]),
+]
+
+
+@pytest.mark.parametrize("dt,act,D,F,E,counts", FFN_CASES)
+@pytest.mark.parametrize("layout", ["ragged", "padded"])
+def test_expert_ffn_from_identical_rows(orc, dt, act, D, F, E, counts, layout):
+    counts = np.array(counts, np.int64)
+    if layout == "ragged":
+        N = int(counts.sum())  # k = 1: rows = N
+        cfg = dict(N=N, D=D, F=F, E=E, k=1, dtype=dt, routing_mode="topk_softmax", second_choice="topk",
+                   activation=act, capacity_mode="none", capacity_factor=0.0, min_capacity=0)
+        offsets = np.concatenate([[0], np.cumsum(counts)])
+    else:
+        C = int(counts.max()) + 3
+        N = E * C  # cf = 1 with k = 1 gives C = N / E
+        cfg = dict(N=N, D=D, F=F, E=E, k=1, dtype=dt, routing_mode="topk_softmax", second_choice="topk",
+                   activation=act, capacity_mode="padded", capacity_factor=1.0, min_capacity=0)
+        offsets = np.arange(E + 1) * C
+    d = B.make_desc(cfg)
+    rows = B.moe_rows(d)
+    wcfg = dict(cfg, seed=31 + D + F, x_std=1.0, wr_var=1.0 / D, w_std=0.05 if dt == "bf16" else (1.0 / D) ** 0.5,
+                w3_std=0.05 if dt == "bf16" else (1.0 / F) ** 0.5, noise_std=None, zipf_s=None)
+    w = inputs.make_inputs(wcfg)
+    xp = inputs.make_rows(rows, D, seed=D + rows, dtype=dt)
+    x_perm = xp.to(DEV)
+    h = torch.full((rows, F), 3.0, dtype=xp.dtype, device=DEV)
+    y_perm = torch.full((rows, D), 3.0, dtype=xp.dtype, device=DEV)
+    scratch = torch.empty(B.moe_scratch_size(d), dtype=torch.uint8, device=DEV)
+    t_off = torch.from_numpy(offsets.astype(np.int32)).to(DEV)
+    t_cnt = torch.from_numpy(counts.astype(np.int32)).to(DEV)
+    B.moe_expert_ffn(d, x_perm, t_off, t_cnt, w["w1"].to(DEV), w["w2"].to(DEV), w["w3"].to(DEV), h, y_perm, scratch)
+    torch.cuda.synchronize()
+    sel = np.concatenate([np.arange(offsets[e], offsets[e] + counts[e]) for e in range(E)])
+    experts = np.concatenate([np.full(counts[e], e) for e in range(E)]).astype(np.int32)
+    hid, out = orc.expert_rows(xp.float().numpy()[sel], experts, w["w1"], w["w2"], w["w3"], act)
+    tol_h = 8e-3 if dt == "bf16" else 1e-5
+    assert_rows_close(host(h)[sel], hid, tol_h, "h")
+    assert_rows_close(host(y_perm)[sel], out, TOL_Y[dt], "y_perm")
+    # rows of other experts' ranges are never written by an expert's tiles
+    if layout == "padded":
+        for e in range(E):
+            lo, hi = offsets[e] + counts[e], offsets[e + 1]
+            if hi - lo > 0 and counts[e] % 128 == 0:
+                assert torch.all(y_perm[lo:hi].float() == 3.0)
+
+
+# ---------------------------------------------------------------------------------------
+# Combine from identical expert outputs
+# ---------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+@pytest.mark.parametrize("N,E,k,cf", [(1, 4, 2, 0.0), (333, 8, 2, 0.0), (1000, 16, 4, 0.6), (64, 8, 8, 0.0)])
+def test_combine_from_identical_rows(orc, dt, N, E, k, cf):
+    padded = cf > 0
+    cfg = _routing_cfg(N, E, k, dtype=dt, D=256, capacity_mode="padded" if padded else "none",
+                       capacity_factor=cf if padded else 0.0)
+    d = B.make_desc(cfg)
+    idx, gate = inputs.make_topk(N, E, k, seed=5 + N, skew=1.0)
+    C = orc.capacity(N, E, k, cf, 0) if padded else None
+    o = orc.dispatch(idx, gate.double(), E, C, padded)
+    rows = B.moe_rows(d)
+    yp = inputs.make_rows(rows, 256, seed=N + 1, dtype=dt)
+    y = torch.empty((N, 256), dtype=yp.dtype, device=DEV)
+    B.moe_combine(d, yp.to(DEV), torch.from_numpy(o.row_of.astype(np.int32)).to(DEV),
+                  torch.from_numpy(o.gate_eff.astype(np.float32)).to(DEV), y)
+    torch.cuda.synchronize()
+    ref = orc.combine(yp.float().numpy(), o.row_of, o.gate_eff.astype(np.float32))
+    tol = 8e-3 if dt == "bf16" else 2e-6
+    assert_rows_close(host(y), ref, tol, "y")
+    gone = np.all(o.dropped == 1, axis=1)
+    assert np.all(host(y)[gone] == 0.0)
+
+
+# ---------------------------------------------------------------------------------------
+# The whole layer
+# ---------------------------------------------------------------------------------------
+
+_CACHE = {}
+
+
+def _workload(cfg):
+    key = cfg["name"]
+    if key not in _CACHE:
+        _CACHE.clear()
+        _CACHE[key] = inputs.make_inputs(cfg)
+    return _CACHE[key]
+
+
+def _check_layer(orc, cfg, sample=None, max_amb=16):
+    """Runs moe_forward and checks routing, dispatch and outputs against the oracle."""
+    inp = _workload(cfg)
+    layer = B.MoELayer(cfg, inp)
+    layer.forward()
+    torch.cuda.synchronize()
+    v = layer.views()
+    N, E, k = cfg["N"], cfg["E"], cfg["k"]
+    padded = cfg["capacity_mode"] == "padded"
+
+    logits = orc.router_logits(inp["x"], inp["w_r"], inp["logit_bias"])
+    r = orc.route(logits, k, cfg["routing_mode"], noise=inp["noise"] if cfg["second_choice"] == "noisy" else None)
+    C = orc.capacity(N, E, k, cfg["capacity_factor"], cfg["min_capacity"]) if padded else None
+    o = orc.dispatch(r.idx, r.gate, E, C, padded)
+
+    g_idx = host(v["topk_idx"])
+    amb = ambiguous_tokens(r)
+    assert len(amb) <= max_amb, f"{len(amb)} near-tie tokens"
+    clear = np.ones(N, bool)
+    clear[amb] = False
+    assert np.array_equal(g_idx[clear], r.idx[clear]), "routing differs on tokens with a clear margin"
+    np.testing.assert_allclose(host(v["topk_gate"])[clear], r.gate[clear], rtol=2e-5, atol=1e-6)
+
+    moved = affected_experts(r.idx, g_idx, amb)
+    stable = np.array([e not in moved for e in range(E)])
+    g_load, g_cnt = host(v["load"]), host(v["counts"])
+    g_off = host(v["offsets"]).astype(np.int64)
+    assert np.array_equal(g_load[stable], o.load[stable])
+    assert np.array_equal(g_cnt[stable], o.counts[stable])
+    assert g_load.sum() == N * k
+    g_row = host(v["row_of"]).astype(np.int64)
+    g_drop = host(v["dropped"])
+    rec_stable = stable[r.idx] & clear[:, None]
+    assert np.array_equal(g_drop[rec_stable], o.dropped[rec_stable])
+    gp = np.where(g_row >= 0, g_row - g_off[np.clip(g_idx, 0, E - 1)], -1)
+    op = np.where(o.row_of >= 0, o.row_of - o.offsets[r.idx], -1)
+    assert np.array_equal(gp[rec_stable], op[rec_stable]), "capacity slot positions differ"
+
+    tok_ok = clear & np.all(stable[r.idx], axis=1)
+    if sample is None:
+        toks = np.nonzero(tok_ok)[0]
+    else:
+        toks = np.array([t for t in sample if tok_ok[t]], np.int64)
+    y_ref = orc.layer_tokens(toks, inp["x"], inp["w1"], inp["w2"], inp["w3"], r.idx, o.dropped, o.gate_eff,
+                             cfg["activation"])
+    y = host(layer.y)[toks]
+    err = assert_rows_close(y, y_ref, TOL_Y[cfg["dtype"]], "layer output")
+    zero = np.all(o.dropped[toks] == 1, axis=1)
+    assert np.all(y[zero] == 0.0), "fully dropped tokens must have increment exactly 0"
+    return dict(layer=layer, routing=r, dispatch=o, amb=amb, err=err, toks=toks, inp=inp)
+
+
+MID = [
+    configs.scaled_config("tiny_fp32", N=64, D=128, F=256),
+    configs.scaled_config("tiny_fp32", N=301, D=256, F=384, E=8, k=3),
+    configs.scaled_config("mixtral_prefill", N=333, D=256, F=512),
+    configs.scaled_config("mixtral_prefill", N=1, D=128, F=128),
+    configs.scaled_config("grok1_layer", N=200, D=384, F=640),
+    configs.scaled_config("mixtral_decode", N=64, D=512, F=384),
+    configs.scaled_config("gshard_capacity", N=1000, D=256, F=384, E=16),
+    configs.scaled_config("gshard_capacity", N=777, D=128, F=256, E=64, capacity_factor=0.5, min_capacity=2),
+    configs.scaled_config("mixtral_prefill", N=257, D=128, F=256, E=1, k=1),
+    configs.scaled_config("mixtral_prefill", N=200, D=128, F=128, E=8, k=8, routing_mode="softmax_topk",
+                          activation="gelu_tanh"),
+]
+
+
+@pytest.mark.parametrize("cfg", MID, ids=lambda c: c["name"])
+def test_layer_mid_size(orc, cfg):
+    _check_layer(orc, cfg)
+
+
+def test_layer_bitwise_reproducible_and_equal_to_steps(orc):
+    cfg = configs.scaled_config("gshard_capacity", N=1000, D=256, F=384, E=16)
+    inp = inputs.make_inputs(cfg)
+    layer = B.MoELayer(cfg, inp)
+    y1 = layer.forward().clone()
+    y2 = layer.forward().clone()
+    assert torch.equal(y1, y2)
+    d = layer.desc
+    N, E, k, D, F = cfg["N"], cfg["E"], cfg["k"], cfg["D"], cfg["F"]
+    rows = B.moe_rows(d)
+    sc = torch.empty(B.moe_scratch_size(d), dtype=torch.uint8, device=DEV)
+    idx = torch.empty((N, k), dtype=torch.int32, device=DEV)
+    gate = torch.empty((N, k), dtype=torch.float32, device=DEV)
+    B.moe_route(d, layer.x, layer.w_r, layer.bias, layer.noise, None, None, None, idx, gate, sc)
+    out, _ = _run_dispatch(d, layer.x, idx, gate)
+    h = torch.empty((rows, F), dtype=layer.x.dtype, device=DEV)
+    yp = torch.empty((rows, D), dtype=layer.x.dtype, device=DEV)
+    B.moe_expert_up(d, out["x_perm"], out["offsets"], out["counts"], layer.w1, layer.w2, h, sc)
+    B.moe_expert_down(d, h, out["offsets"], out["counts"], layer.w3, yp, sc)
+    y3 = torch.empty_like(y1)
+    B.moe_combine(d, yp, out["row_of"], out["gate_eff"], y3)
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y3)
+
+
+@pytest.mark.parametrize("cfg", [configs.scaled_config("gshard_capacity", N=1000, D=256, F=384, E=16),
+                                 configs.scaled_config("mixtral_prefill", N=333, D=256, F=512)],
+                         ids=lambda c: c["name"])
+def test_stats(orc, cfg):
+    res = _check_layer(orc, cfg)
+    layer = res["layer"]
+    st = layer.stats()
+    v = layer.views()
+    o, r = res["dispatch"], res["routing"]
+    N, k, E = cfg["N"], cfg["k"], cfg["E"]
+    # the statistics describe the GPU's own routing exactly
+    g_drop = host(v["dropped"])
+    assert st["routed_slots"] == N * k
+    assert st["dropped_slots"] == int(g_drop.sum())
+    assert st["dropped_tokens"] == int(np.all(g_drop == 1, axis=1).sum())
+    assert st["drop_rate"] == pytest.approx(g_drop.mean(), rel=1e-12)
+    # and the oracle's up to the near-tie tokens (each can move k records)
+    n_amb = len(res["amb"])
+    assert abs(st["dropped_slots"] - int(o.dropped.sum())) <= n_amb * k
+    P, bal, bal_n = orc.balance(r.probs, o.load, k)
+    slack = n_amb * 2 * k * E * P.max() / (N * k)
+    assert abs(st["balance_loss"] - bal) <= 1e-5 * bal + slack
+    assert abs(st["balance_loss_div_n"] - bal_n) <= 1e-5 * bal_n + k * slack
+
+
+# ---- the five workloads at their full sizes ---------------------------------------------
+
+def _spread(N, n, extra=()):
+    s = set(np.linspace(0, N - 1, n).astype(int).tolist()) | set(extra)
+    return np.array(sorted(s), np.int64)
+
+
+@pytest.mark.slow
+def test_workload_tiny_fp32(orc):
+    _check_layer(orc, configs.get_config("tiny_fp32"))
+
+
+@pytest.mark.slow
+def test_workload_mixtral_prefill(orc):
+    cfg = configs.get_config("mixtral_prefill")
+    _check_layer(orc, cfg, sample=_spread(cfg["N"], 40, extra=(1, 63, 64, 4095)))
+
+
+@pytest.mark.slow
+def test_workload_mixtral_decode(orc):
+    res = _check_layer(orc, configs.get_config("mixtral_decode"))
+    load = res["dispatch"].load
+    assert (load == 0).sum() >= 1 and (load > 0).sum() >= 2, f"decode workload must leave an expert empty: {load}"
+
+
+@pytest.mark.slow
+def test_workload_gshard_capacity(orc):
+    cfg = configs.get_config("gshard_capacity")
+    inp = _workload(cfg)
+    # choose sampled tokens that cover every drop case, from the oracle's own dispatch
+    logits = orc.router_logits(inp["x"], inp["w_r"], inp["logit_bias"])
+    r = orc.route(logits, cfg["k"], cfg["routing_mode"], noise=inp["noise"])
+    o = orc.dispatch(r.idx, r.gate, cfg["E"], 640, True)
+    cases = {"kk": (0, 0), "kd": (0, 1), "dk": (1, 0), "dd": (1, 1)}
+    extra = []
+    for name, pat in cases.items():
+        m = np.nonzero((o.dropped[:, 0] == pat[0]) & (o.dropped[:, 1] == pat[1]))[0]
+        assert len(m) > 0, f"drop case {name} absent from the workload"
+        extra += m[:: max(1, len(m) // 8)][:8].tolist()
+    assert (o.load > 640).sum() >= 1
+    res = _check_layer(orc, cfg, sample=_spread(cfg["N"], 16, extra=extra))
+    st = res["layer"].stats()
+    assert st["capacity"] == 640
+    if len(res["amb"]) == 0:
+        assert st["dropped_slots"] == int(o.dropped.sum())
+
+
+@pytest.mark.slow
+def test_workload_grok1_layer(orc):
+    cfg = configs.get_config("grok1_layer")
+    res = _check_layer(orc, cfg, sample=_spread(cfg["N"], 12, extra=(8191,)))
+    gsum = host(res["layer"].views()["topk_gate"]).sum(axis=1)
+    assert np.all(gsum < 1.0)

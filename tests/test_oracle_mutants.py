@@ -26,7 +26,13 @@ MUTANTS = {
                       "out[d] += u * elem(w3, w_dtype, base_dn + d * F + f);"),
     "silu_sign": ("if (kind == ACT_SILU) return z / (1.0 + exp(-z));", "if (kind == ACT_SILU) return z / (1.0 + exp(z));"),
     "gelu_scale": ("return 0.5 * z * (1.0 + erf(z / sqrt(2.0)));", "return 0.5 * z * (1.0 + erf(z));"),
-    "act_on_w2_branch": ("const double u = oracle_act(act, h1[f]) * h2[f];", "const double u = h1[f] * oracle_act(act, h2[f]);"),
+    "act_on_w2_branch": ("h[f] = oracle_act(act, h1[f]) * h2[f];", "h[f] = h1[f] * oracle_act(act, h2[f]);"),
+    "combine_overwrites": ("y[t * D + d] += gate_eff[t * k + j] * y_perm[r * D + d];",
+                           "y[t * D + d] = gate_eff[t * k + j] * y_perm[r * D + d];"),
+    "combine_gate_slot0": ("y[t * D + d] += gate_eff[t * k + j] * y_perm[r * D + d];",
+                           "y[t * D + d] += gate_eff[t * k] * y_perm[r * D + d];"),
+    "rows_wrong_expert": ("xrows + i * D, w1, w2, w3, experts[i], out + i * D)",
+                          "xrows + i * D, w1, w2, w3, experts[0], out + i * D)"),
     "noise_on_slot0": ("val[e] = (j > 0 && noisy) ?", "val[e] = (noisy) ?"),
     "balance_f_div_n": ("b += ((double)load[e] / ((double)N * (double)k)) * P[e];", "b += ((double)load[e] / (double)N) * P[e];"),
     "mode_b_uses_probs": ("for (int32_t j = 0; j < k; ++j) gate[t * k + j] = exp((double)l32[idx[t * k + j]] - ref) / s;",
