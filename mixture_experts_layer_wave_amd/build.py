@@ -16,7 +16,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmoe_mi355x.so")
-SOURCES = ["router.hip", "dispatch.hip", "combine.hip", "gemm.hip", "moe_api.cpp"]
+SOURCES = ["router.hip", "dispatch.hip", "combine.hip", "gemm_f32.hip", "gemm_bf16.hip", "moe_api.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
     "-x", "hip", "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

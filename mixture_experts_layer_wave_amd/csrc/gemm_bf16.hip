@@ -1,0 +1,295 @@
+// gemm_bf16.hip: bf16 grouped GEMMs of the expert FFN on gfx950 matrix cores.
+//
+// Method ("第 12 章 MoE：路由、专家与负载" §12.1 gated FFN f_e(x) = [SiLU(x W1_e) * (x W2_e)] W3_e
+// with W1, W2 [D,F] and W3 [F,D]; "第 5 章 model.py 精读·中：MoE 路由与专家" §5.3.5 the same form
+// with GELU, and §5.3.2 the expert weights stacked on a leading expert axis):
+//   up   : h[r,:]      = act(x_perm[r,:] W1_e) * (x_perm[r,:] W2_e)
+//   down : y_perm[r,:] = h[r,:] W3_e
+// for the rows r of each expert e (rows [offsets[e], offsets[e] + counts[e])).
+//
+// Design.
+//  * Work unit: a BM x (NB * BNF) output tile of one expert, computed by 4 waves (2 x 2);
+//    each wave owns a 128 x 128 accumulator block (NB matrices x 128 rows x BNF/2 columns)
+//    of fp32 MFMA accumulators, 256 per lane. The up projection has NB = 2: the W1 and W2
+//    tiles of the same columns sit side by side, so act(.) * (.) is formed in registers
+//    and h is stored once in bf16.
+//  * v_mfma_f32_32x32x16_bf16 with the operands swapped (weights as the first operand),
+//    so each lane ends with 4 consecutive output columns of one row and stores 8 bytes.
+//  * K loop over 64-wide slices, double-buffered in LDS. A (K contiguous) is read with
+//    ds_read_b128 from rows padded by 16 bytes. B (weights stored N contiguous) keeps its
+//    natural layout and is fed to the MFMA by the gfx950 transposing read
+//    ds_read_b64_tr_b16; rows are padded to 64 bytes modulo 256 so the four rows of a
+//    transposing read land in distinct banks. Fragments of the next 16-wide step are read
+//    while the current step's MFMAs issue. Global loads of slice k+2 are issued as soon as
+//    slice k+1 is written to LDS.
+//  * Persistent, XCD-aware schedule: the grid is a multiple of 8 workgroups; workgroup b
+//    runs on XCD b mod 8 and walks a contiguous eighth of the tile list, so the tiles
+//    sharing one expert's activations and weight columns run concurrently inside one
+//    XCD's L2.
+#include "gemm_common.h"
+
+namespace moe {
+namespace {
+
+typedef short i16x8 __attribute__((ext_vector_type(8)));
+typedef i16x4 __attribute__((address_space(3))) * lds_i16x4_ptr;
+
+constexpr int kXcds = 8;
+
+__device__ __forceinline__ bf16x8 tr_read_b16x8(const bf16* q, int row_stride) {
+  const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_ptr)(q));
+  const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_ptr)(q + 4 * row_stride));
+  const i16x8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+// Direct-to-LDS copy of 16 bytes per lane (global_load_lds_dwordx4): lane l's bytes land
+// at LDS byte address lds_addr + 16 l; lds_addr is wave-uniform and goes through M0.
+// Written as inline asm so the compiler does not treat the in-flight copy as a pending
+// write to every LDS location (it would then wait for all copies before each LDS read);
+// completion is tracked explicitly with wait_vmcnt. The instruction has no destination
+// register, and the leading s_nop covers the M0-write to LDS-DMA hazard.
+__device__ __forceinline__ void load_lds16(const void* gptr, uint32_t lds_addr) {
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gptr), "{m0}"(lds_addr) : "memory");
+}
+
+// Waits until at most N of this wave's vector-memory operations are outstanding.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N <= 63, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Workgroup barrier without the memory fence of __syncthreads() (the fence would wait for
+// every copy in flight). Visibility is explicit: each wave waits for its own copies of a
+// slice before the barrier, and for its own LDS reads (lgkmcnt(0)) so that no read of a
+// stage is still pending when another wave's copy refills that stage after the barrier.
+__device__ __forceinline__ void barrier_no_fence() {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+__device__ __forceinline__ uint32_t lds_addr_of(const bf16* p) {
+  return (uint32_t)(uintptr_t)((const __attribute__((address_space(3))) bf16*)p);
+}
+
+template <int BM, int BNF, int NB, int ACT>
+__global__ __launch_bounds__(512, 1) void k_gemm_bf16(const GemmParams p) {
+  constexpr int BK = 32;                    // K slice per pipeline stage
+  constexpr int STAGES = 4;                 // LDS ring: 3 slices in flight
+  constexpr int WM = BM / 2, WN = BNF / 4;  // wave tile per matrix
+  constexpr int TM = WM / 32, TN = WN / 32;
+  constexpr int A_EL = BM * BK, B_EL = BK * BNF;
+  constexpr int STAGE = A_EL + NB * B_EL;
+  constexpr int A_CP = A_EL * 2 / 1024 / 8;         // 1 KB copies per wave per slice
+  constexpr int B_CPM = B_EL * 2 / 1024;            // 1 KB copies per matrix per slice
+  constexpr int B_CP = NB * B_CPM / 8;              // B copies per wave per slice
+  constexpr int LOADS = A_CP + B_CP;
+  constexpr int B_RPC = 1024 / (BNF * 2);           // B rows per copy
+  constexpr int B_CPR = BNF / 8;                    // 16-byte chunks per B row
+  static_assert(BM == 256 && (BNF == 128 || BNF == 256), "tile shape");
+  static_assert(A_CP >= 1 && B_CP >= 1 && TM >= 1 && TN >= 1 && (NB * B_CPM) % 8 == 0, "tile shape");
+
+  __shared__ __attribute__((aligned(1024))) bf16 ring[STAGES * STAGE];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wid = uniform(tid >> 6);
+  const int wm = wid >> 2, wn = wid & 3;
+  const int K = p.K, N = p.N;
+  const int nk = K / BK;
+
+  const TileScan ts = tile_scan<BM>(p);
+  const int xcd = blockIdx.x % kXcds;
+  const int slot = blockIdx.x / kXcds;
+  const int nslot = gridDim.x / kXcds;
+  const int lo = (int)((int64_t)ts.total * xcd / kXcds);
+  const int hi = (int)((int64_t)ts.total * (xcd + 1) / kXcds);
+
+  // LDS layouts (no padding; 16-byte chunks XOR-swizzled so the MFMA operand reads are
+  // bank-conflict free):
+  //   A [BM][BK]: row r, logical chunk c (8 elements) at physical chunk c ^ ((r / 4) % 4).
+  //   B [BK][BNF]: row k, logical 32-byte segment g at physical segment g ^ (2 (k % 4)).
+  // Fragment addresses (constant per lane):
+  //   A: lane -> row (lane % 32) of each 32-row block, k chunk 2 kk + lane / 32.
+  //   B: transposing read; 16-lane group G -> column half (G & 1), k-half (G >> 1); lane s
+  //      of the group supplies row s / 4 and columns 4 (s % 4) .. +3 of a 4 x 16 block.
+  const int a_row = wm * WM + (lane & 31);
+  const int a_swz = ((lane & 31) >> 2) & 3;
+  const int G = lane >> 4, s16 = lane & 15;
+  const int b_row = 8 * (G >> 1) + (s16 >> 2);
+  const int b_swz = 2 * (s16 >> 2);
+  const int b_seg = (wn * WN) / 16 + (G & 1);
+  const int b_in = 4 * (s16 & 3);
+
+  // Copy coordinates. A copy c covers rows 16 c .. +15: lane -> row 16 c + lane / 4 and
+  // physical chunk lane % 4, which holds logical chunk (lane % 4) ^ (lane / 16).
+  // B copy c (matrix c / B_CPM) covers rows B_RPC (c % B_CPM) ..: lane -> row + lane /
+  // B_CPR and physical chunk pc = lane % B_CPR, holding logical chunk 2 ((pc / 2) ^ h) +
+  // (pc & 1) with h = 2 (row % 4).
+  const int a_cp_col = 8 * ((lane & 3) ^ (lane >> 4));
+  const int ring_addr = (int)lds_addr_of(ring);
+
+  for (int L = lo + slot; L < hi; L += nslot) {
+    Tile tl;
+    if (!tile_of<BM, BNF>(p, ts, L, tl)) continue;
+
+    const bf16* Ag = reinterpret_cast<const bf16*>(p.A) + tl.row_base * K;
+    const int64_t boff = (int64_t)tl.e * K * N + tl.n0;
+    const int mlast = tl.mcount - 1;  // rows past the expert's count re-read a valid row
+
+    const bf16* a_src[A_CP];
+#pragma unroll
+    for (int q = 0; q < A_CP; ++q) {
+      const int c = A_CP * wid + q;
+      const int rr = min(16 * c + (lane >> 2), mlast);
+      a_src[q] = Ag + (int64_t)rr * K + a_cp_col;
+    }
+    const bf16* b_src[B_CP];
+#pragma unroll
+    for (int q = 0; q < B_CP; ++q) {
+      const int c = B_CP * wid + q;
+      const int m = c / B_CPM;
+      const int row = B_RPC * (c % B_CPM) + lane / B_CPR;
+      const int pc = lane % B_CPR;
+      const int lc = 2 * ((pc >> 1) ^ (2 * (row & 3))) + (pc & 1);
+      const bf16* Bm = reinterpret_cast<const bf16*>(m == 0 ? p.B0 : p.B1);
+      b_src[q] = Bm + boff + (int64_t)row * N + 8 * lc;
+    }
+
+    auto issue_slice = [&](int kt) {
+      const int k0 = kt * BK;
+      const int base = ring_addr + (kt % STAGES) * STAGE * 2;
+#pragma unroll
+      for (int q = 0; q < A_CP; ++q) load_lds16(a_src[q] + k0, (uint32_t)uniform(base + (A_CP * wid + q) * 1024));
+#pragma unroll
+      for (int q = 0; q < B_CP; ++q)
+        load_lds16(b_src[q] + (int64_t)k0 * N, (uint32_t)uniform(base + A_EL * 2 + (B_CP * wid + q) * 1024));
+    };
+
+    f32x16 acc[NB][TM][TN];
+#pragma unroll
+    for (int m = 0; m < NB; ++m)
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[m][i][j][r] = 0.f;
+
+#pragma unroll
+    for (int st = 0; st < STAGES - 1; ++st)
+      if (st < nk) issue_slice(st);
+
+    for (int kt = 0; kt < nk; ++kt) {
+      // Slice kt has landed once at most (slices issued after it) * LOADS copies remain.
+      const int ahead = min(STAGES - 2, nk - 1 - kt);
+      if (ahead >= 2) wait_vmcnt<2 * LOADS>();
+      else if (ahead == 1) wait_vmcnt<LOADS>();
+      else wait_vmcnt<0>();
+      barrier_no_fence();  // slice kt visible to every wave; slice kt-1 fully consumed
+      if (kt + STAGES - 1 < nk) issue_slice(kt + STAGES - 1);
+
+      const bf16* As = ring + (kt % STAGES) * STAGE;
+      bf16x8 af[BK / 16][TM], bfr[BK / 16][NB][TN];
+#pragma unroll
+      for (int kk = 0; kk < BK / 16; ++kk) {
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+          af[kk][i] = *reinterpret_cast<const bf16x8*>(As + (a_row + 32 * i) * BK + 8 * ((2 * kk + (lane >> 5)) ^ a_swz));
+#pragma unroll
+        for (int m = 0; m < NB; ++m)
+#pragma unroll
+          for (int j = 0; j < TN; ++j)
+            bfr[kk][m][j] = tr_read_b16x8(As + A_EL + m * B_EL + (kk * 16 + b_row) * BNF +
+                                              16 * ((b_seg + 2 * j) ^ b_swz) + b_in, BNF);
+      }
+#pragma unroll
+      for (int kk = 0; kk < BK / 16; ++kk)
+#pragma unroll
+        for (int m = 0; m < NB; ++m)
+#pragma unroll
+          for (int j = 0; j < TN; ++j)
+#pragma unroll
+            for (int i = 0; i < TM; ++i)
+              acc[m][i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[kk][m][j], af[kk][i], acc[m][i][j], 0, 0, 0);
+    }
+    wait_vmcnt<0>();
+    __syncthreads();  // every wave done reading the ring before the next tile refills it
+
+    // Epilogue. With the operands swapped, accumulator element r of a lane holds row
+    // lane % 32 and column 8 * (r / 4) + 4 * (lane / 32) + r % 4 of its 32 x 32 block.
+    bf16* Cg = reinterpret_cast<bf16*>(p.C) + tl.row_base * N + tl.n0;
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      const int row = wm * WM + 32 * i + (lane & 31);
+      if (row >= tl.mcount) continue;
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int col = wn * WN + 32 * j + 8 * q + 4 * (lane >> 5);
+          bf16x4 o;
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            float v;
+            if constexpr (NB == 2) v = activate<ACT>(acc[0][i][j][4 * q + u]) * acc[1][i][j][4 * q + u];
+            else v = acc[0][i][j][4 * q + u];
+            o[u] = (bf16)v;
+          }
+          *reinterpret_cast<bf16x4*>(Cg + (int64_t)row * N + col) = o;
+        }
+    }
+  }
+}
+
+int g_num_cus = 0;
+
+int persistent_grid(int64_t tiles_bound) {
+  if (g_num_cus <= 0) {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    g_num_cus = n;
+  }
+  int64_t g = tiles_bound < g_num_cus ? tiles_bound : g_num_cus;
+  g = (g + kXcds - 1) / kXcds * kXcds;
+  return (int)g;
+}
+
+template <int BM, int BNF, int NB>
+hipError_t launch_bf16(const GemmParams& p, int act, int64_t mtiles, hipStream_t s) {
+  const int64_t bound = mtiles * p.n_tiles;
+  if (bound <= 0) return hipSuccess;
+  const dim3 grid((unsigned)persistent_grid(bound)), block(512);
+  if constexpr (NB == 2) {
+    if (act == ACT_SILU) hipLaunchKernelGGL((k_gemm_bf16<BM, BNF, 2, ACT_SILU>), grid, block, 0, s, p);
+    else if (act == ACT_GELU_ERF) hipLaunchKernelGGL((k_gemm_bf16<BM, BNF, 2, ACT_GELU_ERF>), grid, block, 0, s, p);
+    else hipLaunchKernelGGL((k_gemm_bf16<BM, BNF, 2, ACT_GELU_TANH>), grid, block, 0, s, p);
+  } else {
+    hipLaunchKernelGGL((k_gemm_bf16<BM, BNF, 1, ACT_SILU>), grid, block, 0, s, p);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_expert_up(const FfnArgs& a, bool bf16_io, hipStream_t s) {
+  if (!bf16_io) return launch_gemm_f32(a, true, s);
+  constexpr int BM = 256, BNF = 128;
+  GemmParams p{a.x_perm, a.w1, a.w2, a.h, a.offsets, a.counts, a.E, a.D, a.F, a.F / BNF, a.rows};
+  return launch_bf16<BM, BNF, 2>(p, a.act, max_m_tiles(a, BM), s);
+}
+
+hipError_t launch_expert_down(const FfnArgs& a, bool bf16_io, hipStream_t s) {
+  if (!bf16_io) return launch_gemm_f32(a, false, s);
+  // 256 x 128 tiles: D is narrow, so wider tiles would leave too few tiles for the last
+  // round over the compute units.
+  constexpr int BM = 256;
+  GemmParams p{a.h, a.w3, nullptr, a.y_perm, a.offsets, a.counts, a.E, a.F, a.D, a.D / 128, a.rows};
+  return launch_bf16<BM, 128, 1>(p, a.act, max_m_tiles(a, BM), s);
+}
+
+}  // namespace moe
