@@ -36,6 +36,14 @@ typedef i16x4 __attribute__((address_space(3))) * lds_i16x4_ptr;
 
 constexpr int kXcds = 8;
 
+// Pipeline shape of the grouped GEMM: K slice per LDS stage and ring depth.
+#ifndef MOE_GEMM_BK
+#define MOE_GEMM_BK 64
+#endif
+#ifndef MOE_GEMM_STAGES
+#define MOE_GEMM_STAGES 2
+#endif
+
 __device__ __forceinline__ bf16x8 tr_read_b16x8(const bf16* q, int row_stride) {
   const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_ptr)(q));
   const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_ptr)(q + 4 * row_stride));
@@ -74,10 +82,19 @@ __device__ __forceinline__ uint32_t lds_addr_of(const bf16* p) {
   return (uint32_t)(uintptr_t)((const __attribute__((address_space(3))) bf16*)p);
 }
 
-template <int BM, int BNF, int NB, int ACT>
+// Waits until this wave's copies of the slice `ahead` slices before the newest issued
+// one have landed (each slice is LOADS copies per wave).
+template <int LOADS>
+__device__ __forceinline__ void wait_for_slice(int ahead) {
+  if (ahead >= 3) wait_vmcnt<3 * LOADS>();
+  else if (ahead == 2) wait_vmcnt<2 * LOADS>();
+  else if (ahead == 1) wait_vmcnt<LOADS>();
+  else wait_vmcnt<0>();
+}
+
+template <int BM, int BNF, int NB, int ACT, int BK, int STAGES>
 __global__ __launch_bounds__(512, 1) void k_gemm_bf16(const GemmParams p) {
-  constexpr int BK = 32;                    // K slice per pipeline stage
-  constexpr int STAGES = 4;                 // LDS ring: 3 slices in flight
+  // BK: K slice per pipeline stage; STAGES: LDS ring depth (STAGES-1 slices in flight).
   constexpr int WM = BM / 2, WN = BNF / 4;  // wave tile per matrix
   constexpr int TM = WM / 32, TN = WN / 32;
   constexpr int A_EL = BM * BK, B_EL = BK * BNF;
@@ -88,7 +105,11 @@ __global__ __launch_bounds__(512, 1) void k_gemm_bf16(const GemmParams p) {
   constexpr int LOADS = A_CP + B_CP;
   constexpr int B_RPC = 1024 / (BNF * 2);           // B rows per copy
   constexpr int B_CPR = BNF / 8;                    // 16-byte chunks per B row
-  static_assert(BM == 256 && (BNF == 128 || BNF == 256), "tile shape");
+  constexpr int A_CPR = BK / 8;                     // 16-byte chunks per A row
+  constexpr int A_RPB = 128 / BK;                   // A rows per 256 bytes (64 banks)
+  constexpr int A_RPC = 512 / BK;                   // A rows per 1 KB copy
+  static_assert(BM == 256 && (BNF == 128 || BNF == 256) && (BK == 32 || BK == 64), "tile shape");
+  static_assert(STAGES >= 2 && STAGES <= 5 && STAGES * STAGE * 2 <= 160 * 1024, "LDS ring");
   static_assert(A_CP >= 1 && B_CP >= 1 && TM >= 1 && TN >= 1 && (NB * B_CPM) % 8 == 0, "tile shape");
 
   __shared__ __attribute__((aligned(1024))) bf16 ring[STAGES * STAGE];
@@ -109,26 +130,26 @@ __global__ __launch_bounds__(512, 1) void k_gemm_bf16(const GemmParams p) {
 
   // LDS layouts (no padding; 16-byte chunks XOR-swizzled so the MFMA operand reads are
   // bank-conflict free):
-  //   A [BM][BK]: row r, logical chunk c (8 elements) at physical chunk c ^ ((r / 4) % 4).
+  //   A [BM][BK]: row r, logical chunk c (8 elements) at physical chunk c ^ f(r),
+  //               f(r) = (r / A_RPB) % A_CPR, so 16 consecutive rows hit 16 bank groups.
   //   B [BK][BNF]: row k, logical 32-byte segment g at physical segment g ^ (2 (k % 4)).
   // Fragment addresses (constant per lane):
   //   A: lane -> row (lane % 32) of each 32-row block, k chunk 2 kk + lane / 32.
   //   B: transposing read; 16-lane group G -> column half (G & 1), k-half (G >> 1); lane s
   //      of the group supplies row s / 4 and columns 4 (s % 4) .. +3 of a 4 x 16 block.
   const int a_row = wm * WM + (lane & 31);
-  const int a_swz = ((lane & 31) >> 2) & 3;
+  const int a_swz = ((lane & 31) / A_RPB) % A_CPR;
   const int G = lane >> 4, s16 = lane & 15;
   const int b_row = 8 * (G >> 1) + (s16 >> 2);
   const int b_swz = 2 * (s16 >> 2);
   const int b_seg = (wn * WN) / 16 + (G & 1);
   const int b_in = 4 * (s16 & 3);
 
-  // Copy coordinates. A copy c covers rows 16 c .. +15: lane -> row 16 c + lane / 4 and
-  // physical chunk lane % 4, which holds logical chunk (lane % 4) ^ (lane / 16).
+  // Copy coordinates. A copy c covers rows A_RPC c ..: lane -> row A_RPC c + lane / A_CPR
+  // and physical chunk lane % A_CPR, which holds logical chunk (lane % A_CPR) ^ f(row).
   // B copy c (matrix c / B_CPM) covers rows B_RPC (c % B_CPM) ..: lane -> row + lane /
   // B_CPR and physical chunk pc = lane % B_CPR, holding logical chunk 2 ((pc / 2) ^ h) +
   // (pc & 1) with h = 2 (row % 4).
-  const int a_cp_col = 8 * ((lane & 3) ^ (lane >> 4));
   const int ring_addr = (int)lds_addr_of(ring);
 
   for (int L = lo + slot; L < hi; L += nslot) {
@@ -143,8 +164,9 @@ __global__ __launch_bounds__(512, 1) void k_gemm_bf16(const GemmParams p) {
 #pragma unroll
     for (int q = 0; q < A_CP; ++q) {
       const int c = A_CP * wid + q;
-      const int rr = min(16 * c + (lane >> 2), mlast);
-      a_src[q] = Ag + (int64_t)rr * K + a_cp_col;
+      const int row = A_RPC * c + lane / A_CPR;
+      const int lc = (lane % A_CPR) ^ ((row / A_RPB) % A_CPR);
+      a_src[q] = Ag + (int64_t)min(row, mlast) * K + 8 * lc;
     }
     const bf16* b_src[B_CP];
 #pragma unroll
@@ -184,10 +206,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm_bf16(const GemmParams p) {
 
     for (int kt = 0; kt < nk; ++kt) {
       // Slice kt has landed once at most (slices issued after it) * LOADS copies remain.
-      const int ahead = min(STAGES - 2, nk - 1 - kt);
-      if (ahead >= 2) wait_vmcnt<2 * LOADS>();
-      else if (ahead == 1) wait_vmcnt<LOADS>();
-      else wait_vmcnt<0>();
+      wait_for_slice<LOADS>(min(STAGES - 2, nk - 1 - kt));
       barrier_no_fence();  // slice kt visible to every wave; slice kt-1 fully consumed
       if (kt + STAGES - 1 < nk) issue_slice(kt + STAGES - 1);
 
@@ -259,17 +278,17 @@ int persistent_grid(int64_t tiles_bound) {
   return (int)g;
 }
 
-template <int BM, int BNF, int NB>
+template <int BM, int BNF, int NB, int BK = MOE_GEMM_BK, int STAGES = MOE_GEMM_STAGES>
 hipError_t launch_bf16(const GemmParams& p, int act, int64_t mtiles, hipStream_t s) {
   const int64_t bound = mtiles * p.n_tiles;
   if (bound <= 0) return hipSuccess;
   const dim3 grid((unsigned)persistent_grid(bound)), block(512);
   if constexpr (NB == 2) {
-    if (act == ACT_SILU) hipLaunchKernelGGL((k_gemm_bf16<BM, BNF, 2, ACT_SILU>), grid, block, 0, s, p);
-    else if (act == ACT_GELU_ERF) hipLaunchKernelGGL((k_gemm_bf16<BM, BNF, 2, ACT_GELU_ERF>), grid, block, 0, s, p);
-    else hipLaunchKernelGGL((k_gemm_bf16<BM, BNF, 2, ACT_GELU_TANH>), grid, block, 0, s, p);
+    if (act == ACT_SILU) hipLaunchKernelGGL((k_gemm_bf16<BM, BNF, 2, ACT_SILU, BK, STAGES>), grid, block, 0, s, p);
+    else if (act == ACT_GELU_ERF) hipLaunchKernelGGL((k_gemm_bf16<BM, BNF, 2, ACT_GELU_ERF, BK, STAGES>), grid, block, 0, s, p);
+    else hipLaunchKernelGGL((k_gemm_bf16<BM, BNF, 2, ACT_GELU_TANH, BK, STAGES>), grid, block, 0, s, p);
   } else {
-    hipLaunchKernelGGL((k_gemm_bf16<BM, BNF, 1, ACT_SILU>), grid, block, 0, s, p);
+    hipLaunchKernelGGL((k_gemm_bf16<BM, BNF, 1, ACT_SILU, BK, STAGES>), grid, block, 0, s, p);
   }
   return hipGetLastError();
 }
@@ -285,9 +304,11 @@ hipError_t launch_expert_up(const FfnArgs& a, bool bf16_io, hipStream_t s) {
 
 hipError_t launch_expert_down(const FfnArgs& a, bool bf16_io, hipStream_t s) {
   if (!bf16_io) return launch_gemm_f32(a, false, s);
-  // 256 x 128 tiles: D is narrow, so wider tiles would leave too few tiles for the last
-  // round over the compute units.
   constexpr int BM = 256;
+  if (a.D % 256 == 0) {
+    GemmParams p{a.h, a.w3, nullptr, a.y_perm, a.offsets, a.counts, a.E, a.F, a.D, a.D / 256, a.rows};
+    return launch_bf16<BM, 256, 1>(p, a.act, max_m_tiles(a, BM), s);
+  }
   GemmParams p{a.h, a.w3, nullptr, a.y_perm, a.offsets, a.counts, a.E, a.F, a.D, a.D / 128, a.rows};
   return launch_bf16<BM, 128, 1>(p, a.act, max_m_tiles(a, BM), s);
 }

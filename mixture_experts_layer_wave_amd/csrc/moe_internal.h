@@ -8,7 +8,7 @@
 
 namespace moe {
 
-constexpr int kRouterTokens = 64;     // tokens per router workgroup
+constexpr int kRouterTokens = 32;     // tokens per router workgroup
 constexpr int kDispatchTokens = 256;  // tokens per dispatch workgroup
 constexpr int kMaxE = 64;
 constexpr int kMaxK = 8;

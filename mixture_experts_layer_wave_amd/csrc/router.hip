@@ -9,20 +9,22 @@
 //   gates = p of the chosen experts (softmax-then-top-k) or softmax over the chosen
 //   logits (top-k-then-softmax, the renormalised form).
 //
-// Design: a workgroup owns 64 tokens, one per lane; its 4 waves split D into quarters
-// so each lane keeps E fp32 accumulators for its token. The W_r rows of the current
-// chunk are staged in LDS and read as wave-wide broadcasts (every lane of a wave reads
-// the same address). The four quarter sums are added in a fixed order, so logits are
-// bit-reproducible. Selection runs in registers on the lane that owns the token: no
-// cross-lane traffic and no atomics.
+// Design: a workgroup owns 32 tokens and its 8 waves split D into 8 equal ranges. Each
+// wave accumulates the 32 x (32 or 64) logit block of its range with v_mfma_f32_32x32x2_f32
+// (fp32 products, fp32 accumulation): lane l feeds x[token l % 32][k] and
+// W_r[k][expert l % 32] for the k of its half (l / 32), so W_r rows are read coalesced and
+// x rows with 16-byte loads. The 8 partial blocks meet in LDS and are added in a fixed
+// order (wave 0 .. 7), so logits are bit-reproducible. Softmax, selection and gates then
+// run in registers on one lane per token: no cross-lane traffic and no atomics.
 #include "moe_device.h"
 #include "moe_internal.h"
 
 namespace moe {
 namespace {
 
-constexpr int kTM = kRouterTokens;  // tokens per workgroup = lanes of a wave
-constexpr int kDC = 16;             // D rows per chunk per wave
+constexpr int kTM = kRouterTokens;  // tokens per workgroup (32)
+constexpr int kWaves = 8;
+constexpr int kKC = 32;             // K chunk per pipeline step: 16 MFMAs of K = 2
 
 template <int EP>
 __device__ __forceinline__ float pick(const float (&v)[EP], int i) {
@@ -32,100 +34,142 @@ __device__ __forceinline__ float pick(const float (&v)[EP], int i) {
   return r;
 }
 
+// Raw chunk of kKC x elements (as 16-byte words) and the W_r values one lane needs.
 template <typename XT>
-__device__ __forceinline__ void load_chunk(const XT* p, float (&xv)[kDC]);
-
-template <>
-__device__ __forceinline__ void load_chunk<float>(const float* p, float (&xv)[kDC]) {
-  const f32x4* q = reinterpret_cast<const f32x4*>(p);
+struct XChunk {
+  static constexpr int kWords = kKC * sizeof(XT) / 16;
+  u32x4 w[kWords];
+  __device__ __forceinline__ void load(const XT* p) {
+    const u32x4* q = reinterpret_cast<const u32x4*>(p);
 #pragma unroll
-  for (int i = 0; i < kDC / 4; ++i) {
-    f32x4 v = q[i];
-    xv[4 * i + 0] = v[0]; xv[4 * i + 1] = v[1]; xv[4 * i + 2] = v[2]; xv[4 * i + 3] = v[3];
+    for (int i = 0; i < kWords; ++i) w[i] = q[i];
   }
-}
-
-template <>
-__device__ __forceinline__ void load_chunk<bf16>(const bf16* p, float (&xv)[kDC]) {
-  const bf16x8* q = reinterpret_cast<const bf16x8*>(p);
-#pragma unroll
-  for (int i = 0; i < kDC / 8; ++i) {
-    bf16x8 v = q[i];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) xv[8 * i + j] = (float)v[j];
+  __device__ __forceinline__ float at(int i) const {  // element i as fp32 (i constant)
+    if constexpr (sizeof(XT) == 2) {
+      const uint32_t u = w[i / 8][(i % 8) / 2];
+      return __uint_as_float((i & 1) ? (u & 0xffff0000u) : (u << 16));
+    } else {
+      return __uint_as_float(w[i / 4][i % 4]);
+    }
   }
-}
+};
 
-template <int EP, typename XT, bool FROM_LOGITS>
-__global__ __launch_bounds__(256) void k_router(const RouterArgs a) {
-  __shared__ float wr_s[4][kDC][EP];
-  __shared__ float red_s[3][EP][kTM];
+// NT: 32-expert column tiles (E <= 32 * NT); EP: register array width of the epilogue.
+template <int NT, int EP, typename XT, bool FROM_LOGITS>
+__global__ __launch_bounds__(512) void k_router(const RouterArgs a) {
+  __shared__ float red_s[kWaves][NT][16][64];  // partial logit blocks, lane-contiguous
   __shared__ float ps_s[EP][kTM];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = uniform(tid >> 6);
   const int E = a.E;
-  const int64_t t = (int64_t)blockIdx.x * kTM + lane;
-  const bool valid = t < a.N;
-
-  float acc[EP];
-#pragma unroll
-  for (int e = 0; e < EP; ++e) acc[e] = 0.f;
+  const int64_t t0 = (int64_t)blockIdx.x * kTM;
 
   if constexpr (!FROM_LOGITS) {
-    const int Dq = a.D / 4;
-    const XT* xrow = reinterpret_cast<const XT*>(a.x) + (valid ? t : 0) * (int64_t)a.D + (int64_t)w * Dq;
-    for (int c = 0; c < Dq; c += kDC) {
-      for (int i = tid; i < 4 * kDC * EP; i += 256) {
-        const int ww = i / (kDC * EP), r = (i / EP) % kDC, e = i % EP;
-        wr_s[ww][r][e] = e < E ? a.w_r[(int64_t)(ww * Dq + c + r) * E + e] : 0.f;
+    f32x16 acc[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[nt][r] = 0.f;
+    const int m = lane & 31, g = lane >> 5;
+    const int64_t trow = min(t0 + m, a.N - 1);  // tail tokens re-read a valid row
+    const int Dw = a.D / kWaves;                 // a multiple of 16
+    const XT* xrow = reinterpret_cast<const XT*>(a.x) + trow * (int64_t)a.D + (int64_t)w * Dw;
+    const float* wr = a.w_r + (int64_t)w * Dw * E;
+    // Two chunks in flight: the loads of chunk c + kKC are issued before the MFMAs of c.
+    XChunk<XT> xc[2];
+    float wv[2][kKC / 2][NT];
+    auto load = [&](int buf, int c) {
+      xc[buf].load(xrow + c);
+#pragma unroll
+      for (int s = 0; s < kKC / 2; ++s)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+          const int e = nt * 32 + m;
+          wv[buf][s][nt] = e < E ? wr[(int64_t)(c + 2 * s + g) * E + e] : 0.f;
+        }
+    };
+    auto compute = [&](int buf) {
+#pragma unroll
+      for (int s = 0; s < kKC / 2; ++s) {
+        const float xa = g ? xc[buf].at(2 * s + 1) : xc[buf].at(2 * s);
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+          acc[nt] = __builtin_amdgcn_mfma_f32_32x32x2f32(xa, wv[buf][s][nt], acc[nt], 0, 0, 0);
       }
-      __syncthreads();
-      float xv[kDC];
-      load_chunk<XT>(xrow + c, xv);
-#pragma unroll
-      for (int r = 0; r < kDC; ++r) {
-#pragma unroll
-        for (int e = 0; e < EP; ++e) acc[e] = fmaf(xv[r], wr_s[w][r][e], acc[e]);
+    };
+    // Dw is a multiple of 16; a final partial chunk is handled 16 at a time below.
+    const int full = Dw / kKC * kKC;
+    if (full > 0) load(0, 0);
+    for (int c = 0; c < full; c += 2 * kKC) {
+      if (c + kKC < full) load(1, c + kKC);
+      compute(0);
+      if (c + kKC < full) {
+        if (c + 2 * kKC < full) load(0, c + 2 * kKC);
+        compute(1);
       }
-      __syncthreads();
     }
-    if (w > 0) {
+    for (int c = full; c < Dw; c += 16) {
 #pragma unroll
-      for (int e = 0; e < EP; ++e) red_s[w - 1][e][lane] = acc[e];
-    }
-    __syncthreads();
-    if (w == 0) {
+      for (int s = 0; s < 8; ++s) {
+        const int k = c + 2 * s + g;
+        const float xa = (float)xrow[k];
 #pragma unroll
-      for (int e = 0; e < EP; ++e) acc[e] = ((acc[e] + red_s[0][e][lane]) + red_s[1][e][lane]) + red_s[2][e][lane];
+        for (int nt = 0; nt < NT; ++nt) {
+          const int e = nt * 32 + m;
+          const float wb = e < E ? wr[(int64_t)k * E + e] : 0.f;
+          acc[nt] = __builtin_amdgcn_mfma_f32_32x32x2f32(xa, wb, acc[nt], 0, 0, 0);
+        }
+      }
     }
-  } else {
-    if (w == 0 && valid) {
 #pragma unroll
-      for (int e = 0; e < EP; ++e) acc[e] = e < E ? a.logits_in[t * E + e] : 0.f;
-    }
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) red_s[w][nt][r][lane] = acc[nt][r];
   }
+  __syncthreads();
 
-  if (w == 0) {
-    float l[EP], p[EP];
+  // Epilogue: lane t (< 32) of wave 0 owns token t0 + t.
+  float p[EP];
+#pragma unroll
+  for (int e = 0; e < EP; ++e) p[e] = 0.f;
+  const int64_t t = t0 + lane;
+  const bool valid = (w == 0) && (lane < kTM) && (t < a.N);
+  if (w == 0 && lane < kTM) {
+    float l[EP];
+    // Accumulator element r of lane l' holds row 8 (r / 4) + 4 (l' / 32) + r % 4 and
+    // column l' % 32 of the 32 x 32 block.
+    const int r_of = 4 * (lane >> 3) + (lane & 3);
+    const int lhi = 32 * ((lane >> 2) & 1);
 #pragma unroll
     for (int e = 0; e < EP; ++e) {
-      float b = (!FROM_LOGITS && a.bias != nullptr && e < E) ? a.bias[e] : 0.f;
-      l[e] = acc[e] + b;
+      float v = 0.f;
+      if (e < E) {
+        if constexpr (FROM_LOGITS) {
+          v = valid ? a.logits_in[t * E + e] : 0.f;
+        } else {
+          const int nt = e / 32, n = e % 32;
+          v = red_s[0][nt][r_of][lhi + n];
+#pragma unroll
+          for (int ww = 1; ww < kWaves; ++ww) v += red_s[ww][nt][r_of][lhi + n];
+          if (a.bias != nullptr) v += a.bias[e];
+        }
+      }
+      l[e] = v;
     }
     // stable softmax over the E experts
-    float m = l[0];
+    float mx = l[0];
 #pragma unroll
-    for (int e = 1; e < EP; ++e) m = (e < E) ? fmaxf(m, l[e]) : m;
-    float s = 0.f;
+    for (int e = 1; e < EP; ++e) mx = (e < E) ? fmaxf(mx, l[e]) : mx;
+    float sum = 0.f;
 #pragma unroll
     for (int e = 0; e < EP; ++e) {
-      p[e] = (e < E) ? expf(l[e] - m) : 0.f;
-      s += p[e];
+      p[e] = (e < E) ? expf(l[e] - mx) : 0.f;
+      sum += p[e];
     }
 #pragma unroll
-    for (int e = 0; e < EP; ++e) p[e] = p[e] / s;
+    for (int e = 0; e < EP; ++e) p[e] = p[e] / sum;
 
     if (valid) {
       if (a.logits_out) for (int e = 0; e < E; ++e) a.logits_out[t * E + e] = pick(l, e);
@@ -160,26 +204,26 @@ __global__ __launch_bounds__(256) void k_router(const RouterArgs a) {
         }
       }
 
-      float g[kMaxK];
+      float gt[kMaxK];
       if (a.mode == 0) {
 #pragma unroll
-        for (int j = 0; j < kMaxK; ++j) g[j] = (j < a.k) ? pick(p, sel[j]) : 0.f;
+        for (int j = 0; j < kMaxK; ++j) gt[j] = (j < a.k) ? pick(p, sel[j]) : 0.f;
       } else {
         const float ref = pick(l, sel[0]);
         float s2 = 0.f;
 #pragma unroll
         for (int j = 0; j < kMaxK; ++j) {
-          g[j] = (j < a.k) ? expf(pick(l, sel[j]) - ref) : 0.f;
-          s2 += g[j];
+          gt[j] = (j < a.k) ? expf(pick(l, sel[j]) - ref) : 0.f;
+          s2 += gt[j];
         }
 #pragma unroll
-        for (int j = 0; j < kMaxK; ++j) g[j] = g[j] / s2;
+        for (int j = 0; j < kMaxK; ++j) gt[j] = gt[j] / s2;
       }
 #pragma unroll
       for (int j = 0; j < kMaxK; ++j) {
         if (j < a.k) {
           a.topk_idx[t * a.k + j] = sel[j];
-          a.topk_gate[t * a.k + j] = g[j];
+          a.topk_gate[t * a.k + j] = gt[j];
         }
       }
     }
@@ -199,15 +243,15 @@ __global__ __launch_bounds__(256) void k_router(const RouterArgs a) {
   }
 }
 
-template <int EP>
+template <int NT, int EP>
 hipError_t launch_ep(const RouterArgs& a, bool bf16_x, hipStream_t s) {
-  const dim3 grid((unsigned)((a.N + kTM - 1) / kTM)), block(256);
+  const dim3 grid((unsigned)((a.N + kTM - 1) / kTM)), block(512);
   if (a.logits_in) {
-    hipLaunchKernelGGL((k_router<EP, float, true>), grid, block, 0, s, a);
+    hipLaunchKernelGGL((k_router<NT, EP, float, true>), grid, block, 0, s, a);
   } else if (bf16_x) {
-    hipLaunchKernelGGL((k_router<EP, bf16, false>), grid, block, 0, s, a);
+    hipLaunchKernelGGL((k_router<NT, EP, bf16, false>), grid, block, 0, s, a);
   } else {
-    hipLaunchKernelGGL((k_router<EP, float, false>), grid, block, 0, s, a);
+    hipLaunchKernelGGL((k_router<NT, EP, float, false>), grid, block, 0, s, a);
   }
   return hipGetLastError();
 }
@@ -215,10 +259,10 @@ hipError_t launch_ep(const RouterArgs& a, bool bf16_x, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_router(const RouterArgs& a, bool bf16_x, hipStream_t s) {
-  if (a.E <= 8) return launch_ep<8>(a, bf16_x, s);
-  if (a.E <= 16) return launch_ep<16>(a, bf16_x, s);
-  if (a.E <= 32) return launch_ep<32>(a, bf16_x, s);
-  return launch_ep<64>(a, bf16_x, s);
+  if (a.E <= 8) return launch_ep<1, 8>(a, bf16_x, s);
+  if (a.E <= 16) return launch_ep<1, 16>(a, bf16_x, s);
+  if (a.E <= 32) return launch_ep<1, 32>(a, bf16_x, s);
+  return launch_ep<2, 64>(a, bf16_x, s);
 }
 
 }  // namespace moe
