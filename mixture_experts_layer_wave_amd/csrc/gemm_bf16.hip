@@ -35,6 +35,7 @@ typedef short i16x8 __attribute__((ext_vector_type(8)));
 typedef i16x4 __attribute__((address_space(3))) * lds_i16x4_ptr;
 
 constexpr int kXcds = 8;
+constexpr int kSplitMax = 8;  // most K pieces of one tail tile
 
 // Pipeline shape of the grouped GEMM: K slice per LDS stage and ring depth.
 #ifndef MOE_GEMM_BK
@@ -92,6 +93,37 @@ __device__ __forceinline__ void wait_for_slice(int ahead) {
   else wait_vmcnt<0>();
 }
 
+// Epilogue of a tile: act(acc W1) * (acc W2) for the gated up-projection (NB = 2), the
+// plain product otherwise, rounded once to bf16. With the operands swapped, accumulator
+// element r of a lane holds row lane % 32 and column 8 (r / 4) + 4 (lane / 32) + r % 4
+// of its 32 x 32 block, so each lane stores 4 consecutive bf16 (8 bytes).
+template <int NB, int ACT, int TM, int TN, int WM, int WN>
+__device__ __forceinline__ void store_tile(const f32x16 (&acc)[NB][TM][TN], const Tile& tl, const GemmParams& p,
+                                           int wm, int wn, int lane) {
+  const int N = p.N;
+  bf16* Cg = reinterpret_cast<bf16*>(p.C) + tl.row_base * N + tl.n0;
+#pragma unroll
+  for (int i = 0; i < TM; ++i) {
+    const int row = wm * WM + 32 * i + (lane & 31);
+    if (row >= tl.mcount) continue;
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int col = wn * WN + 32 * j + 8 * q + 4 * (lane >> 5);
+        bf16x4 o;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          float v;
+          if constexpr (NB == 2) v = activate<ACT>(acc[0][i][j][4 * q + u]) * acc[1][i][j][4 * q + u];
+          else v = acc[0][i][j][4 * q + u];
+          o[u] = (bf16)v;
+        }
+        *reinterpret_cast<bf16x4*>(Cg + (int64_t)row * N + col) = o;
+      }
+  }
+}
+
 template <int BM, int BNF, int NB, int ACT, int BK, int STAGES>
 __global__ __launch_bounds__(512, 1) void k_gemm_bf16(const GemmParams p) {
   // BK: K slice per pipeline stage; STAGES: LDS ring depth (STAGES-1 slices in flight).
@@ -125,8 +157,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm_bf16(const GemmParams p) {
   const int xcd = blockIdx.x % kXcds;
   const int slot = blockIdx.x / kXcds;
   const int nslot = gridDim.x / kXcds;
-  const int lo = (int)((int64_t)ts.total * xcd / kXcds);
-  const int hi = (int)((int64_t)ts.total * (xcd + 1) / kXcds);
+  const XcdShare sh = xcd_share(ts.total, xcd, kXcds, nslot, nk, p);
 
   // LDS layouts (no padding; 16-byte chunks XOR-swizzled so the MFMA operand reads are
   // bank-conflict free):
@@ -152,7 +183,20 @@ __global__ __launch_bounds__(512, 1) void k_gemm_bf16(const GemmParams p) {
   // (pc & 1) with h = 2 (row % 4).
   const int ring_addr = (int)lds_addr_of(ring);
 
-  for (int L = lo + slot; L < hi; L += nslot) {
+  // Work units of this workgroup: its full-K tiles of each round, then (if any) one K
+  // piece of a tail tile.
+  const int units = sh.rounds + (slot < sh.tail * sh.S ? 1 : 0);
+  for (int u = 0; u < units; ++u) {
+    int L, kb = 0, ke = nk, pslot = -1;
+    if (u < sh.rounds) {
+      L = sh.lo + slot + u * nslot;
+    } else {
+      const int i = slot % sh.tail, piece = slot / sh.tail;
+      L = sh.lo + sh.rounds * nslot + i;
+      kb = piece * nk / sh.S;
+      ke = (piece + 1) * nk / sh.S;
+      if (sh.S > 1) pslot = xcd * nslot + slot;
+    }
     Tile tl;
     if (!tile_of<BM, BNF>(p, ts, L, tl)) continue;
 
@@ -180,8 +224,9 @@ __global__ __launch_bounds__(512, 1) void k_gemm_bf16(const GemmParams p) {
       b_src[q] = Bm + boff + (int64_t)row * N + 8 * lc;
     }
 
+    const int nku = ke - kb;  // K slices of this unit
     auto issue_slice = [&](int kt) {
-      const int k0 = kt * BK;
+      const int k0 = (kb + kt) * BK;
       const int base = ring_addr + (kt % STAGES) * STAGE * 2;
 #pragma unroll
       for (int q = 0; q < A_CP; ++q) load_lds16(a_src[q] + k0, (uint32_t)uniform(base + (A_CP * wid + q) * 1024));
@@ -202,13 +247,13 @@ __global__ __launch_bounds__(512, 1) void k_gemm_bf16(const GemmParams p) {
 
 #pragma unroll
     for (int st = 0; st < STAGES - 1; ++st)
-      if (st < nk) issue_slice(st);
+      if (st < nku) issue_slice(st);
 
-    for (int kt = 0; kt < nk; ++kt) {
+    for (int kt = 0; kt < nku; ++kt) {
       // Slice kt has landed once at most (slices issued after it) * LOADS copies remain.
-      wait_for_slice<LOADS>(min(STAGES - 2, nk - 1 - kt));
+      wait_for_slice<LOADS>(min(STAGES - 2, nku - 1 - kt));
       barrier_no_fence();  // slice kt visible to every wave; slice kt-1 fully consumed
-      if (kt + STAGES - 1 < nk) issue_slice(kt + STAGES - 1);
+      if (kt + STAGES - 1 < nku) issue_slice(kt + STAGES - 1);
 
       const bf16* As = ring + (kt % STAGES) * STAGE;
       bf16x8 af[BK / 16][TM], bfr[BK / 16][NB][TN];
@@ -237,30 +282,62 @@ __global__ __launch_bounds__(512, 1) void k_gemm_bf16(const GemmParams p) {
     wait_vmcnt<0>();
     __syncthreads();  // every wave done reading the ring before the next tile refills it
 
-    // Epilogue. With the operands swapped, accumulator element r of a lane holds row
-    // lane % 32 and column 8 * (r / 4) + 4 * (lane / 32) + r % 4 of its 32 x 32 block.
-    bf16* Cg = reinterpret_cast<bf16*>(p.C) + tl.row_base * N + tl.n0;
+    if (pslot >= 0) {
+      // A K piece of a tail tile: keep the raw fp32 accumulators for the reduction.
+      float* P = p.partial + ((int64_t)pslot * 8 + wid) * (NB * TM * TN * 16) * 64 + lane;
 #pragma unroll
-    for (int i = 0; i < TM; ++i) {
-      const int row = wm * WM + 32 * i + (lane & 31);
-      if (row >= tl.mcount) continue;
+      for (int m = 0; m < NB; ++m)
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+          for (int j = 0; j < TN; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) P[(((m * TM + i) * TN + j) * 16 + r) * 64] = acc[m][i][j][r];
+    } else {
+      store_tile<NB, ACT, TM, TN, WM, WN>(acc, tl, p, wm, wn, lane);
+    }
+  }
+}
+
+// Sums the K pieces of the tail tiles of each XCD share in piece order and stores the
+// tiles. Workgroup b handles tail tile b % nslot of XCD b / nslot; it repeats the GEMM's
+// schedule arithmetic from counts[] so both kernels agree on the split.
+template <int BM, int BNF, int NB, int ACT, int BK>
+__global__ __launch_bounds__(512) void k_gemm_tail_reduce(const GemmParams p, int nslot) {
+  constexpr int WM = BM / 2, WN = BNF / 4;
+  constexpr int TM = WM / 32, TN = WN / 32;
+  constexpr int NACC = NB * TM * TN * 16;
+  const int lane = threadIdx.x & 63;
+  const int wid = uniform(threadIdx.x >> 6);
+  const int wm = wid >> 2, wn = wid & 3;
+  const int xcd = blockIdx.x / nslot, i = blockIdx.x % nslot;
+  const TileScan ts = tile_scan<BM>(p);
+  const XcdShare sh = xcd_share(ts.total, xcd, kXcds, nslot, p.K / BK, p);
+  if (sh.S <= 1 || i >= sh.tail) return;
+  Tile tl;
+  if (!tile_of<BM, BNF>(p, ts, sh.lo + sh.rounds * nslot + i, tl)) return;
+  f32x16 acc[NB][TM][TN];
+#pragma unroll
+  for (int m = 0; m < NB; ++m)
+#pragma unroll
+    for (int a = 0; a < TM; ++a)
 #pragma unroll
       for (int j = 0; j < TN; ++j)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int col = wn * WN + 32 * j + 8 * q + 4 * (lane >> 5);
-          bf16x4 o;
+        for (int r = 0; r < 16; ++r) acc[m][a][j][r] = 0.f;
+  for (int piece = 0; piece < sh.S; ++piece) {
+    const int pslot = xcd * nslot + piece * sh.tail + i;
+    const float* P = p.partial + ((int64_t)pslot * 8 + wid) * NACC * 64 + lane;
 #pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            float v;
-            if constexpr (NB == 2) v = activate<ACT>(acc[0][i][j][4 * q + u]) * acc[1][i][j][4 * q + u];
-            else v = acc[0][i][j][4 * q + u];
-            o[u] = (bf16)v;
-          }
-          *reinterpret_cast<bf16x4*>(Cg + (int64_t)row * N + col) = o;
-        }
-    }
+    for (int m = 0; m < NB; ++m)
+#pragma unroll
+      for (int a = 0; a < TM; ++a)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[m][a][j][r] += P[(((m * TM + a) * TN + j) * 16 + r) * 64];
   }
+  store_tile<NB, ACT, TM, TN, WM, WN>(acc, tl, p, wm, wn, lane);
 }
 
 int g_num_cus = 0;
@@ -274,23 +351,31 @@ int persistent_grid(int64_t tiles_bound) {
     g_num_cus = n;
   }
   int64_t g = tiles_bound < g_num_cus ? tiles_bound : g_num_cus;
+  if (g > (int64_t)kGemmPartialUnits) g = kGemmPartialUnits;
   g = (g + kXcds - 1) / kXcds * kXcds;
   return (int)g;
+}
+
+template <int BM, int BNF, int NB, int ACT, int BK, int STAGES>
+hipError_t launch_act(const GemmParams& p, int64_t bound, hipStream_t s) {
+  const int grid = persistent_grid(bound);
+  hipLaunchKernelGGL((k_gemm_bf16<BM, BNF, NB, ACT, BK, STAGES>), dim3(grid), dim3(512), 0, s, p);
+  if (p.partial != nullptr)
+    hipLaunchKernelGGL((k_gemm_tail_reduce<BM, BNF, NB, ACT, BK>), dim3(grid), dim3(512), 0, s, p, grid / kXcds);
+  return hipGetLastError();
 }
 
 template <int BM, int BNF, int NB, int BK = MOE_GEMM_BK, int STAGES = MOE_GEMM_STAGES>
 hipError_t launch_bf16(const GemmParams& p, int act, int64_t mtiles, hipStream_t s) {
   const int64_t bound = mtiles * p.n_tiles;
   if (bound <= 0) return hipSuccess;
-  const dim3 grid((unsigned)persistent_grid(bound)), block(512);
   if constexpr (NB == 2) {
-    if (act == ACT_SILU) hipLaunchKernelGGL((k_gemm_bf16<BM, BNF, 2, ACT_SILU, BK, STAGES>), grid, block, 0, s, p);
-    else if (act == ACT_GELU_ERF) hipLaunchKernelGGL((k_gemm_bf16<BM, BNF, 2, ACT_GELU_ERF, BK, STAGES>), grid, block, 0, s, p);
-    else hipLaunchKernelGGL((k_gemm_bf16<BM, BNF, 2, ACT_GELU_TANH, BK, STAGES>), grid, block, 0, s, p);
+    if (act == ACT_SILU) return launch_act<BM, BNF, 2, ACT_SILU, BK, STAGES>(p, bound, s);
+    if (act == ACT_GELU_ERF) return launch_act<BM, BNF, 2, ACT_GELU_ERF, BK, STAGES>(p, bound, s);
+    return launch_act<BM, BNF, 2, ACT_GELU_TANH, BK, STAGES>(p, bound, s);
   } else {
-    hipLaunchKernelGGL((k_gemm_bf16<BM, BNF, 1, ACT_SILU, BK, STAGES>), grid, block, 0, s, p);
+    return launch_act<BM, BNF, 1, ACT_SILU, BK, STAGES>(p, bound, s);
   }
-  return hipGetLastError();
 }
 
 }  // namespace
@@ -298,7 +383,7 @@ hipError_t launch_bf16(const GemmParams& p, int act, int64_t mtiles, hipStream_t
 hipError_t launch_expert_up(const FfnArgs& a, bool bf16_io, hipStream_t s) {
   if (!bf16_io) return launch_gemm_f32(a, true, s);
   constexpr int BM = 256, BNF = 128;
-  GemmParams p{a.x_perm, a.w1, a.w2, a.h, a.offsets, a.counts, a.E, a.D, a.F, a.F / BNF, a.rows};
+  GemmParams p{a.x_perm, a.w1, a.w2, a.h, a.offsets, a.counts, a.E, a.D, a.F, a.F / BNF, a.rows, a.partial, kSplitMax};
   return launch_bf16<BM, BNF, 2>(p, a.act, max_m_tiles(a, BM), s);
 }
 
@@ -306,10 +391,12 @@ hipError_t launch_expert_down(const FfnArgs& a, bool bf16_io, hipStream_t s) {
   if (!bf16_io) return launch_gemm_f32(a, false, s);
   constexpr int BM = 256;
   if (a.D % 256 == 0) {
-    GemmParams p{a.h, a.w3, nullptr, a.y_perm, a.offsets, a.counts, a.E, a.F, a.D, a.D / 256, a.rows};
+    GemmParams p{a.h, a.w3, nullptr, a.y_perm, a.offsets, a.counts, a.E, a.F, a.D, a.D / 256, a.rows, a.partial,
+                 kSplitMax};
     return launch_bf16<BM, 256, 1>(p, a.act, max_m_tiles(a, BM), s);
   }
-  GemmParams p{a.h, a.w3, nullptr, a.y_perm, a.offsets, a.counts, a.E, a.F, a.D, a.D / 128, a.rows};
+  GemmParams p{a.h, a.w3, nullptr, a.y_perm, a.offsets, a.counts, a.E, a.F, a.D, a.D / 128, a.rows, a.partial,
+               kSplitMax};
   return launch_bf16<BM, 128, 1>(p, a.act, max_m_tiles(a, BM), s);
 }
 

@@ -25,6 +25,8 @@ struct GemmParams {
   int E, K, N;
   int n_tiles;      // N / BN
   int64_t rows;     // rows of A and C: tiles never touch rows outside [0, rows)
+  float* partial;   // split-K partial tiles (null: no split)
+  int split_max;    // most K splits of one tile
 };
 
 struct Tile {
@@ -77,6 +79,26 @@ __device__ __forceinline__ bool tile_of(const GemmParams& p, const TileScan& s, 
   if (t.row_base < 0 || t.row_base >= p.rows) return false;
   if (t.row_base + t.mcount > p.rows) t.mcount = (int)(p.rows - t.row_base);
   return true;
+}
+
+// Persistent schedule of one XCD's share of the tile list. The tiles [lo, hi) are run by
+// nslot workgroups in rounds; the last, partial round (tail tiles) is split along K into
+// S pieces when that fills more workgroups, and the pieces are summed afterwards in a
+// fixed order (deterministic).
+struct XcdShare {
+  int lo, hi, rounds, tail, S;
+};
+
+__device__ __forceinline__ XcdShare xcd_share(int total, int xcd, int xcds, int nslot, int nk, const GemmParams& p) {
+  XcdShare s;
+  s.lo = (int)((int64_t)total * xcd / xcds);
+  s.hi = (int)((int64_t)total * (xcd + 1) / xcds);
+  const int n = s.hi - s.lo;
+  s.rounds = n / nslot;
+  s.tail = n - s.rounds * nslot;
+  s.S = 1;
+  if (p.partial != nullptr && s.tail > 0) s.S = max(1, min(min(nslot / s.tail, p.split_max), nk));
+  return s;
 }
 
 // Upper bound on the m-tiles of all experts, from host-known sizes only.

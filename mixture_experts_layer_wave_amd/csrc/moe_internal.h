@@ -13,6 +13,10 @@ constexpr int kDispatchTokens = 256;  // tokens per dispatch workgroup
 constexpr int kMaxE = 64;
 constexpr int kMaxK = 8;
 constexpr uint32_t kPsumMagic = 0x5053554du;  // marks valid router partial sums
+// Split-K partial tiles of the bf16 grouped GEMM: at most 256 workgroups, each holding
+// 8 waves x 128 fp32 accumulators x 64 lanes.
+constexpr size_t kGemmPartialUnits = 256;
+constexpr size_t kGemmPartialBytes = kGemmPartialUnits * 8 * 128 * 64 * sizeof(float);
 
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
@@ -23,12 +27,13 @@ inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 //   base      : int32 [k][nblk_d][E] exclusive slot-major scan of blockcnt
 //   tokdrop   : int32 [nblk_d]     tokens with every slot dropped, per block
 //   load      : int32 [E]          copy of the pre-capacity histogram
+//   partial   : fp32 split-K partial tiles of the bf16 grouped GEMM (bf16 layers only)
 struct ScratchLayout {
-  size_t header, psum, blockcnt, base, tokdrop, load, total;
+  size_t header, psum, blockcnt, base, tokdrop, load, partial, total;
   int nblk_r, nblk_d;
 };
 
-inline ScratchLayout scratch_layout(int64_t N, int E, int k) {
+inline ScratchLayout scratch_layout(int64_t N, int E, int k, bool bf16) {
   ScratchLayout s;
   s.nblk_r = (int)((N + kRouterTokens - 1) / kRouterTokens);
   s.nblk_d = (int)((N + kDispatchTokens - 1) / kDispatchTokens);
@@ -39,6 +44,7 @@ inline ScratchLayout scratch_layout(int64_t N, int E, int k) {
   s.base = o; o = align_up(o + sizeof(int32_t) * (size_t)k * s.nblk_d * E, 256);
   s.tokdrop = o; o = align_up(o + sizeof(int32_t) * (size_t)s.nblk_d, 256);
   s.load = o; o = align_up(o + sizeof(int32_t) * (size_t)E, 256);
+  s.partial = o; o = align_up(o + (bf16 ? kGemmPartialBytes : 0), 256);
   s.total = o;
   return s;
 }
@@ -119,6 +125,7 @@ struct FfnArgs {
   int64_t rows;             // rows of the expert buffers
   int64_t max_rows_per_expert;  // host bound on counts[e] (N, or C when padded)
   int D, F, E, act;
+  float* partial;           // scratch for split-K partial tiles (kGemmPartialBytes)
 };
 // Gated up-projection (h) and down-projection (y_perm) of every expert's rows.
 hipError_t launch_expert_up(const FfnArgs& a, bool bf16, hipStream_t s);
