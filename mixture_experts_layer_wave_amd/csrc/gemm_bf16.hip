@@ -124,7 +124,16 @@ __device__ __forceinline__ void store_tile(const f32x16 (&acc)[NB][TM][TN], cons
   }
 }
 
-template <int BM, int BNF, int NB, int ACT, int BK, int STAGES>
+// Stream-K range of workgroup w over the W = tiles * nk (tile, K slice) work items, and
+// the workgroup that owns work item s.
+__device__ __forceinline__ int64_t sk_begin(int64_t w, int64_t W, int64_t G) { return w * W / G; }
+__device__ __forceinline__ int64_t sk_owner(int64_t s, int64_t W, int64_t G) { return ((s + 1) * G - 1) / W; }
+
+// STREAMK = false: persistent full tiles per XCD share, tail round split along K.
+// STREAMK = true : stream-K; the (tile, K slice) list is cut into equal contiguous ranges,
+//                  one per workgroup; a tile cut by a range boundary leaves fp32 partials
+//                  (slot 2w for the workgroup's first tile, 2w + 1 for its last).
+template <int BM, int BNF, int NB, int ACT, int BK, int STAGES, bool STREAMK>
 __global__ __launch_bounds__(512, 1) void k_gemm_bf16(const GemmParams p) {
   // BK: K slice per pipeline stage; STAGES: LDS ring depth (STAGES-1 slices in flight).
   constexpr int WM = BM / 2, WN = BNF / 4;  // wave tile per matrix
@@ -140,7 +149,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm_bf16(const GemmParams p) {
   constexpr int A_CPR = BK / 8;                     // 16-byte chunks per A row
   constexpr int A_RPB = 128 / BK;                   // A rows per 256 bytes (64 banks)
   constexpr int A_RPC = 512 / BK;                   // A rows per 1 KB copy
-  static_assert(BM == 256 && (BNF == 128 || BNF == 256) && (BK == 32 || BK == 64), "tile shape");
+  static_assert((BM == 256 || BM == 64) && (BNF == 128 || BNF == 256) && (BK == 32 || BK == 64), "tile shape");
   static_assert(STAGES >= 2 && STAGES <= 5 && STAGES * STAGE * 2 <= 160 * 1024, "LDS ring");
   static_assert(A_CP >= 1 && B_CP >= 1 && TM >= 1 && TN >= 1 && (NB * B_CPM) % 8 == 0, "tile shape");
 
@@ -183,12 +192,28 @@ __global__ __launch_bounds__(512, 1) void k_gemm_bf16(const GemmParams p) {
   // (pc & 1) with h = 2 (row % 4).
   const int ring_addr = (int)lds_addr_of(ring);
 
-  // Work units of this workgroup: its full-K tiles of each round, then (if any) one K
-  // piece of a tail tile.
-  const int units = sh.rounds + (slot < sh.tail * sh.S ? 1 : 0);
+  // Work units of this workgroup. Persistent: its full-K tiles of each round, then (if
+  // any) one K piece of a tail tile. Stream-K: every tile its range touches.
+  int units, sk_t0 = 0;
+  int64_t sk_s0 = 0, sk_s1 = 0;
+  if constexpr (STREAMK) {
+    const int64_t W = (int64_t)ts.total * nk;
+    sk_s0 = sk_begin(blockIdx.x, W, gridDim.x);
+    sk_s1 = sk_begin(blockIdx.x + 1, W, gridDim.x);
+    sk_t0 = (int)(sk_s0 / nk);
+    units = sk_s1 > sk_s0 ? (int)((sk_s1 - 1) / nk) - sk_t0 + 1 : 0;
+  } else {
+    units = sh.rounds + (slot < sh.tail * sh.S ? 1 : 0);
+  }
   for (int u = 0; u < units; ++u) {
     int L, kb = 0, ke = nk, pslot = -1;
-    if (u < sh.rounds) {
+    if constexpr (STREAMK) {
+      L = sk_t0 + u;
+      const int64_t base = (int64_t)L * nk;
+      kb = (int)(max(sk_s0, base) - base);
+      ke = (int)(min(sk_s1, base + nk) - base);
+      if (kb != 0 || ke != nk) pslot = 2 * blockIdx.x + (u == 0 ? 0 : 1);
+    } else if (u < sh.rounds) {
       L = sh.lo + slot + u * nslot;
     } else {
       const int i = slot % sh.tail, piece = slot / sh.tail;
@@ -340,6 +365,52 @@ __global__ __launch_bounds__(512) void k_gemm_tail_reduce(const GemmParams p, in
   store_tile<NB, ACT, TM, TN, WM, WN>(acc, tl, p, wm, wn, lane);
 }
 
+// Stream-K fix-up: workgroup b sums, in workgroup order, the partials of tile b if a
+// range boundary cut it, and stores the tile.
+template <int BM, int BNF, int NB, int ACT, int BK>
+__global__ __launch_bounds__(512) void k_gemm_streamk_reduce(const GemmParams p, int grid) {
+  constexpr int WM = BM / 2, WN = BNF / 4;
+  constexpr int TM = WM / 32, TN = WN / 32;
+  constexpr int NACC = NB * TM * TN * 16;
+  const int lane = threadIdx.x & 63;
+  const int wid = uniform(threadIdx.x >> 6);
+  const int wm = wid >> 2, wn = wid & 3;
+  const int nk = p.K / BK;
+  const TileScan ts = tile_scan<BM>(p);
+  const int t = blockIdx.x;
+  if (t >= ts.total) return;
+  const int64_t W = (int64_t)ts.total * nk;
+  const int64_t wa = sk_owner((int64_t)t * nk, W, grid), wb = sk_owner((int64_t)(t + 1) * nk - 1, W, grid);
+  if (wa == wb) return;  // stored directly by its only workgroup
+  Tile tl;
+  if (!tile_of<BM, BNF>(p, ts, t, tl)) return;
+  f32x16 acc[NB][TM][TN];
+#pragma unroll
+  for (int m = 0; m < NB; ++m)
+#pragma unroll
+    for (int a = 0; a < TM; ++a)
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[m][a][j][r] = 0.f;
+  for (int64_t w = wa; w <= wb; ++w) {
+    const int64_t b0 = sk_begin(w, W, grid);
+    if (sk_begin(w + 1, W, grid) <= b0) continue;  // empty range (fewer items than workgroups)
+    const int first = (int)(b0 / nk);
+    const int64_t pslot = 2 * w + (t == first ? 0 : 1);
+    const float* P = p.partial + (pslot * 8 + wid) * NACC * 64 + lane;
+#pragma unroll
+    for (int m = 0; m < NB; ++m)
+#pragma unroll
+      for (int a = 0; a < TM; ++a)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[m][a][j][r] += P[(((m * TM + a) * TN + j) * 16 + r) * 64];
+  }
+  store_tile<NB, ACT, TM, TN, WM, WN>(acc, tl, p, wm, wn, lane);
+}
+
 int g_num_cus = 0;
 
 int persistent_grid(int64_t tiles_bound) {
@@ -356,32 +427,49 @@ int persistent_grid(int64_t tiles_bound) {
   return (int)g;
 }
 
-template <int BM, int BNF, int NB, int ACT, int BK, int STAGES>
+template <int BM, int BNF, int NB, int ACT, int BK, int STAGES, bool STREAMK>
 hipError_t launch_act(const GemmParams& p, int64_t bound, hipStream_t s) {
-  const int grid = persistent_grid(bound);
-  hipLaunchKernelGGL((k_gemm_bf16<BM, BNF, NB, ACT, BK, STAGES>), dim3(grid), dim3(512), 0, s, p);
-  if (p.partial != nullptr)
-    hipLaunchKernelGGL((k_gemm_tail_reduce<BM, BNF, NB, ACT, BK>), dim3(grid), dim3(512), 0, s, p, grid / kXcds);
+  if constexpr (STREAMK) {
+    // Every compute unit takes an equal share of the work; the fix-up covers every tile.
+    const int grid = persistent_grid(1 << 30);
+    hipLaunchKernelGGL((k_gemm_bf16<BM, BNF, NB, ACT, BK, STAGES, true>), dim3(grid), dim3(512), 0, s, p);
+    hipLaunchKernelGGL((k_gemm_streamk_reduce<BM, BNF, NB, ACT, BK>), dim3((unsigned)bound), dim3(512), 0, s, p,
+                       grid);
+  } else {
+    const int grid = persistent_grid(bound);
+    hipLaunchKernelGGL((k_gemm_bf16<BM, BNF, NB, ACT, BK, STAGES, false>), dim3(grid), dim3(512), 0, s, p);
+    if (p.partial != nullptr)
+      hipLaunchKernelGGL((k_gemm_tail_reduce<BM, BNF, NB, ACT, BK>), dim3(grid), dim3(512), 0, s, p, grid / kXcds);
+  }
   return hipGetLastError();
 }
 
-template <int BM, int BNF, int NB, int BK = MOE_GEMM_BK, int STAGES = MOE_GEMM_STAGES>
+template <int BM, int BNF, int NB, int BK = MOE_GEMM_BK, int STAGES = MOE_GEMM_STAGES, bool STREAMK = false>
 hipError_t launch_bf16(const GemmParams& p, int act, int64_t mtiles, hipStream_t s) {
   const int64_t bound = mtiles * p.n_tiles;
   if (bound <= 0) return hipSuccess;
   if constexpr (NB == 2) {
-    if (act == ACT_SILU) return launch_act<BM, BNF, 2, ACT_SILU, BK, STAGES>(p, bound, s);
-    if (act == ACT_GELU_ERF) return launch_act<BM, BNF, 2, ACT_GELU_ERF, BK, STAGES>(p, bound, s);
-    return launch_act<BM, BNF, 2, ACT_GELU_TANH, BK, STAGES>(p, bound, s);
+    if (act == ACT_SILU) return launch_act<BM, BNF, 2, ACT_SILU, BK, STAGES, STREAMK>(p, bound, s);
+    if (act == ACT_GELU_ERF) return launch_act<BM, BNF, 2, ACT_GELU_ERF, BK, STAGES, STREAMK>(p, bound, s);
+    return launch_act<BM, BNF, 2, ACT_GELU_TANH, BK, STAGES, STREAMK>(p, bound, s);
   } else {
-    return launch_act<BM, BNF, 1, ACT_SILU, BK, STAGES>(p, bound, s);
+    return launch_act<BM, BNF, 1, ACT_SILU, BK, STAGES, STREAMK>(p, bound, s);
   }
 }
+
+// Skinny regime (every expert has at most 64 rows, e.g. decode): 64-row tiles, a deeper
+// ring (weights stream from HBM with little compute per slice) and stream-K balancing.
+constexpr int kSkinnyRows = 64;
+bool skinny(const FfnArgs& a) { return a.partial != nullptr && a.max_rows_per_expert <= kSkinnyRows; }
 
 }  // namespace
 
 hipError_t launch_expert_up(const FfnArgs& a, bool bf16_io, hipStream_t s) {
   if (!bf16_io) return launch_gemm_f32(a, true, s);
+  if (skinny(a)) {
+    GemmParams p{a.x_perm, a.w1, a.w2, a.h, a.offsets, a.counts, a.E, a.D, a.F, a.F / 128, a.rows, a.partial, 1};
+    return launch_bf16<kSkinnyRows, 128, 2, 64, 4, true>(p, a.act, max_m_tiles(a, kSkinnyRows), s);
+  }
   constexpr int BM = 256, BNF = 128;
   GemmParams p{a.x_perm, a.w1, a.w2, a.h, a.offsets, a.counts, a.E, a.D, a.F, a.F / BNF, a.rows, a.partial, kSplitMax};
   return launch_bf16<BM, BNF, 2>(p, a.act, max_m_tiles(a, BM), s);
@@ -389,6 +477,10 @@ hipError_t launch_expert_up(const FfnArgs& a, bool bf16_io, hipStream_t s) {
 
 hipError_t launch_expert_down(const FfnArgs& a, bool bf16_io, hipStream_t s) {
   if (!bf16_io) return launch_gemm_f32(a, false, s);
+  if (skinny(a)) {
+    GemmParams p{a.h, a.w3, nullptr, a.y_perm, a.offsets, a.counts, a.E, a.F, a.D, a.D / 128, a.rows, a.partial, 1};
+    return launch_bf16<kSkinnyRows, 128, 1, 64, 4, true>(p, a.act, max_m_tiles(a, kSkinnyRows), s);
+  }
   constexpr int BM = 256;
   if (a.D % 256 == 0) {
     GemmParams p{a.h, a.w3, nullptr, a.y_perm, a.offsets, a.counts, a.E, a.F, a.D, a.D / 256, a.rows, a.partial,

@@ -170,6 +170,9 @@ FFN_CASES = [
     ("bf16", "gelu_erf", 384, 256, 3, [64, 200, 129]),
     ("bf16", "gelu_tanh", 128, 512, 2, [5, 300]),
     ("bf16", "silu", 4096, 1024, 2, [40, 131]),
+    ("bf16", "silu", 256, 384, 4, [30, 0, 20, 14]),         # <= 64 rows per expert: stream-K path
+    ("bf16", "gelu_erf", 512, 256, 8, [1, 2, 3, 4, 5, 6, 7, 8]),
+    ("bf16", "silu", 4096, 512, 3, [64, 0, 0]),
     ("f32", "silu", 128, 256, 4, [30, 33, 0, 65]),
     ("f32", "gelu_erf", 256, 128, 3, [64, 1, 100]),
 ]
