@@ -13,7 +13,6 @@ oracle timed on a bounded sample of the same workload on the host cores.
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import os
 import sys
@@ -40,16 +39,10 @@ def parse():
     p.add_argument("--workload", default="mixtral_prefill")
     p.add_argument("--cpu-sample", type=int, default=768, help="tokens in the oracle's timed FFN sample")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--copy-mib", type=int, default=0,
+                   help="instead of the bench: run a plain device copy of this many MiB `steps` times "
+                        "(calibration of the HBM byte counters)")
     return p.parse_args()
-
-
-def source_hash() -> str:
-    h = hashlib.sha256()
-    csrc = os.path.join(ROOT, "mixture_experts_layer_wave_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
-        with open(os.path.join(csrc, name), "rb") as f:
-            h.update(name.encode() + f.read())
-    return h.hexdigest()[:16]
 
 
 def traffic_from_profiles(workload: str, kernel_stage: str):
@@ -60,6 +53,7 @@ def traffic_from_profiles(workload: str, kernel_stage: str):
         return None
     with open(path) as f:
         t = json.load(f)
+    from mixture_experts_layer_wave_amd.profiling import source_hash
     if t.get("source_hash") != source_hash():
         return None
     st = t.get("stages", {}).get(kernel_stage)
@@ -101,6 +95,14 @@ def main():
         sys.exit(2)
     import numpy as np
     import torch
+    if args.copy_mib > 0:
+        src = torch.empty(args.copy_mib * 2 ** 20, dtype=torch.uint8, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_mib": args.copy_mib, "copies": args.steps}), flush=True)
+        return
     from mixture_experts_layer_wave_amd import binding as B
     from mixture_experts_layer_wave_amd import configs, inputs
 

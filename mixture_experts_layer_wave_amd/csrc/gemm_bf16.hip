@@ -429,6 +429,10 @@ int persistent_grid(int64_t tiles_bound) {
 
 template <int BM, int BNF, int NB, int ACT, int BK, int STAGES, bool STREAMK>
 hipError_t launch_act(const GemmParams& p, int64_t bound, hipStream_t s) {
+  // fp32 partial tiles: 8 waves x NACC accumulators x 64 lanes per slot; stream-K uses two
+  // slots per workgroup, the tail split one.
+  constexpr size_t kSlotBytes = (size_t)8 * (NB * (BM / 64) * (BNF / 128) * 16) * 64 * sizeof(float);
+  static_assert((STREAMK ? 2 : 1) * kGemmPartialUnits * kSlotBytes <= kGemmPartialBytes, "partial scratch");
   if constexpr (STREAMK) {
     // Every compute unit takes an equal share of the work; the fix-up covers every tile.
     const int grid = persistent_grid(1 << 30);
@@ -460,6 +464,15 @@ hipError_t launch_bf16(const GemmParams& p, int act, int64_t mtiles, hipStream_t
 // Skinny regime (every expert has at most 64 rows, e.g. decode): 64-row tiles, a deeper
 // ring (weights stream from HBM with little compute per slice) and stream-K balancing.
 constexpr int kSkinnyRows = 64;
+#ifndef MOE_SKINNY_BNF
+#define MOE_SKINNY_BNF 128
+#endif
+#ifndef MOE_SKINNY_BK
+#define MOE_SKINNY_BK 64
+#endif
+#ifndef MOE_SKINNY_STAGES
+#define MOE_SKINNY_STAGES 4
+#endif
 bool skinny(const FfnArgs& a) { return a.partial != nullptr && a.max_rows_per_expert <= kSkinnyRows; }
 
 }  // namespace
@@ -467,7 +480,12 @@ bool skinny(const FfnArgs& a) { return a.partial != nullptr && a.max_rows_per_ex
 hipError_t launch_expert_up(const FfnArgs& a, bool bf16_io, hipStream_t s) {
   if (!bf16_io) return launch_gemm_f32(a, true, s);
   if (skinny(a)) {
-    GemmParams p{a.x_perm, a.w1, a.w2, a.h, a.offsets, a.counts, a.E, a.D, a.F, a.F / 128, a.rows, a.partial, 1};
+    constexpr int BNF = MOE_SKINNY_BNF;
+    GemmParams p{a.x_perm, a.w1, a.w2, a.h, a.offsets, a.counts, a.E, a.D, a.F, a.F / BNF, a.rows, a.partial, 1};
+    if (a.F % BNF == 0)
+      return launch_bf16<kSkinnyRows, BNF, 2, MOE_SKINNY_BK, MOE_SKINNY_STAGES, true>(p, a.act,
+                                                                                       max_m_tiles(a, kSkinnyRows), s);
+    p.n_tiles = a.F / 128;
     return launch_bf16<kSkinnyRows, 128, 2, 64, 4, true>(p, a.act, max_m_tiles(a, kSkinnyRows), s);
   }
   constexpr int BM = 256, BNF = 128;

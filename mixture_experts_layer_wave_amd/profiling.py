@@ -1,0 +1,233 @@
+"""Summaries of rocprofv3 output for the layer's kernels (measurement tooling).
+
+Two commands, both reading the CSV files that ``rocprofv3 --output-format csv`` writes:
+
+``stats``   kernel-trace statistics (``*_kernel_stats.csv``) -> a Markdown table of every
+            kernel's calls and average duration, plus per-stage sums (a stage is one call
+            of the C ABI, e.g. the gated up-projection = its GEMM kernel + its split-K or
+            stream-K fix-up kernel).
+``traffic`` two counter runs (``FETCH_SIZE`` and ``WRITE_SIZE``, KiB per dispatch) of the
+            bench, and the same two counters for a plain device copy of known size. The
+            copy gives the factor that turns counter KiB into bytes actually moved
+            (bytes copied / counter bytes); the stage averages are scaled by it and written
+            as JSON together with a hash of the kernel sources, so that a later change of
+            the kernels invalidates them.
+
+Stage of a kernel: from its name and, for the templated GEMMs, the NB template argument
+(2 = gated up-projection with two weight matrices, 1 = down-projection).
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import glob
+import hashlib
+import json
+import os
+import re
+from collections import defaultdict
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(PKG, "csrc")
+
+STAGE_ORDER = ["route", "dispatch", "expert_up", "expert_down", "expert_ffn", "combine", "stats", "other"]
+
+
+def source_hash() -> str:
+    """Hash of every file of the kernel sources (names + contents)."""
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(CSRC)):
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(name.encode() + f.read())
+    return h.hexdigest()[:16]
+
+
+def parse_kernel(name: str):
+    """(base name, integer/bool template arguments) from a demangled or an Itanium-mangled
+    kernel name."""
+    m = re.search(r"(k_[a-z0-9_]+)<([^>]*)>", name)
+    if m:
+        args = []
+        for tok in m.group(2).split(","):
+            tok = tok.strip()
+            if re.fullmatch(r"-?\d+", tok):
+                args.append(int(tok))
+            elif tok in ("true", "false"):
+                args.append(int(tok == "true"))
+        return m.group(1), args
+    m = re.search(r"\d+(k_[a-z0-9_]+)(I(.*?)E)?E?v", name)
+    if m:
+        base = m.group(1)
+        args = [int(v) for v in re.findall(r"L[ib](-?\d+)E", m.group(3) or "")]
+        return base, args
+    m = re.search(r"(k_[a-z0-9_]+)", name)
+    return (m.group(1) if m else name), []
+
+
+def stage_of(name: str) -> str:
+    base, args = parse_kernel(name)
+    if base == "k_router":
+        return "route"
+    if base in ("k_dispatch_count", "k_dispatch_scan", "k_dispatch_assign", "k_gather"):
+        return "dispatch"
+    if base in ("k_gemm_bf16", "k_gemm_tail_reduce", "k_gemm_streamk_reduce") and len(args) >= 3:
+        return "expert_up" if args[2] == 2 else "expert_down"
+    if base == "k_gemm_f32":
+        return "expert_ffn"
+    if base == "k_combine":
+        return "combine"
+    if base == "k_stats":
+        return "stats"
+    return "other"
+
+
+def short_name(name: str) -> str:
+    base, args = parse_kernel(name)
+    return f"{base}<{', '.join(str(a) for a in args)}>" if args else base
+
+
+def _one(pattern: str) -> str:
+    files = sorted(glob.glob(pattern, recursive=True))
+    if not files:
+        raise SystemExit(f"no file matches {pattern}")
+    return files[0]
+
+
+def kernel_stats(stats_csv: str):
+    rows = []
+    with open(stats_csv) as f:
+        for r in csv.DictReader(f):
+            rows.append({"name": r["Name"], "calls": int(r["Calls"]), "avg_us": float(r["AverageNs"]) / 1e3,
+                         "total_us": float(r["TotalDurationNs"]) / 1e3, "min_us": float(r["MinNs"]) / 1e3,
+                         "max_us": float(r["MaxNs"]) / 1e3})
+    return rows
+
+
+def trace_last(trace_csv: str, last: int):
+    """Per kernel name: average duration (us) of its last `last` dispatches, and its
+    launch resources."""
+    per = defaultdict(list)
+    info = {}
+    with open(trace_csv) as f:
+        for r in csv.DictReader(f):
+            per[r["Kernel_Name"]].append((int(r["Dispatch_Id"]), (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3))
+            info[r["Kernel_Name"]] = (r["Grid_Size_X"], r["Workgroup_Size_X"], r["VGPR_Count"], r["Accum_VGPR_Count"],
+                                      r["LDS_Block_Size"], r["Scratch_Size"])
+    out = {}
+    for k, v in per.items():
+        v.sort()
+        tail = [d for _, d in v[-last:]]
+        out[k] = (sum(tail) / len(tail), info[k])
+    return out
+
+
+def bench_stages(log: str):
+    """The stage averages (ms) that bench.py measured with HIP events in the profiled run."""
+    with open(log) as f:
+        for line in reversed(f.read().splitlines()):
+            if line.startswith("{") and '"stages_ms"' in line:
+                return json.loads(line)["stages_ms"]
+    return None
+
+
+def cmd_stats(a):
+    rows = kernel_stats(_one(os.path.join(a.dir, "**", "*kernel_stats.csv")) if os.path.isdir(a.dir) else a.dir)
+    last = trace_last(_one(os.path.join(a.dir, "**", "*kernel_trace.csv")), a.last) if a.last else {}
+    stage, stage_last = defaultdict(float), defaultdict(float)
+    lines = [f"# Kernel durations: {a.title}", "", "Command:", "", "```", a.cmd, "```", "",
+             f"Kernel sources hash: `{source_hash()}`", "",
+             f"`avg` is over every call (warm-up included); `timed avg` over the last {a.last} calls, the "
+             "timed steps of the run." if a.last else "", "",
+             "| kernel | stage | calls | avg us | timed avg us | min us | max us | grid x wg | vgpr+agpr | lds B |",
+             "|---|---|---:|---:|---:|---:|---:|---|---|---:|"]
+    for r in sorted(rows, key=lambda r: STAGE_ORDER.index(stage_of(r["name"]))):
+        st = stage_of(r["name"])
+        tl, inf = last.get(r["name"], (float("nan"), ("", "", "", "", "", "")))
+        lines.append(f"| `{short_name(r['name'])}` | {st} | {r['calls']} | {r['avg_us']:.2f} | {tl:.2f} | "
+                     f"{r['min_us']:.2f} | {r['max_us']:.2f} | {inf[0]} x {inf[1]} | {inf[2]}+{inf[3]} | {inf[4]} |")
+        if st != "other":
+            stage[st] += r["avg_us"]
+            stage_last[st] += tl
+    bench = bench_stages(a.bench_log) if a.bench_log else None
+    lines += ["", "Per-stage sums (each kernel is called once per step). `bench events` is what bench.py "
+              "measured for the stage with HIP events on the launch stream in the same run.", "",
+              "| stage | avg us | timed avg us | bench events us |", "|---|---:|---:|---:|"]
+    for st in STAGE_ORDER:
+        if st in stage:
+            be = bench.get(st) * 1e3 if bench and st in bench else float("nan")
+            lines.append(f"| {st} | {stage[st]:.2f} | {stage_last[st]:.2f} | {be:.2f} |")
+    lines.append("")
+    text = "\n".join(lines)
+    if a.out:
+        with open(a.out, "w") as f:
+            f.write(text)
+    print(text)
+
+
+def counter_avgs(counter_csv: str, counter: str):
+    """Average value of `counter` per dispatch, per kernel name."""
+    tot, disp = defaultdict(float), defaultdict(set)
+    with open(counter_csv) as f:
+        for r in csv.DictReader(f):
+            if r["Counter_Name"] != counter:
+                continue
+            tot[r["Kernel_Name"]] += float(r["Counter_Value"])
+            disp[r["Kernel_Name"]].add(r["Dispatch_Id"])
+    return {k: tot[k] / len(disp[k]) for k in tot}
+
+
+def cmd_traffic(a):
+    fetch = counter_avgs(_one(os.path.join(a.fetch, "**", "*counter_collection.csv")), "FETCH_SIZE")
+    write = counter_avgs(_one(os.path.join(a.write, "**", "*counter_collection.csv")), "WRITE_SIZE")
+    cf = counter_avgs(_one(os.path.join(a.copy_fetch, "**", "*counter_collection.csv")), "FETCH_SIZE")
+    cw = counter_avgs(_one(os.path.join(a.copy_write, "**", "*counter_collection.csv")), "WRITE_SIZE")
+    # the copy run launches one kernel kind: the largest per-dispatch figure is the copy
+    copy_bytes = a.copy_mib * 2 ** 20
+    f_fetch = copy_bytes / (max(cf.values()) * 1024.0)
+    f_write = copy_bytes / (max(cw.values()) * 1024.0)
+    stages = defaultdict(lambda: {"fetch_kib": 0.0, "write_kib": 0.0, "kernels": []})
+    for k in sorted(set(fetch) | set(write)):
+        st = stage_of(k)
+        if st == "other":
+            continue
+        stages[st]["fetch_kib"] += fetch.get(k, 0.0)
+        stages[st]["write_kib"] += write.get(k, 0.0)
+        stages[st]["kernels"].append(short_name(k))
+    out = {"workload": a.workload, "source_hash": source_hash(), "copy_mib": a.copy_mib,
+           "scale_fetch": f_fetch, "scale_write": f_write, "command": a.cmd, "stages": {}}
+    for st, v in stages.items():
+        hbm = v["fetch_kib"] * 1024.0 * f_fetch + v["write_kib"] * 1024.0 * f_write
+        out["stages"][st] = {"kernels": v["kernels"], "fetch_kib_per_launch": v["fetch_kib"],
+                             "write_kib_per_launch": v["write_kib"], "hbm_bytes_per_launch": hbm}
+    text = json.dumps(out, indent=1)
+    if a.out:
+        with open(a.out, "w") as f:
+            f.write(text + "\n")
+    print(text)
+
+
+def main():
+    p = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    sub = p.add_subparsers(dest="cmd_name", required=True)
+    s = sub.add_parser("stats")
+    s.add_argument("dir", help="rocprofv3 output directory (or the kernel_stats.csv itself)")
+    s.add_argument("--title", required=True)
+    s.add_argument("--cmd", required=True, help="the command that produced the profile")
+    s.add_argument("--last", type=int, default=0, help="also average the last N calls of each kernel")
+    s.add_argument("--bench-log", help="log of the profiled bench.py run (its JSON line)")
+    s.add_argument("--out")
+    t = sub.add_parser("traffic")
+    t.add_argument("--fetch", required=True)
+    t.add_argument("--write", required=True)
+    t.add_argument("--copy-fetch", required=True)
+    t.add_argument("--copy-write", required=True)
+    t.add_argument("--copy-mib", type=int, required=True)
+    t.add_argument("--workload", required=True)
+    t.add_argument("--cmd", required=True)
+    t.add_argument("--out")
+    a = p.parse_args()
+    cmd_stats(a) if a.cmd_name == "stats" else cmd_traffic(a)
+
+
+if __name__ == "__main__":
+    main()
