@@ -129,6 +129,69 @@ __device__ __forceinline__ void store_tile(const f32x16 (&acc)[NB][TM][TN], cons
 __device__ __forceinline__ int64_t sk_begin(int64_t w, int64_t W, int64_t G) { return w * W / G; }
 __device__ __forceinline__ int64_t sk_owner(int64_t s, int64_t W, int64_t G) { return ((s + 1) * G - 1) / W; }
 
+// Stream-K schedule over G workgroups: the first dp = (T / G) G tiles run whole, one per
+// workgroup per round; the remaining T - dp tiles are cut into G equal (tile, K slice)
+// ranges, so every workgroup streams the same number of K slices.
+struct SkPlan {
+  int dp;     // data-parallel tiles
+  int64_t W;  // stream-K work items: (T - dp) * nk
+};
+__device__ __forceinline__ SkPlan sk_plan(int T, int G, int nk) {
+  SkPlan s;
+  s.dp = T / G * G;
+  s.W = (int64_t)(T - s.dp) * nk;
+  return s;
+}
+
+// fp32 partial tiles. A slot holds one workgroup's raw accumulators of one tile as 16-byte
+// groups: group g (of NACC / 4 per lane) of wave w, lane l at float4 index
+// ((slot * 8 + w) * NACC / 4 + g) * 64 + l, with g = ((m * TM + i) * TN + j) * 4 + q
+// holding accumulator elements 4q .. 4q + 3 of block (m, i, j).
+template <int BM, int BNF, int NB>
+struct Frag {
+  static constexpr int WM = BM / 2, WN = BNF / 4, TM = WM / 32, TN = WN / 32;
+  static constexpr int NACC = NB * TM * TN * 16;
+  static constexpr int G4 = TM * TN * 4;       // 16-byte groups per matrix per lane
+  static constexpr int ITEMS = 8 * G4 * 64;    // fix-up threads per tile
+};
+
+template <int BM, int BNF, int NB>
+__device__ __forceinline__ f32x4* slot_base(const GemmParams& p, int64_t slot, int wid) {
+  return reinterpret_cast<f32x4*>(p.partial) + (slot * 8 + wid) * (Frag<BM, BNF, NB>::NACC / 4) * 64;
+}
+
+// Fix-up thread `it` of a tile: sums the 16-byte groups (one per matrix) of the slots that
+// next_slot() yields, in order, applies the epilogue and stores 4 bf16 of one row.
+template <int BM, int BNF, int NB, int ACT, typename Slots>
+__device__ __forceinline__ void fixup_item(const GemmParams& p, const Tile& tl, int it, Slots next_slot) {
+  using FR = Frag<BM, BNF, NB>;
+  const int w = it / (FR::G4 * 64), rem = it % (FR::G4 * 64);
+  const int g = rem / 64, lane = rem % 64;
+  f32x4 acc[NB];
+#pragma unroll
+  for (int m = 0; m < NB; ++m) acc[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+  int64_t slot;
+  while (next_slot(slot)) {
+    const f32x4* P = slot_base<BM, BNF, NB>(p, slot, w) + lane;
+#pragma unroll
+    for (int m = 0; m < NB; ++m) acc[m] += P[(m * FR::G4 + g) * 64];
+  }
+  const int q = g % 4, ij = g / 4, i = ij / FR::TN, j = ij % FR::TN;
+  const int row = (w >> 2) * FR::WM + 32 * i + (lane & 31);
+  if (row >= tl.mcount) return;
+  const int col = (w & 3) * FR::WN + 32 * j + 8 * q + 4 * (lane >> 5);
+  bf16x4 o;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    float v;
+    if constexpr (NB == 2) v = activate<ACT>(acc[0][u]) * acc[1][u];
+    else v = acc[0][u];
+    o[u] = (bf16)v;
+  }
+  bf16* C = reinterpret_cast<bf16*>(p.C) + (tl.row_base + row) * p.N + tl.n0 + col;
+  *reinterpret_cast<bf16x4*>(C) = o;
+}
+
 // STREAMK = false: persistent full tiles per XCD share, tail round split along K.
 // STREAMK = true : stream-K; the (tile, K slice) list is cut into equal contiguous ranges,
 //                  one per workgroup; a tile cut by a range boundary leaves fp32 partials
@@ -194,25 +257,32 @@ __global__ __launch_bounds__(512, 1) void k_gemm_bf16(const GemmParams p) {
 
   // Work units of this workgroup. Persistent: its full-K tiles of each round, then (if
   // any) one K piece of a tail tile. Stream-K: every tile its range touches.
-  int units, sk_t0 = 0;
+  int units, sk_t0 = 0, dp_rounds = 0;
   int64_t sk_s0 = 0, sk_s1 = 0;
+  SkPlan sk{0, 0};
   if constexpr (STREAMK) {
-    const int64_t W = (int64_t)ts.total * nk;
-    sk_s0 = sk_begin(blockIdx.x, W, gridDim.x);
-    sk_s1 = sk_begin(blockIdx.x + 1, W, gridDim.x);
+    sk = sk_plan(ts.total, gridDim.x, nk);
+    dp_rounds = sk.dp / gridDim.x;
+    sk_s0 = sk_begin(blockIdx.x, sk.W, gridDim.x);
+    sk_s1 = sk_begin(blockIdx.x + 1, sk.W, gridDim.x);
     sk_t0 = (int)(sk_s0 / nk);
-    units = sk_s1 > sk_s0 ? (int)((sk_s1 - 1) / nk) - sk_t0 + 1 : 0;
+    units = dp_rounds + (sk_s1 > sk_s0 ? (int)((sk_s1 - 1) / nk) - sk_t0 + 1 : 0);
   } else {
     units = sh.rounds + (slot < sh.tail * sh.S ? 1 : 0);
   }
   for (int u = 0; u < units; ++u) {
     int L, kb = 0, ke = nk, pslot = -1;
     if constexpr (STREAMK) {
-      L = sk_t0 + u;
-      const int64_t base = (int64_t)L * nk;
-      kb = (int)(max(sk_s0, base) - base);
-      ke = (int)(min(sk_s1, base + nk) - base);
-      if (kb != 0 || ke != nk) pslot = 2 * blockIdx.x + (u == 0 ? 0 : 1);
+      if (u < dp_rounds) {
+        L = blockIdx.x + u * gridDim.x;
+      } else {
+        const int ls = sk_t0 + (u - dp_rounds);  // tile index within the stream-K tiles
+        const int64_t base = (int64_t)ls * nk;
+        kb = (int)(max(sk_s0, base) - base);
+        ke = (int)(min(sk_s1, base + nk) - base);
+        if (kb != 0 || ke != nk) pslot = 2 * blockIdx.x + (u == dp_rounds ? 0 : 1);
+        L = sk.dp + ls;
+      }
     } else if (u < sh.rounds) {
       L = sh.lo + slot + u * nslot;
     } else {
@@ -308,8 +378,8 @@ __global__ __launch_bounds__(512, 1) void k_gemm_bf16(const GemmParams p) {
     __syncthreads();  // every wave done reading the ring before the next tile refills it
 
     if (pslot >= 0) {
-      // A K piece of a tail tile: keep the raw fp32 accumulators for the reduction.
-      float* P = p.partial + ((int64_t)pslot * 8 + wid) * (NB * TM * TN * 16) * 64 + lane;
+      // A K piece of a tile: keep the raw fp32 accumulators for the fix-up.
+      f32x4* P = slot_base<BM, BNF, NB>(p, pslot, wid) + lane;
 #pragma unroll
       for (int m = 0; m < NB; ++m)
 #pragma unroll
@@ -317,98 +387,82 @@ __global__ __launch_bounds__(512, 1) void k_gemm_bf16(const GemmParams p) {
 #pragma unroll
           for (int j = 0; j < TN; ++j)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) P[(((m * TM + i) * TN + j) * 16 + r) * 64] = acc[m][i][j][r];
+            for (int q = 0; q < 4; ++q)
+              P[(((m * TM + i) * TN + j) * 4 + q) * 64] =
+                  f32x4{acc[m][i][j][4 * q], acc[m][i][j][4 * q + 1], acc[m][i][j][4 * q + 2], acc[m][i][j][4 * q + 3]};
     } else {
       store_tile<NB, ACT, TM, TN, WM, WN>(acc, tl, p, wm, wn, lane);
     }
   }
 }
 
-// Sums the K pieces of the tail tiles of each XCD share in piece order and stores the
-// tiles. Workgroup b handles tail tile b % nslot of XCD b / nslot; it repeats the GEMM's
-// schedule arithmetic from counts[] so both kernels agree on the split.
+// Fix-up of the tail split: sums the K pieces of every split tail tile in piece order and
+// stores the tiles. Grid-stride over (tail tile, fix-up thread); the tail tiles of the XCD
+// shares are numbered in XCD order. Repeats the GEMM's schedule arithmetic from counts[]
+// so both kernels agree on the split. Every wave handles 64 consecutive threads of one
+// tile (ITEMS is a multiple of 64), so the tile lookup stays wave-uniform.
 template <int BM, int BNF, int NB, int ACT, int BK>
-__global__ __launch_bounds__(512) void k_gemm_tail_reduce(const GemmParams p, int nslot) {
-  constexpr int WM = BM / 2, WN = BNF / 4;
-  constexpr int TM = WM / 32, TN = WN / 32;
-  constexpr int NACC = NB * TM * TN * 16;
-  const int lane = threadIdx.x & 63;
-  const int wid = uniform(threadIdx.x >> 6);
-  const int wm = wid >> 2, wn = wid & 3;
-  const int xcd = blockIdx.x / nslot, i = blockIdx.x % nslot;
-  const TileScan ts = tile_scan<BM>(p);
-  const XcdShare sh = xcd_share(ts.total, xcd, kXcds, nslot, p.K / BK, p);
-  if (sh.S <= 1 || i >= sh.tail) return;
-  Tile tl;
-  if (!tile_of<BM, BNF>(p, ts, sh.lo + sh.rounds * nslot + i, tl)) return;
-  f32x16 acc[NB][TM][TN];
-#pragma unroll
-  for (int m = 0; m < NB; ++m)
-#pragma unroll
-    for (int a = 0; a < TM; ++a)
-#pragma unroll
-      for (int j = 0; j < TN; ++j)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[m][a][j][r] = 0.f;
-  for (int piece = 0; piece < sh.S; ++piece) {
-    const int pslot = xcd * nslot + piece * sh.tail + i;
-    const float* P = p.partial + ((int64_t)pslot * 8 + wid) * NACC * 64 + lane;
-#pragma unroll
-    for (int m = 0; m < NB; ++m)
-#pragma unroll
-      for (int a = 0; a < TM; ++a)
-#pragma unroll
-        for (int j = 0; j < TN; ++j)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) acc[m][a][j][r] += P[(((m * TM + a) * TN + j) * 16 + r) * 64];
-  }
-  store_tile<NB, ACT, TM, TN, WM, WN>(acc, tl, p, wm, wn, lane);
-}
-
-// Stream-K fix-up: workgroup b sums, in workgroup order, the partials of tile b if a
-// range boundary cut it, and stores the tile.
-template <int BM, int BNF, int NB, int ACT, int BK>
-__global__ __launch_bounds__(512) void k_gemm_streamk_reduce(const GemmParams p, int grid) {
-  constexpr int WM = BM / 2, WN = BNF / 4;
-  constexpr int TM = WM / 32, TN = WN / 32;
-  constexpr int NACC = NB * TM * TN * 16;
-  const int lane = threadIdx.x & 63;
-  const int wid = uniform(threadIdx.x >> 6);
-  const int wm = wid >> 2, wn = wid & 3;
+__global__ __launch_bounds__(256) void k_gemm_tail_reduce(const GemmParams p, int nslot) {
+  using FR = Frag<BM, BNF, NB>;
   const int nk = p.K / BK;
   const TileScan ts = tile_scan<BM>(p);
-  const int t = blockIdx.x;
-  if (t >= ts.total) return;
-  const int64_t W = (int64_t)ts.total * nk;
-  const int64_t wa = sk_owner((int64_t)t * nk, W, grid), wb = sk_owner((int64_t)(t + 1) * nk - 1, W, grid);
-  if (wa == wb) return;  // stored directly by its only workgroup
-  Tile tl;
-  if (!tile_of<BM, BNF>(p, ts, t, tl)) return;
-  f32x16 acc[NB][TM][TN];
-#pragma unroll
-  for (int m = 0; m < NB; ++m)
-#pragma unroll
-    for (int a = 0; a < TM; ++a)
-#pragma unroll
-      for (int j = 0; j < TN; ++j)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[m][a][j][r] = 0.f;
-  for (int64_t w = wa; w <= wb; ++w) {
-    const int64_t b0 = sk_begin(w, W, grid);
-    if (sk_begin(w + 1, W, grid) <= b0) continue;  // empty range (fewer items than workgroups)
-    const int first = (int)(b0 / nk);
-    const int64_t pslot = 2 * w + (t == first ? 0 : 1);
-    const float* P = p.partial + (pslot * 8 + wid) * NACC * 64 + lane;
-#pragma unroll
-    for (int m = 0; m < NB; ++m)
-#pragma unroll
-      for (int a = 0; a < TM; ++a)
-#pragma unroll
-        for (int j = 0; j < TN; ++j)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) acc[m][a][j][r] += P[(((m * TM + a) * TN + j) * 16 + r) * 64];
+  int total = 0;
+  for (int x = 0; x < kXcds; ++x) {
+    const XcdShare sh = xcd_share(ts.total, x, kXcds, nslot, nk, p);
+    if (sh.S > 1) total += sh.tail;
   }
-  store_tile<NB, ACT, TM, TN, WM, WN>(acc, tl, p, wm, wn, lane);
+  const int64_t items = (int64_t)total * FR::ITEMS;
+  for (int64_t gi = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; gi < items; gi += (int64_t)gridDim.x * blockDim.x) {
+    int i = (int)(gi / FR::ITEMS);
+    const int it = (int)(gi % FR::ITEMS);
+    int x = 0;
+    XcdShare sh = xcd_share(ts.total, 0, kXcds, nslot, nk, p);
+    for (;;) {
+      const int n = sh.S > 1 ? sh.tail : 0;
+      if (i < n || x == kXcds - 1) break;
+      i -= n;
+      sh = xcd_share(ts.total, ++x, kXcds, nslot, nk, p);
+    }
+    Tile tl;
+    if (!tile_of<BM, BNF>(p, ts, sh.lo + sh.rounds * nslot + i, tl)) continue;
+    int piece = 0;
+    fixup_item<BM, BNF, NB, ACT>(p, tl, it, [&](int64_t& slot) {
+      if (piece >= sh.S) return false;
+      slot = (int64_t)x * nslot + (int64_t)piece * sh.tail + i;
+      ++piece;
+      return true;
+    });
+  }
+}
+
+// Stream-K fix-up: for every stream-K tile cut by a range boundary, sums the partials of
+// the workgroups that share it in workgroup order and stores the tile. Grid-stride over
+// (stream-K tile, fix-up thread), wave-uniform tiles as above.
+template <int BM, int BNF, int NB, int ACT, int BK>
+__global__ __launch_bounds__(256) void k_gemm_streamk_reduce(const GemmParams p, int grid) {
+  using FR = Frag<BM, BNF, NB>;
+  const int nk = p.K / BK;
+  const TileScan ts = tile_scan<BM>(p);
+  const SkPlan sk = sk_plan(ts.total, grid, nk);
+  const int64_t items = (int64_t)(ts.total - sk.dp) * FR::ITEMS;
+  for (int64_t gi = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; gi < items; gi += (int64_t)gridDim.x * blockDim.x) {
+    const int ls = (int)(gi / FR::ITEMS), it = (int)(gi % FR::ITEMS);
+    const int64_t wa = sk_owner((int64_t)ls * nk, sk.W, grid), wb = sk_owner((int64_t)(ls + 1) * nk - 1, sk.W, grid);
+    if (wa == wb) continue;  // stored directly by its only workgroup
+    Tile tl;
+    if (!tile_of<BM, BNF>(p, ts, sk.dp + ls, tl)) continue;
+    int64_t w = wa;
+    fixup_item<BM, BNF, NB, ACT>(p, tl, it, [&](int64_t& slot) {
+      for (; w <= wb; ++w) {
+        const int64_t b0 = sk_begin(w, sk.W, grid);
+        if (sk_begin(w + 1, sk.W, grid) <= b0) continue;  // empty range (fewer items than workgroups)
+        slot = 2 * w + ((int64_t)ls == b0 / nk ? 0 : 1);
+        ++w;
+        return true;
+      }
+      return false;
+    });
+  }
 }
 
 int g_num_cus = 0;
@@ -431,19 +485,27 @@ template <int BM, int BNF, int NB, int ACT, int BK, int STAGES, bool STREAMK>
 hipError_t launch_act(const GemmParams& p, int64_t bound, hipStream_t s) {
   // fp32 partial tiles: 8 waves x NACC accumulators x 64 lanes per slot; stream-K uses two
   // slots per workgroup, the tail split one.
-  constexpr size_t kSlotBytes = (size_t)8 * (NB * (BM / 64) * (BNF / 128) * 16) * 64 * sizeof(float);
+  using FR = Frag<BM, BNF, NB>;
+  constexpr size_t kSlotBytes = (size_t)8 * FR::NACC * 64 * sizeof(float);
   static_assert((STREAMK ? 2 : 1) * kGemmPartialUnits * kSlotBytes <= kGemmPartialBytes, "partial scratch");
+  // Fix-up grid: at most `grid` split tiles (tail tiles < one round; stream-K tiles < G).
+  auto fixup_grid = [&](int grid) {
+    const int64_t threads = (bound < grid ? bound : grid) * (int64_t)FR::ITEMS;
+    const int64_t wg = (threads + 255) / 256;
+    return (unsigned)(wg < 2048 ? wg : 2048);
+  };
   if constexpr (STREAMK) {
-    // Every compute unit takes an equal share of the work; the fix-up covers every tile.
+    // Every compute unit takes an equal share of the K slices.
     const int grid = persistent_grid(1 << 30);
     hipLaunchKernelGGL((k_gemm_bf16<BM, BNF, NB, ACT, BK, STAGES, true>), dim3(grid), dim3(512), 0, s, p);
-    hipLaunchKernelGGL((k_gemm_streamk_reduce<BM, BNF, NB, ACT, BK>), dim3((unsigned)bound), dim3(512), 0, s, p,
+    hipLaunchKernelGGL((k_gemm_streamk_reduce<BM, BNF, NB, ACT, BK>), dim3(fixup_grid(grid)), dim3(256), 0, s, p,
                        grid);
   } else {
     const int grid = persistent_grid(bound);
     hipLaunchKernelGGL((k_gemm_bf16<BM, BNF, NB, ACT, BK, STAGES, false>), dim3(grid), dim3(512), 0, s, p);
     if (p.partial != nullptr)
-      hipLaunchKernelGGL((k_gemm_tail_reduce<BM, BNF, NB, ACT, BK>), dim3(grid), dim3(512), 0, s, p, grid / kXcds);
+      hipLaunchKernelGGL((k_gemm_tail_reduce<BM, BNF, NB, ACT, BK>), dim3(fixup_grid(grid)), dim3(256), 0, s, p,
+                         grid / kXcds);
   }
   return hipGetLastError();
 }
