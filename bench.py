@@ -68,11 +68,13 @@ def cpu_baseline(cfg, inp, sample: int):
     N = cfg["N"]
     t0 = time.perf_counter()
     logits = orc.router_logits(inp["x"], inp["w_r"], inp["logit_bias"])
-    r = orc.route(logits, cfg["k"], cfg["routing_mode"],
-                  inp["noise"] if cfg["second_choice"] == "noisy" else None)
+    sc = cfg["second_choice"]
+    r = orc.route(logits, cfg["k"], cfg["routing_mode"], inp["noise"] if sc != "topk" else None,
+                  noise_all=sc == "noisy_all")
     padded = cfg["capacity_mode"] == "padded"
-    C = orc.capacity(N, cfg["E"], cfg["k"], cfg["capacity_factor"], cfg["min_capacity"]) if padded else None
-    o = orc.dispatch(r.idx, r.gate, cfg["E"], C, padded)
+    C = (orc.capacity(N, cfg["E"], cfg["k"], cfg["capacity_factor"], cfg["min_capacity"], cfg["capacity_formula"])
+         if padded else None)
+    o = orc.dispatch(r.idx, r.gate, cfg["E"], C, padded, token_major=cfg["capacity_priority"] == "token_major")
     t1 = time.perf_counter()
     toks = np.linspace(0, N - 1, min(sample, N)).astype(np.int64)
     orc.layer_tokens(toks, inp["x"], inp["w1"], inp["w2"], inp["w3"], r.idx, o.dropped, o.gate_eff,

@@ -72,12 +72,16 @@ enum { MOE_DT_F32 = 0, MOE_DT_BF16 = 1 };
  *                [BOOK12] §12.1). */
 enum { MOE_ROUTE_SOFTMAX_TOPK = 0, MOE_ROUTE_TOPK_SOFTMAX = 1 };
 
-/* Selection of slots 1..k-1 ([SERIES] §3, GShard random routing):
- *  TOPK : all k slots are the k largest clean logits.
- *  NOISY: slot 0 is the clean argmax; slot j>=1 is the argmax, over experts not yet
- *         chosen, of fl32(logit + noise) where noise[N,E] is supplied by the caller.
- *         Gates always use the clean probabilities. */
-enum { MOE_SECOND_TOPK = 0, MOE_SECOND_NOISY = 1 };
+/* Noise in the selection (noise[N,E] fp32 is supplied by the caller):
+ *  TOPK     : no noise; all k slots are the k largest logits.
+ *  NOISY    : GShard random routing ([SERIES] §3): slot 0 is the clean argmax; slot
+ *             j>=1 is the argmax, over experts not yet chosen, of fl32(logit + noise).
+ *             Gates, probabilities and statistics use the clean logits.
+ *  NOISY_ALL: noisy top-k gating ([GROK5] §5.2.2, logit' = logit + N(0, sigma)): the
+ *             logits are replaced by logit' = fl32(logit + noise) before softmax,
+ *             selection and gates; logits_out and probs_out report logit' and its
+ *             softmax, and the balance statistic uses that softmax. */
+enum { MOE_SECOND_TOPK = 0, MOE_SECOND_NOISY = 1, MOE_SECOND_NOISY_ALL = 2 };
 
 /* Activation of the W1 branch: f_e(x) = [act(x W1_e) * (x W2_e)] W3_e
  * ([BOOK12] §12.1 gated FFN with SiLU; [GROK5] §5.3.5 GELU(x W_g) * (x W_v), exact erf
@@ -89,6 +93,20 @@ enum { MOE_ACT_SILU = 0, MOE_ACT_GELU_ERF = 1, MOE_ACT_GELU_TANH = 2 };
  *  PADDED: zero-padded [E, C, D] buffers with capacity C ([SERIES] §2.1, §2.3);
  *          rows = E*C; records beyond C are dropped ([F2C] §3.2). */
 enum { MOE_CAP_NONE = 0, MOE_CAP_PADDED = 1 };
+
+/* Order in which records claim capacity positions (PADDED; with NONE it only orders the
+ * rows inside each expert):
+ *  SLOT_MAJOR : every slot-0 record (tokens ascending) before every slot-1 record, and
+ *               so on, so first choices are served before second choices.
+ *  TOKEN_MAJOR: token by token, slots ascending inside a token, the loop of
+ *               dispatch_to_experts ([F2C] §3.2). */
+enum { MOE_PRIO_SLOT_MAJOR = 0, MOE_PRIO_TOKEN_MAJOR = 1 };
+
+/* Capacity formula (PADDED):
+ *  TOKENS_K: C = ceil(CF * N * k / E)     ([F2C] §3.1; [SERIES] §2.1)
+ *  TOKENS  : C = ceil((N / E) * CF)       (Switch, no k: [SERIES] §7.2)
+ * then C = max(C, min_capacity). */
+enum { MOE_CAPF_TOKENS_K = 0, MOE_CAPF_TOKENS = 1 };
 
 typedef struct moe_desc {
   int64_t N;              /* tokens (B*T flattened, [BOOK12] §12.2)                      */
@@ -103,6 +121,8 @@ typedef struct moe_desc {
   int32_t capacity_mode;  /* MOE_CAP_*                                                   */
   int32_t min_capacity;   /* PADDED: lower bound on C (>= 0)                             */
   double capacity_factor; /* PADDED: CF > 0                                              */
+  int32_t capacity_priority; /* MOE_PRIO_*                                               */
+  int32_t capacity_formula;  /* MOE_CAPF_* (PADDED)                                      */
 } moe_desc;
 
 /* Limits of this implementation (MOE_E_UNSUPPORTED beyond them, MOE_E_INVAL below 1):
@@ -126,9 +146,11 @@ MOE_API const char* moe_status_string(int status);
 
 /* ---- host-only queries (no GPU work; safe without a device) ---------------------- */
 
-/* Expert capacity ([F2C] §3.1; [SERIES] §2.1 with min_capacity):
- *   PADDED: C = max(ceil(CF * N * k / E), min_capacity), evaluated in double as
- *           ceil(((CF*N)*k)/E). Worked example [SERIES] §2.1: N=8, E=4, k=2, CF=1 -> 4.
+/* Expert capacity ([F2C] §3.1; [SERIES] §2.1 with min_capacity, §7.2 Switch form):
+ *   PADDED, TOKENS_K: C = max(ceil(CF * N * k / E), min_capacity), evaluated in double
+ *           as ceil(((CF*N)*k)/E). Worked example [SERIES] §2.1: N=8, E=4, k=2, CF=1 -> 4.
+ *   PADDED, TOKENS  : C = max(ceil((N / E) * CF), min_capacity), evaluated in double as
+ *           ceil((N/E)*CF).
  *   NONE  : C = N (no expert can receive more than N records, so nothing drops).
  * Errors: MOE_E_INVAL for NULL pointers, N<1, E<1, k<1, k>E, or CF<=0 in PADDED mode
  * (the invalid-input rule of [F2C] §3.1). */
@@ -178,7 +200,7 @@ MOE_API int moe_workspace_layout(const moe_desc* desc, moe_ws_layout* layout);
  *   x          [N,D] dtype       required unless logits_in is given (then ignored)
  *   w_r        [D,E] fp32        required unless logits_in is given (then ignored)
  *   logit_bias [E]   fp32        optional additive per-expert logit bias (NULL = none)
- *   noise      [N,E] fp32        required iff second_choice == NOISY, else ignored
+ *   noise      [N,E] fp32        required iff second_choice is NOISY or NOISY_ALL, else ignored
  *   logits_in  [N,E] fp32        optional: route these logits and skip the GEMM
  *   logits_out [N,E] fp32        optional output of the logits
  *   probs_out  [N,E] fp32        optional output of softmax over all E
@@ -195,8 +217,9 @@ MOE_API int moe_route(const moe_desc* desc, const void* x, const float* w_r, con
  * ([F2C] §1.3 load, §3.1-3.2 capacity and dropped mask; [SERIES] §2.2 overflow cases,
  *  §2.3 zero padding; [BOOK12] §12.2 expert-grouped buffers).
  *   load[e]   = #{(t,j): topk_idx[t,j] = e}   (before capacity)
- *   Slot positions are assigned slot-major: every slot-0 record (tokens ascending)
- *   before every slot-1 record, and so on; a record is kept iff its position < C.
+ *   Positions inside an expert are assigned in the order of capacity_priority
+ *   (MOE_PRIO_*: slot-major by default, or token-major); a record is kept iff its
+ *   position < C.
  *   counts[e] = min(load[e], C) rows filled; offsets[e] = first row of expert e
  *   (NONE: exclusive scan of counts; PADDED: e*C); offsets[E] = rows.
  *   row_of[t,j] = row of the record, or -1 if dropped; dropped[t,j] = 1 if dropped.

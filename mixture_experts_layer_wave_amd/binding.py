@@ -20,7 +20,9 @@ LIB_PATH = os.path.join(PKG, "libmoe_mi355x.so")
 MOE_OK, MOE_E_INVAL, MOE_E_UNSUPPORTED, MOE_E_WORKSPACE, MOE_E_HIP = 0, -1, -2, -3, -4
 DTYPE = {"f32": 0, "bf16": 1}
 ROUTE = {"softmax_topk": 0, "topk_softmax": 1}
-SECOND = {"topk": 0, "noisy": 1}
+SECOND = {"topk": 0, "noisy": 1, "noisy_all": 2}
+PRIO = {"slot_major": 0, "token_major": 1}
+CAPF = {"tokens_k": 0, "tokens": 1}
 ACT = {"silu": 0, "gelu_erf": 1, "gelu_tanh": 2}
 CAP = {"none": 0, "padded": 1}
 EXPORTED = ["moe_status_string", "moe_capacity", "moe_rows", "moe_scratch_size", "moe_workspace_size",
@@ -40,7 +42,8 @@ class moe_desc(ctypes.Structure):
                 ("E", ctypes.c_int32), ("k", ctypes.c_int32), ("dtype", ctypes.c_int32),
                 ("routing_mode", ctypes.c_int32), ("second_choice", ctypes.c_int32),
                 ("activation", ctypes.c_int32), ("capacity_mode", ctypes.c_int32),
-                ("min_capacity", ctypes.c_int32), ("capacity_factor", ctypes.c_double)]
+                ("min_capacity", ctypes.c_int32), ("capacity_factor", ctypes.c_double),
+                ("capacity_priority", ctypes.c_int32), ("capacity_formula", ctypes.c_int32)]
 
 
 class moe_stats(ctypes.Structure):
@@ -107,7 +110,8 @@ def make_desc(cfg: dict) -> moe_desc:
     return moe_desc(int(cfg["N"]), int(cfg["D"]), int(cfg["F"]), int(cfg["E"]), int(cfg["k"]),
                     DTYPE[cfg["dtype"]], ROUTE[cfg["routing_mode"]], SECOND[cfg["second_choice"]],
                     ACT[cfg["activation"]], CAP[cfg["capacity_mode"]], int(cfg.get("min_capacity", 0)),
-                    float(cfg.get("capacity_factor", 0.0)))
+                    float(cfg.get("capacity_factor", 0.0)), PRIO[cfg.get("capacity_priority", "slot_major")],
+                    CAPF[cfg.get("capacity_formula", "tokens_k")])
 
 
 def _tdtype(d: moe_desc):

@@ -5,14 +5,17 @@
 // rate; "8.1 MoE 系列" §2.1-2.3 capacity, overflow cases A/B and zero-padded buffers;
 // "第 12 章 MoE：路由、专家与负载" §12.2 expert-grouped buffers, N*k records):
 //   load[e] counts the (token, slot) records of expert e. Positions inside an expert are
-//   assigned slot-major: all slot-0 records in token order, then slot 1, ...; a record
-//   is kept iff its position is below the capacity C. A token whose kept slots are a
+//   assigned slot-major (all slot-0 records in token order, then slot 1, ...) or, on
+//   request, token-major (the dispatch_to_experts loop of "MoE 公式到源码对照" §3.2:
+//   token by token, slots ascending); a record is kept iff its position is below C. A token whose kept slots are a
 //   strict subset keeps the whole gate mass on them; a token with none kept contributes 0.
 //
-// Design: deterministic by construction, with no global atomics. Three passes:
-//   count  : each 256-token workgroup builds, per slot, its expert histogram with one
+// Design: deterministic by construction, with no global atomics. Three passes over
+// "segments" (one per slot in slot-major order; a single segment of all slots in
+// token-major order):
+//   count  : each 256-token workgroup builds, per segment, its expert histogram with one
 //            wave ballot per expert (rank = popcount of lower lanes with equal expert);
-//   scan   : one wave scans the block histograms in (slot, block) order per expert,
+//   scan   : one wave scans the block histograms in (segment, block) order per expert,
 //            giving each block's base position, the loads, counts and offsets;
 //   assign : the same ballots give each record's rank inside its block; position =
 //            base + rank. Rows, drop mask and gates after the drop rule are written.
@@ -39,11 +42,58 @@ __device__ __forceinline__ void wave_match(int e, int E, int (*cnt_s)[kMaxE], in
   }
 }
 
+// Token-major match over all k slots of each lane's token: on return rank[j] = records of
+// expert e[j] in lower lanes (any slot) plus those in earlier slots of the same lane, and
+// cnt_s[w][x] = records of expert x in wave w.
+__device__ __forceinline__ void wave_match_tokens(const int (&e)[kMaxK], int k, int E, int (*cnt_s)[kMaxE],
+                                                  int (&rank)[kMaxK]) {
+  const int w = threadIdx.x >> 6;
+  const int lane = lane_id();
+  const uint64_t lt = lanemask_lt();
+#pragma unroll
+  for (int j = 0; j < kMaxK; ++j) rank[j] = 0;
+  for (int x = 0; x < E; ++x) {
+    int c = 0, below = 0;
+    for (int j = 0; j < k; ++j) {
+      const uint64_t m = __ballot(e[j] == x);
+      c += __popcll(m);
+      below += __popcll(m & lt);
+    }
+    int same = 0;  // earlier slots of this lane with expert x
+#pragma unroll
+    for (int j = 0; j < kMaxK; ++j) {
+      if (j < k && e[j] == x) {
+        rank[j] = below + same;
+        ++same;
+      }
+    }
+    if (lane == 0) cnt_s[w][x] = c;
+  }
+}
+
+__device__ __forceinline__ void load_experts(const DispatchArgs& a, int64_t t, bool valid, int (&e)[kMaxK]) {
+#pragma unroll
+  for (int j = 0; j < kMaxK; ++j) {
+    int v = (valid && j < a.k) ? a.topk_idx[t * a.k + j] : -1;
+    if (v >= a.E) v = -1;  // out-of-range ids are ignored (they never index LDS or scratch)
+    e[j] = v;
+  }
+}
+
 __global__ __launch_bounds__(256) void k_dispatch_count(const DispatchArgs a) {
   __shared__ int cnt_s[4][kMaxE];
   const int tid = threadIdx.x;
   const int64_t t = (int64_t)blockIdx.x * kTB + tid;
   const bool valid = t < a.N;
+  if (a.token_major) {
+    int e[kMaxK], rank[kMaxK];
+    load_experts(a, t, valid, e);
+    wave_match_tokens(e, a.k, a.E, cnt_s, rank);
+    __syncthreads();
+    if (tid < a.E)
+      a.blockcnt[(int64_t)blockIdx.x * a.E + tid] = cnt_s[0][tid] + cnt_s[1][tid] + cnt_s[2][tid] + cnt_s[3][tid];
+    return;
+  }
   for (int j = 0; j < a.k; ++j) {
     int e = valid ? a.topk_idx[t * a.k + j] : -1;
     if (e >= a.E) e = -1;  // out-of-range ids are ignored (they never index LDS or scratch)
@@ -62,7 +112,8 @@ __global__ __launch_bounds__(64) void k_dispatch_scan(const DispatchArgs a) {
   const int e = threadIdx.x;
   if (e < a.E) {
     int run = 0;
-    for (int j = 0; j < a.k; ++j) {
+    const int nseg = a.token_major ? 1 : a.k;
+    for (int j = 0; j < nseg; ++j) {
       for (int b = 0; b < a.nblk; ++b) {
         const int64_t i = ((int64_t)j * a.nblk + b) * a.E + e;
         a.base[i] = run;
@@ -99,26 +150,40 @@ __global__ __launch_bounds__(256) void k_dispatch_assign(const DispatchArgs a) {
 #pragma unroll
   for (int j = 0; j < kMaxK; ++j) { row[j] = -1; kept[j] = false; }
 
+  // position = base of (segment, block, expert) + records of the expert in lower waves
+  // of the block + rank inside the wave; kept iff below C.
+  auto place = [&](int j, int e, int seg, int rank) {
+    int prefix = 0;
+    for (int ww = 0; ww < w; ++ww) prefix += cnt_s[ww][e];
+    const int64_t pos = (int64_t)a.base[((int64_t)seg * a.nblk + blockIdx.x) * a.E + e] + prefix + rank;
+    const bool k_ok = (a.C < 0) || (pos < a.C);
+    int r = -1;
+    if (k_ok) {
+      const int off = a.padded ? (int)((int64_t)e * a.C) : a.offsets[e];
+      r = off + (int)pos;
+    }
+#pragma unroll
+    for (int jj = 0; jj < kMaxK; ++jj)
+      if (jj == j) { row[jj] = r; kept[jj] = k_ok; }
+  };
+
+  if (a.token_major) {
+    int e[kMaxK], rank[kMaxK];
+    load_experts(a, t, valid, e);
+    wave_match_tokens(e, a.k, a.E, cnt_s, rank);
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < kMaxK; ++j)
+      if (j < a.k && e[j] >= 0) place(j, e[j], 0, rank[j]);
+    __syncthreads();
+  } else
   for (int j = 0; j < a.k; ++j) {
     int e = valid ? a.topk_idx[t * a.k + j] : -1;
     if (e >= a.E) e = -1;  // out-of-range ids are treated as dropped records
     int rank;
     wave_match(e, a.E, cnt_s, rank);
     __syncthreads();
-    if (e >= 0) {
-      int prefix = 0;
-      for (int ww = 0; ww < w; ++ww) prefix += cnt_s[ww][e];
-      const int64_t pos = (int64_t)a.base[((int64_t)j * a.nblk + blockIdx.x) * a.E + e] + prefix + rank;
-      const bool k_ok = (a.C < 0) || (pos < a.C);
-      int r = -1;
-      if (k_ok) {
-        const int off = a.padded ? (int)((int64_t)e * a.C) : a.offsets[e];
-        r = off + (int)pos;
-      }
-#pragma unroll
-      for (int jj = 0; jj < kMaxK; ++jj)
-        if (jj == j) { row[jj] = r; kept[jj] = k_ok; }
-    }
+    if (e >= 0) place(j, e, j, rank);
     __syncthreads();
   }
 

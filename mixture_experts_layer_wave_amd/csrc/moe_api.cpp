@@ -23,7 +23,9 @@ int check_desc(const moe_desc* d) {
   if (d->N < 1 || d->D < 1 || d->F < 1 || d->E < 1 || d->k < 1 || d->k > d->E) return MOE_E_INVAL;
   if (d->dtype != MOE_DT_F32 && d->dtype != MOE_DT_BF16) return MOE_E_INVAL;
   if (d->routing_mode != MOE_ROUTE_SOFTMAX_TOPK && d->routing_mode != MOE_ROUTE_TOPK_SOFTMAX) return MOE_E_INVAL;
-  if (d->second_choice != MOE_SECOND_TOPK && d->second_choice != MOE_SECOND_NOISY) return MOE_E_INVAL;
+  if (d->second_choice < MOE_SECOND_TOPK || d->second_choice > MOE_SECOND_NOISY_ALL) return MOE_E_INVAL;
+  if (d->capacity_priority != MOE_PRIO_SLOT_MAJOR && d->capacity_priority != MOE_PRIO_TOKEN_MAJOR) return MOE_E_INVAL;
+  if (d->capacity_formula != MOE_CAPF_TOKENS_K && d->capacity_formula != MOE_CAPF_TOKENS) return MOE_E_INVAL;
   if (d->activation < MOE_ACT_SILU || d->activation > MOE_ACT_GELU_TANH) return MOE_E_INVAL;
   if (d->capacity_mode != MOE_CAP_NONE && d->capacity_mode != MOE_CAP_PADDED) return MOE_E_INVAL;
   if (d->capacity_mode == MOE_CAP_PADDED && (!(d->capacity_factor > 0.0) || d->min_capacity < 0)) return MOE_E_INVAL;
@@ -36,7 +38,9 @@ int check_desc(const moe_desc* d) {
 
 int capacity_of(const moe_desc* d, int64_t* C) {
   if (d->capacity_mode == MOE_CAP_NONE) { *C = d->N; return MOE_OK; }
-  const double c = ceil(((d->capacity_factor * (double)d->N) * (double)d->k) / (double)d->E);
+  const double c = d->capacity_formula == MOE_CAPF_TOKENS
+                       ? ceil(((double)d->N / (double)d->E) * d->capacity_factor)
+                       : ceil(((d->capacity_factor * (double)d->N) * (double)d->k) / (double)d->E);
   if (!(c < 4.0e18)) return MOE_E_UNSUPPORTED;
   int64_t ci = (int64_t)c;
   if (ci < d->min_capacity) ci = d->min_capacity;
@@ -88,7 +92,7 @@ int do_route(const moe_desc* d, const void* x, const float* w_r, const float* bi
              void* scratch, hipStream_t st) {
   RouterArgs a{};
   a.x = x; a.w_r = w_r; a.bias = bias;
-  a.noise = d->second_choice == MOE_SECOND_NOISY ? noise : nullptr;
+  a.noise = d->second_choice != MOE_SECOND_TOPK ? noise : nullptr;
   a.logits_in = logits_in; a.logits_out = logits_out; a.probs_out = probs_out;
   a.topk_idx = idx; a.topk_gate = gate;
   if (scratch) {
@@ -97,7 +101,7 @@ int do_route(const moe_desc* d, const void* x, const float* w_r, const float* bi
     a.psum_magic = at<uint32_t>(scratch, s.header + 64);
   }
   a.N = d->N; a.D = (int)d->D; a.E = d->E; a.k = d->k;
-  a.mode = d->routing_mode; a.noisy = d->second_choice == MOE_SECOND_NOISY;
+  a.mode = d->routing_mode; a.noisy = d->second_choice;
   return status_of(launch_router(a, d->dtype == MOE_DT_BF16, st));
 }
 
@@ -119,6 +123,7 @@ int do_dispatch(const moe_desc* d, const void* x, const int32_t* idx, const floa
   a.load = load; a.counts = counts; a.offsets = offsets; a.row_of = row_of; a.dropped = dropped;
   a.gate_eff = gate_eff; a.token_of_row = token_of_row;
   a.N = d->N; a.E = d->E; a.k = d->k; a.nblk = s.nblk_d;
+  a.token_major = d->capacity_priority == MOE_PRIO_TOKEN_MAJOR;
   const bool padded = d->capacity_mode == MOE_CAP_PADDED;
   a.C = padded ? C : -1;
   a.padded = padded;
@@ -239,7 +244,7 @@ int moe_route(const moe_desc* d, const void* x, const float* w_r, const float* l
   int rc = check_desc(d);
   if (rc) return rc;
   if (!logits_in) { REQUIRE(x); REQUIRE(w_r); OPTIONAL(logit_bias); } else { REQUIRE(logits_in); }
-  if (d->second_choice == MOE_SECOND_NOISY) REQUIRE(noise);
+  if (d->second_choice != MOE_SECOND_TOPK) REQUIRE(noise);
   OPTIONAL(logits_out); OPTIONAL(probs_out);
   REQUIRE(topk_idx); REQUIRE(topk_gate);
   if (scratch) {
@@ -313,7 +318,7 @@ int moe_forward(const moe_desc* d, const void* x, const float* w_r, const float*
   int rc = check_desc(d);
   if (rc) return rc;
   REQUIRE(x); REQUIRE(w_r); OPTIONAL(logit_bias); REQUIRE(w1); REQUIRE(w2); REQUIRE(w3); REQUIRE(y);
-  if (d->second_choice == MOE_SECOND_NOISY) REQUIRE(noise);
+  if (d->second_choice != MOE_SECOND_TOPK) REQUIRE(noise);
   int64_t rows;
   rc = rows_of(d, &rows);
   if (rc) return rc;

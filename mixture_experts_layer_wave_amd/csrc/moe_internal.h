@@ -24,7 +24,8 @@ inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 //   header    : moe_stats (64 B) + magic word
 //   psum      : fp32 [nblk_r][E]   per-router-block sums of the probabilities
 //   blockcnt  : int32 [k][nblk_d][E] per-dispatch-block expert histogram of each slot
-//   base      : int32 [k][nblk_d][E] exclusive slot-major scan of blockcnt
+//               (token-major order: one segment [1][nblk_d][E] over all slots)
+//   base      : int32 [k][nblk_d][E] exclusive scan of blockcnt in record order
 //   tokdrop   : int32 [nblk_d]     tokens with every slot dropped, per block
 //   load      : int32 [E]          copy of the pre-capacity histogram
 //   partial   : fp32 split-K partial tiles of the bf16 grouped GEMM (bf16 layers only)
@@ -63,7 +64,8 @@ struct RouterArgs {
   float* psum;            // [nblk_r][E] or null
   uint32_t* psum_magic;   // or null
   int64_t N;
-  int D, E, k, mode, noisy;
+  int D, E, k, mode;
+  int noisy;  // MOE_SECOND_*: 1 = noise on slots >= 1, 2 = noise replaces the logits
 };
 hipError_t launch_router(const RouterArgs& a, bool bf16_x, hipStream_t s);
 
@@ -86,6 +88,7 @@ struct DispatchArgs {
   int E, k, nblk;
   int64_t C;                // -1: no capacity
   int padded;
+  int token_major;          // positions in token-major record order (else slot-major)
 };
 hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t s);
 

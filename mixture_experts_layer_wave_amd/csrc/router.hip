@@ -4,8 +4,9 @@
 // Method ("第 5 章 model.py 精读·中：MoE 路由与专家", §5.2, §5.2.1, §5.2.3; "MoE 公式到源码对照"
 // §1.1-1.2; "8.1 MoE 系列" §3 for the GShard noisy second choice):
 //   logits = fp32(x) W_r in fp32; p = softmax(logits) with the maximum subtracted;
-//   slots = k largest logits (lower index wins ties), slot 0 the largest; in noisy mode
-//   slots >= 1 use fl32(logit + noise) over the experts not chosen yet;
+//   slots = k largest logits (lower index wins ties), slot 0 the largest; in GShard mode
+//   slots >= 1 use fl32(logit + noise) over the experts not chosen yet; in noisy top-k
+//   gating ("第 5 章 ..." §5.2.2) logit' = fl32(logit + noise) replaces the logits;
 //   gates = p of the chosen experts (softmax-then-top-k) or softmax over the chosen
 //   logits (top-k-then-softmax, the renormalised form).
 //
@@ -156,6 +157,7 @@ __global__ __launch_bounds__(512) void k_router(const RouterArgs a) {
           if (a.bias != nullptr) v += a.bias[e];
         }
       }
+      if (a.noisy == 2 && e < E && t < a.N) v += a.noise[t * E + e];  // noisy top-k gating: logit'
       l[e] = v;
     }
     // stable softmax over the E experts
@@ -179,7 +181,7 @@ __global__ __launch_bounds__(512) void k_router(const RouterArgs a) {
       float z[EP];
 #pragma unroll
       for (int e = 0; e < EP; ++e) z[e] = l[e];
-      if (a.noisy) {
+      if (a.noisy == 1) {
 #pragma unroll
         for (int e = 0; e < EP; ++e) z[e] = (e < E) ? l[e] + a.noise[t * E + e] : 0.f;
       }
@@ -190,7 +192,7 @@ __global__ __launch_bounds__(512) void k_router(const RouterArgs a) {
       for (int j = 0; j < kMaxK; ++j) {
         sel[j] = 0;
         if (j < a.k) {
-          const bool use_z = (j > 0) && a.noisy;
+          const bool use_z = (j > 0) && a.noisy == 1;
           int best = -1;
           float bv = 0.f;
 #pragma unroll

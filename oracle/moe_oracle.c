@@ -23,7 +23,11 @@
  *   - Ties between equal fp32 values go to the lower expert index.
  *   - GShard noisy slot j>=1: argmax over unchosen experts of fl32(logit + noise)
  *     ([SERIES] §3, one noise draw per (token, expert)).
- *   - Capacity slots are filled slot-major, tokens ascending within a slot.
+ *   - Noisy top-k gating ([GROK5] §5.2.2, logit' = logit + N(0, sigma)): every quantity
+ *     after the logits (softmax, selection, gates) uses logit' = fl32(logit + noise).
+ *   - Capacity slots are filled slot-major, tokens ascending within a slot; the
+ *     token-major order of the [F2C] §3.2 loop is the alternative.
+ *   - Switch capacity ([SERIES] §7.2): C = ceil((N / E) * CF), no k.
  *   - Drop rule for a partly dropped token: the kept slots take the whole gate mass in
  *     proportion to their gates ([SERIES] §2.2 case A, generalised).
  *
@@ -92,10 +96,15 @@ void oracle_router_logits(int64_t N, int64_t D, int32_t E, int x_dtype, const vo
 #define MODE_SOFTMAX_TOPK 0 /* gates = full-softmax probabilities, unnormalised */
 #define MODE_TOPK_SOFTMAX 1 /* gates = softmax over the selected logits          */
 
-/* For each token t (logits are rounded to fp32 first, the router's precision):
+#define NOISE_NONE 0   /* clean top-k                                          */
+#define NOISE_SECOND 1 /* GShard: slots >= 1 compare fl32(l + noise)            */
+#define NOISE_ALL 2    /* noisy top-k gating: l is replaced by fl32(l + noise)  */
+
+/* For each token t (logits are rounded to fp32 first, the router's precision; with
+ * NOISE_ALL the fp32 logits are first replaced by fl32(l + noise[t,e])):
  *   probs[t,e] = exp(l_e - max l) / sum_e' exp(l_e' - max l)          ([F2C] §1.1)
  *   slot j: the unchosen expert with the largest value, lower index on ties; the value
- *   is l_e for slot 0 and for every slot when !noisy, else fl32(l_e + noise[t,e])
+ *   is l_e, except for slots j >= 1 under NOISE_SECOND: fl32(l_e + noise[t,e])
  *   ([GROK5] §5.2.3; [SERIES] §3)
  *   mode SOFTMAX_TOPK: gate_j = probs[t, idx_j]                        ([GROK5] §5.2.3 A)
  *   mode TOPK_SOFTMAX: gate_j = exp(l_{idx_j}) / sum_i exp(l_{idx_i})   ([BOOK12] §12.1)
@@ -106,7 +115,7 @@ void oracle_router_logits(int64_t N, int64_t D, int32_t E, int x_dtype, const vo
 int oracle_route(int64_t N, int32_t E, int32_t k, int mode, int noisy, const double* logits,
                  const float* noise, int32_t* idx, double* gate, double* probs, double* margin) {
   if (N < 0 || E < 1 || k < 1 || k > E || E > 4096) return ORACLE_EINVAL;
-  if (noisy && !noise) return ORACLE_EINVAL;
+  if (noisy < NOISE_NONE || noisy > NOISE_ALL || (noisy && !noise)) return ORACLE_EINVAL;
   int bad = 0;
 #pragma omp parallel for schedule(static) reduction(| : bad)
   for (int64_t t = 0; t < N; ++t) {
@@ -116,6 +125,8 @@ int oracle_route(int64_t N, int32_t E, int32_t k, int mode, int noisy, const dou
     unsigned char* chosen = (unsigned char*)calloc(E, 1);
     if (!l32 || !val || !q || !chosen) { bad = 1; free(l32); free(val); free(q); free(chosen); continue; }
     for (int32_t e = 0; e < E; ++e) l32[e] = (float)logits[t * E + e];
+    if (noisy == NOISE_ALL)
+      for (int32_t e = 0; e < E; ++e) l32[e] = l32[e] + noise[t * E + e]; /* fp32 sum, rounded once */
 
     /* softmax over all E experts of the fp32 logits */
     double m = l32[0];
@@ -127,7 +138,7 @@ int oracle_route(int64_t N, int32_t E, int32_t k, int mode, int noisy, const dou
     double tok_margin = INFINITY;
     for (int32_t j = 0; j < k; ++j) {
       for (int32_t e = 0; e < E; ++e)
-        val[e] = (j > 0 && noisy) ? (float)(l32[e] + noise[t * E + e]) : l32[e];
+        val[e] = (j > 0 && noisy == NOISE_SECOND) ? (float)(l32[e] + noise[t * E + e]) : l32[e];
       int32_t best = -1;
       for (int32_t e = 0; e < E; ++e)
         if (!chosen[e] && (best < 0 || val[e] > val[best])) best = e;
@@ -163,11 +174,15 @@ int oracle_route(int64_t N, int32_t E, int32_t k, int mode, int noisy, const dou
 
 /* ---- step 5: capacity ([F2C] §3.1; [SERIES] §2.1) ---------------------------------- */
 
-/* C = max(ceil(CF * N * k / E), min_capacity), the product evaluated left to right in
- * double. Invalid inputs are an error, as in [F2C] §3.1. */
-int oracle_capacity(int64_t N, int32_t E, int32_t k, double cf, int32_t min_capacity, int64_t* C) {
-  if (N < 0 || E <= 0 || cf <= 0.0 || k <= 0 || min_capacity < 0) return ORACLE_EINVAL;
-  double c = ceil(((cf * (double)N) * (double)k) / (double)E);
+/* formula 0: C = max(ceil(CF * N * k / E), min_capacity), the product evaluated left to
+ * right in double ([F2C] §3.1).
+ * formula 1: C = max(ceil((N / E) * CF), min_capacity), the Switch form without k
+ * ([SERIES] §7.2: tokens per batch / experts x capacity factor).
+ * Invalid inputs are an error, as in [F2C] §3.1. */
+int oracle_capacity(int64_t N, int32_t E, int32_t k, double cf, int32_t min_capacity, int formula, int64_t* C) {
+  if (N < 0 || E <= 0 || cf <= 0.0 || k <= 0 || min_capacity < 0 || formula < 0 || formula > 1)
+    return ORACLE_EINVAL;
+  double c = formula == 0 ? ceil(((cf * (double)N) * (double)k) / (double)E) : ceil(((double)N / (double)E) * cf);
   int64_t ci = (int64_t)c;
   *C = ci > min_capacity ? ci : (int64_t)min_capacity;
   return ORACLE_OK;
@@ -176,13 +191,14 @@ int oracle_capacity(int64_t N, int32_t E, int32_t k, double cf, int32_t min_capa
 /* ---- steps 5-6: load histogram, capacity slots, drop mask ----------------------------- */
 
 /* load[e] = #{(t,j): idx[t,j] = e}                                    ([F2C] §1.3)
- * Records are visited slot-major, tokens ascending within a slot; a record is accepted
- * while its expert holds fewer than C records, otherwise it is dropped ([F2C] §3.2).
+ * Records are visited slot-major (tokens ascending within a slot), or token-major (slots
+ * ascending within a token, the loop of [F2C] §3.2) when token_major; a record is
+ * accepted while its expert holds fewer than C records, otherwise it is dropped.
  * C < 0 means no capacity limit. counts[e] = accepted records of expert e.
  * offsets[e] = e*C when padded, else the exclusive prefix sum of counts; offsets[E] = rows.
  * row_of[t,j] = offsets[e] + position, or -1 when dropped. */
 int oracle_dispatch(int64_t N, int32_t E, int32_t k, const int32_t* idx, int64_t C, int padded,
-                    int64_t* load, int64_t* counts, int64_t* offsets, int64_t* row_of,
+                    int token_major, int64_t* load, int64_t* counts, int64_t* offsets, int64_t* row_of,
                     uint8_t* dropped) {
   if (N < 0 || E < 1 || k < 1 || (padded && C < 0)) return ORACLE_EINVAL;
   for (int32_t e = 0; e < E; ++e) { load[e] = 0; counts[e] = 0; }
@@ -194,18 +210,20 @@ int oracle_dispatch(int64_t N, int32_t E, int32_t k, const int32_t* idx, int64_t
     }
   int64_t* pos = (int64_t*)malloc(sizeof(int64_t) * (size_t)(N * k > 0 ? N * k : 1));
   if (!pos) return ORACLE_EINVAL;
-  for (int32_t j = 0; j < k; ++j)
-    for (int64_t t = 0; t < N; ++t) {
-      int32_t e = idx[t * k + j];
-      if (C < 0 || counts[e] < C) {
-        pos[t * k + j] = counts[e];
-        counts[e] += 1;
-        dropped[t * k + j] = 0;
-      } else {
-        pos[t * k + j] = -1;
-        dropped[t * k + j] = 1;
-      }
+  for (int64_t v = 0; v < N * k; ++v) {
+    /* the v-th record in visiting order */
+    const int64_t t = token_major ? v / k : v % N;
+    const int32_t j = token_major ? (int32_t)(v % k) : (int32_t)(v / N);
+    const int32_t e = idx[t * k + j];
+    if (C < 0 || counts[e] < C) {
+      pos[t * k + j] = counts[e];
+      counts[e] += 1;
+      dropped[t * k + j] = 0;
+    } else {
+      pos[t * k + j] = -1;
+      dropped[t * k + j] = 1;
     }
+  }
   int64_t run = 0;
   for (int32_t e = 0; e < E; ++e) {
     offsets[e] = padded ? (int64_t)e * C : run;

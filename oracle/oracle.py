@@ -27,6 +27,7 @@ ORACLE_LIB = os.path.join(HERE, "libmoe_oracle.so")
 
 ACT = {"silu": 0, "gelu_erf": 1, "gelu_tanh": 2}
 MODE = {"softmax_topk": 0, "topk_softmax": 1}
+CAPF = {"tokens_k": 0, "tokens": 1}
 
 _i64 = ctypes.c_int64
 _i32 = ctypes.c_int32
@@ -111,9 +112,9 @@ class Oracle:
         L.oracle_route.restype = _int
         L.oracle_route.argtypes = [_i64, _i32, _i32, _int, _int, _vp, _vp, _vp, _vp, _vp, _vp]
         L.oracle_capacity.restype = _int
-        L.oracle_capacity.argtypes = [_i64, _i32, _i32, _dbl, _i32, ctypes.POINTER(_i64)]
+        L.oracle_capacity.argtypes = [_i64, _i32, _i32, _dbl, _i32, _int, ctypes.POINTER(_i64)]
         L.oracle_dispatch.restype = _int
-        L.oracle_dispatch.argtypes = [_i64, _i32, _i32, _vp, _i64, _int, _vp, _vp, _vp, _vp, _vp]
+        L.oracle_dispatch.argtypes = [_i64, _i32, _i32, _vp, _i64, _int, _int, _vp, _vp, _vp, _vp, _vp]
         L.oracle_drop_rule.restype = None
         L.oracle_drop_rule.argtypes = [_i64, _i32, _vp, _vp, _vp]
         L.oracle_expert_ffn.restype = _int
@@ -146,8 +147,12 @@ class Oracle:
         self.lib.oracle_router_logits(N, D, E, _dtype_code(xh), _ptr(xh), _ptr(wr), _ptr(b), _ptr(out))
         return out
 
-    def route(self, logits, k: int, mode: str, noise=None) -> Routing:
-        """Softmax, selection and gates from logits (rounded to fp32 for the decisions)."""
+    def route(self, logits, k: int, mode: str, noise=None, noise_all: bool = False) -> Routing:
+        """Softmax, selection and gates from logits (rounded to fp32 for the decisions).
+
+        noise given: GShard second choice (slots >= 1 compare fl32(l + noise)), or, with
+        noise_all, noisy top-k gating (every step uses fl32(l + noise)). The returned
+        logits are the fp32 values the selection used (noisy ones under noise_all)."""
         lg = _host(logits, np.float64)
         N, E = lg.shape
         nz = _host(noise, np.float32)
@@ -155,22 +160,27 @@ class Oracle:
         gate = np.empty((N, k), np.float64)
         probs = np.empty((N, E), np.float64)
         margin = np.empty((N,), np.float64)
-        rc = self.lib.oracle_route(N, E, k, MODE[mode], 1 if nz is not None else 0, _ptr(lg), _ptr(nz),
+        noisy = 0 if nz is None else (2 if noise_all else 1)
+        rc = self.lib.oracle_route(N, E, k, MODE[mode], noisy, _ptr(lg), _ptr(nz),
                                    _ptr(idx), _ptr(gate), _ptr(probs), _ptr(margin))
         if rc != 0:
             raise ValueError("oracle_route: invalid inputs")
-        l32 = lg.astype(np.float32).astype(np.float64)
+        l32 = lg.astype(np.float32)
+        if noisy == 2:
+            l32 = l32 + nz  # fp32 sums, as the oracle compares them
+        l32 = l32.astype(np.float64)
         return Routing(l32, probs, idx, gate, margin)
 
     # -- capacity / dispatch -------------------------------------------------------------
-    def capacity(self, N: int, E: int, k: int, cf: float, min_capacity: int = 0) -> int:
+    def capacity(self, N: int, E: int, k: int, cf: float, min_capacity: int = 0, formula: str = "tokens_k") -> int:
+        """formula "tokens_k": ceil(CF N k / E) ([F2C] §3.1); "tokens": ceil((N / E) CF) ([SERIES] §7.2)."""
         c = _i64(0)
-        rc = self.lib.oracle_capacity(N, E, k, float(cf), int(min_capacity), ctypes.byref(c))
+        rc = self.lib.oracle_capacity(N, E, k, float(cf), int(min_capacity), CAPF[formula], ctypes.byref(c))
         if rc != 0:
             raise ValueError("invalid capacity inputs")
         return c.value
 
-    def dispatch(self, idx, gate, E: int, capacity: int | None, padded: bool) -> Dispatch:
+    def dispatch(self, idx, gate, E: int, capacity: int | None, padded: bool, token_major: bool = False) -> Dispatch:
         ih = _host(idx, np.int32)
         gh = _host(gate, np.float64)
         N, k = ih.shape
@@ -180,7 +190,8 @@ class Oracle:
         offsets = np.empty(E + 1, np.int64)
         row_of = np.empty((N, k), np.int64)
         dropped = np.empty((N, k), np.uint8)
-        rc = self.lib.oracle_dispatch(N, E, k, _ptr(ih), C, 1 if padded else 0, _ptr(load), _ptr(counts),
+        rc = self.lib.oracle_dispatch(N, E, k, _ptr(ih), C, 1 if padded else 0, 1 if token_major else 0,
+                                      _ptr(load), _ptr(counts),
                                       _ptr(offsets), _ptr(row_of), _ptr(dropped))
         if rc != 0:
             raise ValueError("oracle_dispatch: invalid inputs")
@@ -268,11 +279,13 @@ class Oracle:
         cfg = inputs["cfg"]
         if logits is None:
             logits = self.router_logits(inputs["x"], inputs["w_r"], inputs.get("logit_bias"))
+        sc = cfg["second_choice"]
         r = self.route(logits, cfg["k"], cfg["routing_mode"],
-                       inputs.get("noise") if cfg["second_choice"] == "noisy" else None)
+                       inputs.get("noise") if sc in ("noisy", "noisy_all") else None, noise_all=sc == "noisy_all")
         padded = cfg["capacity_mode"] == "padded"
-        C = self.capacity(cfg["N"], cfg["E"], cfg["k"], cfg["capacity_factor"], cfg["min_capacity"]) if padded else None
-        d = self.dispatch(r.idx, r.gate, cfg["E"], C, padded)
+        C = (self.capacity(cfg["N"], cfg["E"], cfg["k"], cfg["capacity_factor"], cfg["min_capacity"],
+                           cfg.get("capacity_formula", "tokens_k")) if padded else None)
+        d = self.dispatch(r.idx, r.gate, cfg["E"], C, padded, cfg.get("capacity_priority", "slot_major") == "token_major")
         if tokens is None:
             tokens = np.arange(cfg["N"])
         y = self.layer_tokens(tokens, inputs["x"], inputs["w1"], inputs["w2"], inputs["w3"], r.idx, d.dropped,

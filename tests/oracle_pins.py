@@ -95,6 +95,21 @@ def pin_capacity_examples(orc):
         raise AssertionError(f"invalid capacity inputs accepted: {c}")
 
 
+def pin_switch_capacity_examples(orc):
+    """Switch capacity without k ([SERIES] §7.2); for k = 1 it equals the k form."""
+    g = golden("switch_capacity_examples.json")
+    for c in g["cases"]:
+        assert orc.capacity(c["N"], c["E"], c["k"], c["cf"], c["min_capacity"], "tokens") == c["C"], c
+        if c["k"] == 1:
+            assert orc.capacity(c["N"], c["E"], 1, c["cf"], c["min_capacity"], "tokens_k") == c["C"], c
+    for c in g["invalid"]:
+        try:
+            orc.capacity(c["N"], c["E"], c["k"], c["cf"], 0, "tokens")
+        except ValueError:
+            continue
+        raise AssertionError(f"invalid capacity inputs accepted: {c}")
+
+
 # ---------------------------------------------------------------------------------------
 # Routing ([GROK5] §5.2.3; [F2C] §1.1-1.2; [SERIES] §1.2, §3; [BOOK12] §12.1)
 # ---------------------------------------------------------------------------------------
@@ -215,6 +230,40 @@ def pin_gshard_noisy_example(orc):
     assert clean.idx[0].tolist() == [0, 1] and clean.idx[1].tolist() == [2, 3]
 
 
+def pin_noisy_topk_example(orc):
+    """Noisy top-k gating ([GROK5] §5.2.2): the noisy logits drive selection and gates."""
+    g = golden("noisy_topk_example.json")
+    lg, nz = np.array(g["logits"]), np.array(g["noise"], np.float32)
+    r1 = orc.route(lg, 1, "softmax_topk", noise=nz, noise_all=True)
+    assert r1.idx.tolist() == g["top1"], r1.idx
+    _close(r1.gate, g["top1_gate_softmax_topk"], rtol=1e-12)
+    r2 = orc.route(lg, 2, "topk_softmax", noise=nz, noise_all=True)
+    assert r2.idx.tolist() == g["top2"], r2.idx
+    _close(r2.gate, g["top2_gates_topk_softmax"], rtol=1e-12)
+    clean = orc.route(lg, 1, "softmax_topk")
+    assert clean.idx[:, 0].tolist() == [0, 0]
+
+
+def pin_noisy_topk_invariants(orc):
+    """Zero noise reproduces the clean router; otherwise routing the noisy logits equals
+    routing fl32(logit + noise) with no noise (the noise replaces the logits everywhere,
+    probabilities included), in both gate modes."""
+    rng = np.random.default_rng(31)
+    lg = rng.standard_normal((64, 8)).astype(np.float32)
+    nz = rng.standard_normal((64, 8)).astype(np.float32)
+    for mode in ("softmax_topk", "topk_softmax"):
+        for k in (1, 2, 3):
+            a = orc.route(lg, k, mode, noise=np.zeros_like(nz), noise_all=True)
+            b = orc.route(lg, k, mode)
+            assert np.array_equal(a.idx, b.idx)
+            _close(a.gate, b.gate, rtol=0.0)
+            c = orc.route(lg, k, mode, noise=nz, noise_all=True)
+            d = orc.route((lg + nz).astype(np.float64), k, mode)
+            assert np.array_equal(c.idx, d.idx)
+            _close(c.gate, d.gate, rtol=1e-15)
+            _close(c.probs, d.probs, rtol=1e-15)
+
+
 # ---------------------------------------------------------------------------------------
 # Dispatch, capacity slots, drop rule ([F2C] §1.3, §3.2-3.3; [SERIES] §2.2; [BOOK12] §12.2)
 # ---------------------------------------------------------------------------------------
@@ -270,6 +319,48 @@ def pin_slot_major_priority(orc):
     # slot 0: t0->e1 pos0, t1->e0 pos0, t2->e0 pos1, t3->e1 pos1; every slot 1 drops.
     assert d.dropped.tolist() == [[0, 1], [0, 1], [0, 1], [0, 1]]
     assert d.row_of.tolist() == [[2, -1], [0, -1], [1, -1], [3, -1]]
+
+
+def pin_token_major_example(orc):
+    """The token-by-token loop of [F2C] §3.2 against its worked outcome, and the
+    slot-major order on the same records."""
+    g = golden("token_major_example.json")
+    idx, gate = np.array(g["idx"], np.int32), np.array(g["gate"])
+    for order in ("token_major", "slot_major"):
+        d = orc.dispatch(idx, gate, g["E"], g["capacity"], True, token_major=order == "token_major")
+        want = g[order]
+        assert d.load.tolist() == g["load"]
+        assert d.counts.tolist() == want["counts"], order
+        assert d.dropped.tolist() == want["dropped"], order
+        assert d.row_of.tolist() == want["row_of"], order
+        _close(d.gate_eff, want["gate_eff"], rtol=1e-15, atol=1e-15)
+
+
+def pin_priority_invariants(orc):
+    """Both visiting orders keep min(load, C) records per expert and fill each buffer
+    from position 0; without a capacity, the token-major rows of an expert follow token
+    order, and k = 1 makes the two orders identical."""
+    rng = np.random.default_rng(17)
+    N, E, k = 150, 5, 2
+    lg = rng.standard_normal((N, E))
+    lg[:, 1] += 1.0
+    r = orc.route(lg, k, "topk_softmax")
+    for C in (1, 9, 33, 200):
+        for tm in (False, True):
+            d = orc.dispatch(r.idx, r.gate, E, C, True, token_major=tm)
+            assert np.array_equal(d.counts, np.minimum(d.load, C))
+            for e in range(E):
+                rows = np.sort(d.row_of[(r.idx == e) & (d.dropped == 0)])
+                assert np.array_equal(rows, e * C + np.arange(d.counts[e]))
+    d = orc.dispatch(r.idx, r.gate, E, None, False, token_major=True)
+    for e in range(E):
+        t, j = np.nonzero(r.idx == e)
+        assert np.all(np.diff(d.row_of[t, j]) > 0)  # np.nonzero lists tokens ascending
+    r1 = orc.route(lg, 1, "softmax_topk")
+    for C in (3, 40):
+        a = orc.dispatch(r1.idx, r1.gate, E, C, True, token_major=True)
+        b = orc.dispatch(r1.idx, r1.gate, E, C, True, token_major=False)
+        assert np.array_equal(a.row_of, b.row_of) and np.array_equal(a.dropped, b.dropped)
 
 
 # ---------------------------------------------------------------------------------------

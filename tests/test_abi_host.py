@@ -64,6 +64,20 @@ def test_capacity_examples_through_abi(L):
     assert B.moe_capacity(_desc(N=100)) == 100  # no capacity limit: C = N
 
 
+def test_switch_capacity_examples_through_abi(L):
+    g = oracle_pins.golden("switch_capacity_examples.json")
+    for c in g["cases"]:
+        d = _desc(N=c["N"], E=c["E"], k=c["k"], capacity_mode="padded", capacity_factor=c["cf"],
+                  min_capacity=c["min_capacity"], capacity_formula="tokens")
+        assert B.moe_capacity(d) == c["C"], c
+    for c in g["invalid"]:
+        d = _desc(N=c["N"], E=max(c["E"], 0), k=c["k"], capacity_mode="padded", capacity_factor=c["cf"],
+                  capacity_formula="tokens")
+        with pytest.raises(B.MoeError) as ei:
+            B.moe_capacity(d)
+        assert ei.value.status == B.MOE_E_INVAL
+
+
 def test_rows_and_sizes(L):
     d5 = B.make_desc(configs.get_config("gshard_capacity"))
     assert B.moe_capacity(d5) == 640
@@ -99,7 +113,8 @@ def test_invalid_desc_rejected(L, kw, status):
 
 def test_bad_enums_rejected(L):
     for field, val in (("dtype", 5), ("routing_mode", 2), ("second_choice", 3), ("activation", 9),
-                       ("capacity_mode", 4)):
+                       ("capacity_mode", 4), ("capacity_priority", 2), ("capacity_formula", -1),
+                       ("second_choice", -1)):
         d = _desc()
         setattr(d, field, val)
         assert L.moe_rows(ctypes.byref(d), ctypes.byref(ctypes.c_int64())) == B.MOE_E_INVAL, field

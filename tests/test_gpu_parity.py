@@ -24,8 +24,11 @@ def _dev(t):
     return None if t is None else t.to(DEV)
 
 
+NOISE = {False: "topk", "second": "noisy", "all": "noisy_all"}
+
+
 def _routing_cfg(N, E, k, mode="topk_softmax", noisy=False, dtype="bf16", D=128, F=128, **kw):
-    c = dict(N=N, D=D, F=F, E=E, k=k, dtype=dtype, routing_mode=mode, second_choice="noisy" if noisy else "topk",
+    c = dict(N=N, D=D, F=F, E=E, k=k, dtype=dtype, routing_mode=mode, second_choice=NOISE[noisy],
              activation="silu", capacity_mode="none", capacity_factor=0.0, min_capacity=0)
     c.update(kw)
     return c
@@ -45,9 +48,9 @@ ROUTE_CASES = [
 
 @pytest.mark.parametrize("N,E,k,dist", ROUTE_CASES)
 @pytest.mark.parametrize("mode", ["softmax_topk", "topk_softmax"])
-@pytest.mark.parametrize("noisy", [False, True])
+@pytest.mark.parametrize("noisy", [False, "second", "all"])
 def test_route_from_identical_logits(orc, N, E, k, dist, mode, noisy):
-    if noisy and k < 2:
+    if noisy == "second" and k < 2:
         pytest.skip("noisy second choice needs k >= 2")
     seed = 10 * N + E + k
     kw = {}
@@ -66,9 +69,11 @@ def test_route_from_identical_logits(orc, N, E, k, dist, mode, noisy):
     lout = torch.empty((N, E), dtype=torch.float32, device=DEV)
     B.moe_route(d, None, None, None, _dev(noise), _dev(logits), lout, probs, idx, gate)
     torch.cuda.synchronize()
-    r = orc.route(logits, k, mode, noise=noise)
+    r = orc.route(logits, k, mode, noise=noise, noise_all=noisy == "all")
     assert np.array_equal(host(idx), r.idx), "selection differs from the oracle on identical logits"
-    assert np.array_equal(host(lout), logits.numpy())
+    # logits_out: the logits the routing used (logit + noise, one fp32 rounding, under noisy_all)
+    want = logits.numpy() + noise.numpy() if noisy == "all" else logits.numpy()
+    assert np.array_equal(host(lout), want)
     np.testing.assert_allclose(host(gate), r.gate, rtol=2e-6, atol=1e-7)
     np.testing.assert_allclose(host(probs), r.probs, rtol=2e-6, atol=1e-7)
 
@@ -109,6 +114,7 @@ DISPATCH_CASES = [
     (1000, 64, 2, 1.2, "padded", 1.25, 4), (4096, 8, 2, 0.5, "padded", 1.0, 0),
     (700, 16, 4, 2.0, "padded", 0.5, 1), (513, 4, 4, 0.0, "padded", 0.3, 0), (300, 64, 8, 1.0, "none", 0.0, 0),
     (999, 8, 1, 3.0, "padded", 2.0, 0), (128, 2, 2, 0.0, "padded", 0.01, 1), (50, 64, 2, 0.0, "padded", 10.0, 0),
+    (2000, 16, 2, 1.0, "padded", 1.0, 0), (1025, 8, 4, 1.5, "padded", 0.7, 2),
 ]
 
 
@@ -130,15 +136,20 @@ def _run_dispatch(d, x, idx, gate):
 
 
 @pytest.mark.parametrize("N,E,k,skew,cap,cf,minc", DISPATCH_CASES)
-def test_dispatch_from_identical_records(orc, N, E, k, skew, cap, cf, minc):
-    cfg = _routing_cfg(N, E, k, capacity_mode=cap, capacity_factor=cf, min_capacity=minc, D=128)
+@pytest.mark.parametrize("prio,formula", [("slot_major", "tokens_k"), ("token_major", "tokens_k"),
+                                          ("token_major", "tokens")])
+def test_dispatch_from_identical_records(orc, N, E, k, skew, cap, cf, minc, prio, formula):
+    cfg = _routing_cfg(N, E, k, capacity_mode=cap, capacity_factor=cf, min_capacity=minc, D=128,
+                       capacity_priority=prio, capacity_formula=formula)
     d = B.make_desc(cfg)
     idx, gate = inputs.make_topk(N, E, k, seed=N * 7 + E, skew=skew)
     x = inputs.make_rows(N, 128, seed=N, dtype="bf16")
     out, _ = _run_dispatch(d, x.to(DEV), idx.to(DEV), gate.to(DEV))
     padded = cap == "padded"
-    C = orc.capacity(N, E, k, cf, minc) if padded else None
-    o = orc.dispatch(idx, gate.double(), E, C, padded)
+    C = orc.capacity(N, E, k, cf, minc, formula) if padded else None
+    if padded:
+        assert B.moe_capacity(d) == C
+    o = orc.dispatch(idx, gate.double(), E, C, padded, token_major=prio == "token_major")
     assert np.array_equal(host(out["load"]), o.load)
     assert np.array_equal(host(out["counts"]), o.counts)
     assert np.array_equal(host(out["offsets"]), o.offsets)
@@ -263,6 +274,20 @@ def _workload(cfg):
     return _CACHE[key]
 
 
+def _oracle_routing(orc, cfg, inp):
+    """The oracle's routing and dispatch of a workload (all N tokens)."""
+    N, E, k = cfg["N"], cfg["E"], cfg["k"]
+    padded = cfg["capacity_mode"] == "padded"
+    sc = cfg["second_choice"]
+    logits = orc.router_logits(inp["x"], inp["w_r"], inp["logit_bias"])
+    r = orc.route(logits, k, cfg["routing_mode"], noise=inp["noise"] if sc != "topk" else None,
+                  noise_all=sc == "noisy_all")
+    C = (orc.capacity(N, E, k, cfg["capacity_factor"], cfg["min_capacity"], cfg.get("capacity_formula", "tokens_k"))
+         if padded else None)
+    o = orc.dispatch(r.idx, r.gate, E, C, padded, token_major=cfg.get("capacity_priority") == "token_major")
+    return r, o
+
+
 def _check_layer(orc, cfg, sample=None, max_amb=16):
     """Runs moe_forward and checks routing, dispatch and outputs against the oracle."""
     inp = _workload(cfg)
@@ -273,10 +298,7 @@ def _check_layer(orc, cfg, sample=None, max_amb=16):
     N, E, k = cfg["N"], cfg["E"], cfg["k"]
     padded = cfg["capacity_mode"] == "padded"
 
-    logits = orc.router_logits(inp["x"], inp["w_r"], inp["logit_bias"])
-    r = orc.route(logits, k, cfg["routing_mode"], noise=inp["noise"] if cfg["second_choice"] == "noisy" else None)
-    C = orc.capacity(N, E, k, cfg["capacity_factor"], cfg["min_capacity"]) if padded else None
-    o = orc.dispatch(r.idx, r.gate, E, C, padded)
+    r, o = _oracle_routing(orc, cfg, inp)
 
     g_idx = host(v["topk_idx"])
     amb = ambiguous_tokens(r)
@@ -327,6 +349,12 @@ MID = [
     configs.scaled_config("mixtral_prefill", N=257, D=128, F=256, E=1, k=1),
     configs.scaled_config("mixtral_prefill", N=200, D=128, F=128, E=8, k=8, routing_mode="softmax_topk",
                           activation="gelu_tanh"),
+    configs.scaled_config("switch_top1", N=1000, D=256, F=384),
+    configs.scaled_config("switch_top1", N=600, D=128, F=256, E=64, capacity_factor=0.5),
+    configs.scaled_config("gshard_capacity", N=900, D=128, F=256, E=16, capacity_priority="token_major",
+                          capacity_formula="tokens", capacity_factor=1.5, name="gshard_token_major"),
+    configs.scaled_config("mixtral_prefill", N=300, D=128, F=256, k=2, second_choice="noisy_all", noise_std=0.5,
+                          name="mixtral_noisy_all"),
 ]
 
 
@@ -361,7 +389,8 @@ def test_layer_bitwise_reproducible_and_equal_to_steps(orc):
 
 
 @pytest.mark.parametrize("cfg", [configs.scaled_config("gshard_capacity", N=1000, D=256, F=384, E=16),
-                                 configs.scaled_config("mixtral_prefill", N=333, D=256, F=512)],
+                                 configs.scaled_config("mixtral_prefill", N=333, D=256, F=512),
+                                 configs.scaled_config("switch_top1", N=1000, D=256, F=384)],
                          ids=lambda c: c["name"])
 def test_stats(orc, cfg):
     res = _check_layer(orc, cfg)
@@ -430,6 +459,20 @@ def test_workload_gshard_capacity(orc):
     assert st["capacity"] == 640
     if len(res["amb"]) == 0:
         assert st["dropped_slots"] == int(o.dropped.sum())
+
+
+@pytest.mark.slow
+def test_workload_switch_top1(orc):
+    cfg = configs.get_config("switch_top1")
+    inp = _workload(cfg)
+    r, o = _oracle_routing(orc, cfg, inp)
+    C = orc.capacity(cfg["N"], cfg["E"], cfg["k"], cfg["capacity_factor"], cfg["min_capacity"], "tokens")
+    assert C == 512 and (o.load > C).sum() >= 1, "the workload must overflow an expert"
+    gone = np.nonzero(o.dropped[:, 0] == 1)[0]
+    kept = np.nonzero(o.dropped[:, 0] == 0)[0]
+    extra = gone[:: max(1, len(gone) // 8)][:8].tolist() + kept[:: max(1, len(kept) // 8)][:8].tolist()
+    res = _check_layer(orc, cfg, sample=_spread(cfg["N"], 16, extra=extra))
+    assert res["layer"].stats()["capacity"] == C
 
 
 @pytest.mark.slow

@@ -15,13 +15,16 @@ MUTANTS = {
     "softmax_sign": ("probs[t * E + e] = exp((double)l32[e] - m) / z;", "probs[t * E + e] = exp(m - (double)l32[e]) / z;"),
     "tie_to_higher_index": ("if (!chosen[e] && (best < 0 || val[e] > val[best])) best = e;",
                             "if (!chosen[e] && (best < 0 || val[e] >= val[best])) best = e;"),
-    "token_major_capacity": ("  for (int32_t j = 0; j < k; ++j)\n    for (int64_t t = 0; t < N; ++t) {\n      int32_t e = idx[t * k + j];\n      if (C < 0",
-                             "  for (int64_t t = 0; t < N; ++t)\n    for (int32_t j = 0; j < k; ++j) {\n      int32_t e = idx[t * k + j];\n      if (C < 0"),
+    "priority_always_token_major": ("const int64_t t = token_major ? v / k : v % N;\n    const int32_t j = token_major ? (int32_t)(v % k) : (int32_t)(v / N);",
+                                    "const int64_t t = v / k;\n    const int32_t j = (int32_t)(v % k);"),
+    "priority_always_slot_major": ("const int64_t t = token_major ? v / k : v % N;\n    const int32_t j = token_major ? (int32_t)(v % k) : (int32_t)(v / N);",
+                                   "const int64_t t = v % N;\n    const int32_t j = (int32_t)(v / N);"),
     "no_drop_renormalisation": ("else gate_eff[t * k + j] = g * all / kept;", "else gate_eff[t * k + j] = g;"),
-    "capacity_without_k": ("double c = ceil(((cf * (double)N) * (double)k) / (double)E);",
-                           "double c = ceil((cf * (double)N) / (double)E);"),
-    "capacity_floor": ("double c = ceil(((cf * (double)N) * (double)k) / (double)E);",
-                       "double c = floor(((cf * (double)N) * (double)k) / (double)E);"),
+    "capacity_without_k": ("ceil(((cf * (double)N) * (double)k) / (double)E)", "ceil((cf * (double)N) / (double)E)"),
+    "capacity_floor": ("ceil(((cf * (double)N) * (double)k) / (double)E)", "floor(((cf * (double)N) * (double)k) / (double)E)"),
+    "switch_capacity_with_k": ("ceil(((double)N / (double)E) * cf)", "ceil(((double)N / (double)E) * cf * (double)k)"),
+    "switch_capacity_floor": ("ceil(((double)N / (double)E) * cf)", "floor(((double)N / (double)E) * cf)"),
+    "noise_all_ignored": ("if (noisy == NOISE_ALL)\n      for (int32_t e = 0; e < E; ++e) l32[e] = l32[e] + noise[t * E + e];", ";"),
     "w3_transposed": ("out[d] += u * elem(w3, w_dtype, base_dn + f * D + d);",
                       "out[d] += u * elem(w3, w_dtype, base_dn + d * F + f);"),
     "silu_sign": ("if (kind == ACT_SILU) return z / (1.0 + exp(-z));", "if (kind == ACT_SILU) return z / (1.0 + exp(z));"),
@@ -33,7 +36,8 @@ MUTANTS = {
                            "y[t * D + d] += gate_eff[t * k] * y_perm[r * D + d];"),
     "rows_wrong_expert": ("xrows + i * D, w1, w2, w3, experts[i], out + i * D)",
                           "xrows + i * D, w1, w2, w3, experts[0], out + i * D)"),
-    "noise_on_slot0": ("val[e] = (j > 0 && noisy) ?", "val[e] = (noisy) ?"),
+    "noise_on_slot0": ("val[e] = (j > 0 && noisy == NOISE_SECOND) ?", "val[e] = (noisy == NOISE_SECOND) ?"),
+    "noise_second_on_all": ("val[e] = (j > 0 && noisy == NOISE_SECOND) ?", "val[e] = (j > 0 && noisy) ?"),
     "balance_f_div_n": ("b += ((double)load[e] / ((double)N * (double)k)) * P[e];", "b += ((double)load[e] / (double)N) * P[e];"),
     "mode_b_uses_probs": ("for (int32_t j = 0; j < k; ++j) gate[t * k + j] = exp((double)l32[idx[t * k + j]] - ref) / s;",
                           "for (int32_t j = 0; j < k; ++j) gate[t * k + j] = probs[t * E + idx[t * k + j]];"),
