@@ -15,8 +15,10 @@
 // token-major order):
 //   count  : each 256-token workgroup builds, per segment, its expert histogram with one
 //            wave ballot per expert (rank = popcount of lower lanes with equal expert);
-//   scan   : one wave scans the block histograms in (segment, block) order per expert,
-//            giving each block's base position, the loads, counts and offsets;
+//   scan   : one workgroup of 16 waves; each wave scans the block histograms of its
+//            experts in (segment, block) order (stored expert-major, so 64 consecutive
+//            entries per load and a wave prefix sum per 64), giving each block's base
+//            position, the loads and counts; then one wave scans the counts into offsets;
 //   assign : the same ballots give each record's rank inside its block; position =
 //            base + rank. Rows, drop mask and gates after the drop rule are written.
 // The gather then copies token rows into the expert buffers with 16-byte vector moves.
@@ -91,7 +93,7 @@ __global__ __launch_bounds__(256) void k_dispatch_count(const DispatchArgs a) {
     wave_match_tokens(e, a.k, a.E, cnt_s, rank);
     __syncthreads();
     if (tid < a.E)
-      a.blockcnt[(int64_t)blockIdx.x * a.E + tid] = cnt_s[0][tid] + cnt_s[1][tid] + cnt_s[2][tid] + cnt_s[3][tid];
+      a.blockcnt[(int64_t)tid * a.nblk + blockIdx.x] = cnt_s[0][tid] + cnt_s[1][tid] + cnt_s[2][tid] + cnt_s[3][tid];
     return;
   }
   for (int j = 0; j < a.k; ++j) {
@@ -101,39 +103,104 @@ __global__ __launch_bounds__(256) void k_dispatch_count(const DispatchArgs a) {
     wave_match(e, a.E, cnt_s, rank);
     __syncthreads();
     if (tid < a.E)
-      a.blockcnt[((int64_t)j * a.nblk + blockIdx.x) * a.E + tid] =
+      a.blockcnt[((int64_t)tid * a.k + j) * a.nblk + blockIdx.x] =
           cnt_s[0][tid] + cnt_s[1][tid] + cnt_s[2][tid] + cnt_s[3][tid];
     __syncthreads();
   }
 }
 
-__global__ __launch_bounds__(64) void k_dispatch_scan(const DispatchArgs a) {
+// Inclusive prefix sum over the 64 lanes of a wave.
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  const int lane = lane_id();
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int u = __shfl_up(v, off);
+    if (lane >= off) v += u;
+  }
+  return v;
+}
+
+constexpr int kScanWaves = 16;
+
+__global__ __launch_bounds__(64 * kScanWaves) void k_dispatch_scan(const DispatchArgs a) {
   __shared__ int cnt_s[kMaxE];
-  const int e = threadIdx.x;
-  if (e < a.E) {
-    int run = 0;
-    const int nseg = a.token_major ? 1 : a.k;
-    for (int j = 0; j < nseg; ++j) {
-      for (int b = 0; b < a.nblk; ++b) {
-        const int64_t i = ((int64_t)j * a.nblk + b) * a.E + e;
-        a.base[i] = run;
-        run += a.blockcnt[i];
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+  const int nseg = a.token_major ? 1 : a.k;
+  const int64_t len = (int64_t)nseg * a.nblk;  // (segment, block) entries per expert
+  // Short sequences (<= 512 entries): lane l holds entries 8 l .. 8 l + 7 of each of this
+  // wave's experts (all loads issued together); a running sum inside the lane and one
+  // wave scan of the lane totals per expert give the exclusive prefixes.
+  constexpr int kPer = kMaxE / kScanWaves;
+  if (len <= 8 * 64) {
+    int v[kPer][8];
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int e = w + kScanWaves * i;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int64_t q = 8 * lane + u;
+        v[i][u] = (e < a.E && q < len) ? a.blockcnt[(int64_t)e * len + q] : 0;
       }
     }
-    a.load[e] = run;
-    a.load_copy[e] = run;
-    const int c = (a.C < 0 || run < a.C) ? run : (int)a.C;
-    a.counts[e] = c;
-    cnt_s[e] = c;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int e = w + kScanWaves * i;
+      if (e >= a.E) break;
+      int tot = 0;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) tot += v[i][u];
+      const int incl = wave_incl_scan(tot);
+      int run_l = incl - tot;  // entries of lower lanes
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int64_t q = 8 * lane + u;
+        if (q < len) a.base[(int64_t)e * len + q] = run_l;
+        run_l += v[i][u];
+      }
+      const int run = __shfl(incl, 63);
+      if (lane == 0) {
+        a.load[e] = run;
+        a.load_copy[e] = run;
+        const int c = (a.C < 0 || run < a.C) ? run : (int)a.C;
+        a.counts[e] = c;
+        cnt_s[e] = c;
+      }
+    }
+  } else
+  for (int e = w; e < a.E; e += kScanWaves) {
+    const int32_t* cnt = a.blockcnt + (int64_t)e * len;
+    int32_t* base = a.base + (int64_t)e * len;
+    int run = 0;
+    for (int64_t c0 = 0; c0 < len; c0 += 8 * 64) {
+      int v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int64_t q = c0 + 64 * u + lane;
+        v[u] = q < len ? cnt[q] : 0;
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int incl = wave_incl_scan(v[u]);
+        const int64_t q = c0 + 64 * u + lane;
+        if (q < len) base[q] = run + incl - v[u];
+        run += __shfl(incl, 63);
+      }
+    }
+    if (lane == 0) {
+      a.load[e] = run;
+      a.load_copy[e] = run;
+      const int c = (a.C < 0 || run < a.C) ? run : (int)a.C;
+      a.counts[e] = c;
+      cnt_s[e] = c;
+    }
   }
   __syncthreads();
-  if (e == 0) {
-    int off = 0;
-    for (int x = 0; x < a.E; ++x) {
-      a.offsets[x] = a.padded ? (int)((int64_t)x * a.C) : off;
-      off += cnt_s[x];
-    }
-    a.offsets[a.E] = a.padded ? (int)((int64_t)a.E * a.C) : off;
+  if (w == 0) {
+    const int c = lane < a.E ? cnt_s[lane] : 0;
+    const int incl = wave_incl_scan(c);
+    if (lane < a.E) a.offsets[lane] = a.padded ? (int)((int64_t)lane * a.C) : incl - c;
+    if (lane == 63) a.offsets[a.E] = a.padded ? (int)((int64_t)a.E * a.C) : incl;
   }
 }
 
@@ -155,7 +222,7 @@ __global__ __launch_bounds__(256) void k_dispatch_assign(const DispatchArgs a) {
   auto place = [&](int j, int e, int seg, int rank) {
     int prefix = 0;
     for (int ww = 0; ww < w; ++ww) prefix += cnt_s[ww][e];
-    const int64_t pos = (int64_t)a.base[((int64_t)seg * a.nblk + blockIdx.x) * a.E + e] + prefix + rank;
+    const int64_t pos = (int64_t)a.base[((int64_t)e * (a.token_major ? 1 : a.k) + seg) * a.nblk + blockIdx.x] + prefix + rank;
     const bool k_ok = (a.C < 0) || (pos < a.C);
     int r = -1;
     if (k_ok) {
@@ -292,7 +359,7 @@ __global__ __launch_bounds__(64) void k_stats(const StatsArgs a) {
 
 hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(k_dispatch_count, dim3(a.nblk), dim3(256), 0, s, a);
-  hipLaunchKernelGGL(k_dispatch_scan, dim3(1), dim3(64), 0, s, a);
+  hipLaunchKernelGGL(k_dispatch_scan, dim3(1), dim3(64 * kScanWaves), 0, s, a);
   hipLaunchKernelGGL(k_dispatch_assign, dim3(a.nblk), dim3(256), 0, s, a);
   return hipGetLastError();
 }

@@ -62,7 +62,7 @@ size_t esize(const moe_desc* d) { return d->dtype == MOE_DT_BF16 ? 2 : 4; }
 
 moe_ws_layout layout_of(const moe_desc* d, int64_t rows) {
   moe_ws_layout L;
-  const ScratchLayout s = scratch_layout(d->N, d->E, d->k, d->dtype == MOE_DT_BF16);
+  const ScratchLayout s = scratch_layout(d->N, d->D, d->E, d->k, d->dtype == MOE_DT_BF16);
   const size_t nk = (size_t)d->N * d->k;
   size_t o = 0;
   L.scratch = o; o = align_up(o + s.total, 256);
@@ -96,9 +96,10 @@ int do_route(const moe_desc* d, const void* x, const float* w_r, const float* bi
   a.logits_in = logits_in; a.logits_out = logits_out; a.probs_out = probs_out;
   a.topk_idx = idx; a.topk_gate = gate;
   if (scratch) {
-    const ScratchLayout s = scratch_layout(d->N, d->E, d->k, d->dtype == MOE_DT_BF16);
+    const ScratchLayout s = scratch_layout(d->N, d->D, d->E, d->k, d->dtype == MOE_DT_BF16);
     a.psum = at<float>(scratch, s.psum);
     a.psum_magic = at<uint32_t>(scratch, s.header + 64);
+    if (d->dtype == MOE_DT_BF16) a.rpart = at<float>(scratch, s.rpart);
   }
   a.N = d->N; a.D = (int)d->D; a.E = d->E; a.k = d->k;
   a.mode = d->routing_mode; a.noisy = d->second_choice;
@@ -113,7 +114,7 @@ int do_dispatch(const moe_desc* d, const void* x, const int32_t* idx, const floa
   if (rc) return rc;
   rc = rows_of(d, &rows);
   if (rc) return rc;
-  const ScratchLayout s = scratch_layout(d->N, d->E, d->k, d->dtype == MOE_DT_BF16);
+  const ScratchLayout s = scratch_layout(d->N, d->D, d->E, d->k, d->dtype == MOE_DT_BF16);
   DispatchArgs a{};
   a.topk_idx = idx; a.topk_gate = gate;
   a.blockcnt = at<int32_t>(scratch, s.blockcnt);
@@ -140,7 +141,7 @@ FfnArgs ffn_args(const moe_desc* d, int64_t C, int64_t rows, const void* x_perm,
                  const int32_t* counts, const void* w1, const void* w2, const void* w3, void* h, void* y_perm,
                  void* scratch) {
   FfnArgs a{};
-  if (d->dtype == MOE_DT_BF16) a.partial = at<float>(scratch, scratch_layout(d->N, d->E, d->k, true).partial);
+  if (d->dtype == MOE_DT_BF16) a.partial = at<float>(scratch, scratch_layout(d->N, d->D, d->E, d->k, true).partial);
   a.x_perm = x_perm; a.offsets = offsets; a.counts = counts; a.w1 = w1; a.w2 = w2; a.w3 = w3;
   a.h = h; a.y_perm = y_perm; a.rows = rows;
   a.max_rows_per_expert = d->capacity_mode == MOE_CAP_PADDED ? (C < d->N ? C : d->N) : d->N;
@@ -214,7 +215,7 @@ int moe_scratch_size(const moe_desc* d, size_t* bytes) {
   if (!bytes) return MOE_E_INVAL;
   int rc = check_desc(d);
   if (rc) return rc;
-  *bytes = scratch_layout(d->N, d->E, d->k, d->dtype == MOE_DT_BF16).total;
+  *bytes = scratch_layout(d->N, d->D, d->E, d->k, d->dtype == MOE_DT_BF16).total;
   return MOE_OK;
 }
 
@@ -249,7 +250,7 @@ int moe_route(const moe_desc* d, const void* x, const float* w_r, const float* l
   REQUIRE(topk_idx); REQUIRE(topk_gate);
   if (scratch) {
     OPTIONAL(scratch);
-    if (scratch_bytes < scratch_layout(d->N, d->E, d->k, d->dtype == MOE_DT_BF16).total) return MOE_E_WORKSPACE;
+    if (scratch_bytes < scratch_layout(d->N, d->D, d->E, d->k, d->dtype == MOE_DT_BF16).total) return MOE_E_WORKSPACE;
   }
   return do_route(d, x, w_r, logit_bias, noise, logits_in, logits_out, probs_out, topk_idx, topk_gate, scratch,
                   (hipStream_t)stream);
@@ -266,7 +267,7 @@ int moe_dispatch(const moe_desc* d, const void* x, const int32_t* topk_idx, cons
   REQUIRE(x); REQUIRE(topk_idx); REQUIRE(topk_gate); REQUIRE(load); REQUIRE(counts); REQUIRE(offsets);
   REQUIRE(row_of); REQUIRE(dropped); REQUIRE(gate_eff); REQUIRE(token_of_row); REQUIRE(x_perm);
   if (!scratch || !aligned16(scratch)) return MOE_E_WORKSPACE;
-  if (scratch_bytes < scratch_layout(d->N, d->E, d->k, d->dtype == MOE_DT_BF16).total) return MOE_E_WORKSPACE;
+  if (scratch_bytes < scratch_layout(d->N, d->D, d->E, d->k, d->dtype == MOE_DT_BF16).total) return MOE_E_WORKSPACE;
   return do_dispatch(d, x, topk_idx, topk_gate, load, counts, offsets, row_of, dropped, gate_eff, token_of_row,
                      x_perm, scratch, (hipStream_t)stream);
 }
@@ -279,7 +280,7 @@ int moe_expert_ffn(const moe_desc* d, const void* x_perm, const int32_t* offsets
   REQUIRE(x_perm); REQUIRE(offsets); REQUIRE(counts); REQUIRE(w1); REQUIRE(w2); REQUIRE(w3); REQUIRE(h);
   REQUIRE(y_perm);
   if (!scratch || !aligned16(scratch)) return MOE_E_WORKSPACE;
-  if (scratch_bytes < scratch_layout(d->N, d->E, d->k, d->dtype == MOE_DT_BF16).total) return MOE_E_WORKSPACE;
+  if (scratch_bytes < scratch_layout(d->N, d->D, d->E, d->k, d->dtype == MOE_DT_BF16).total) return MOE_E_WORKSPACE;
   return do_ffn(d, x_perm, offsets, counts, w1, w2, w3, h, y_perm, scratch, 3, (hipStream_t)stream);
 }
 
@@ -289,7 +290,7 @@ int moe_expert_up(const moe_desc* d, const void* x_perm, const int32_t* offsets,
   if (rc) return rc;
   REQUIRE(x_perm); REQUIRE(offsets); REQUIRE(counts); REQUIRE(w1); REQUIRE(w2); REQUIRE(h);
   if (!scratch || !aligned16(scratch)) return MOE_E_WORKSPACE;
-  if (scratch_bytes < scratch_layout(d->N, d->E, d->k, d->dtype == MOE_DT_BF16).total) return MOE_E_WORKSPACE;
+  if (scratch_bytes < scratch_layout(d->N, d->D, d->E, d->k, d->dtype == MOE_DT_BF16).total) return MOE_E_WORKSPACE;
   return do_ffn(d, x_perm, offsets, counts, w1, w2, nullptr, h, nullptr, scratch, 1, (hipStream_t)stream);
 }
 
@@ -299,7 +300,7 @@ int moe_expert_down(const moe_desc* d, const void* h, const int32_t* offsets, co
   if (rc) return rc;
   REQUIRE(h); REQUIRE(offsets); REQUIRE(counts); REQUIRE(w3); REQUIRE(y_perm);
   if (!scratch || !aligned16(scratch)) return MOE_E_WORKSPACE;
-  if (scratch_bytes < scratch_layout(d->N, d->E, d->k, d->dtype == MOE_DT_BF16).total) return MOE_E_WORKSPACE;
+  if (scratch_bytes < scratch_layout(d->N, d->D, d->E, d->k, d->dtype == MOE_DT_BF16).total) return MOE_E_WORKSPACE;
   return do_ffn(d, nullptr, offsets, counts, nullptr, nullptr, w3, const_cast<void*>(h), y_perm, scratch, 2,
                 (hipStream_t)stream);
 }
@@ -345,7 +346,7 @@ int moe_read_stats(const moe_desc* d, const void* scratch, size_t scratch_bytes,
   int rc = check_desc(d);
   if (rc) return rc;
   if (!out) return MOE_E_INVAL;
-  const ScratchLayout s = scratch_layout(d->N, d->E, d->k, d->dtype == MOE_DT_BF16);
+  const ScratchLayout s = scratch_layout(d->N, d->D, d->E, d->k, d->dtype == MOE_DT_BF16);
   if (!scratch || !aligned16(scratch) || scratch_bytes < s.total) return MOE_E_WORKSPACE;
   int64_t C;
   rc = capacity_of(d, &C);

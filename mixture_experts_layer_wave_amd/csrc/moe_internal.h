@@ -8,7 +8,9 @@
 
 namespace moe {
 
-constexpr int kRouterTokens = 32;     // tokens per router workgroup
+constexpr int kRouterTokens = 32;     // tokens per router partial-sum block (psum)
+constexpr int kRouterTile = 256;      // tokens per split-K router workgroup (8 waves x 32)
+constexpr int kRouterChunk = 64;      // K per pipeline step of the split-K router
 constexpr int kDispatchTokens = 256;  // tokens per dispatch workgroup
 constexpr int kMaxE = 64;
 constexpr int kMaxK = 8;
@@ -20,21 +22,40 @@ constexpr size_t kGemmPartialBytes = kGemmPartialUnits * 8 * 128 * 64 * sizeof(f
 
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
+// Split-K router plan for bf16 x: `tiles` token tiles of kRouterTile tokens times S
+// splits of D (Ks = D / S, a multiple of kRouterChunk), about 256 workgroups in all.
+struct RouterSplit {
+  int tiles, S, Ks;
+};
+inline RouterSplit router_split(int64_t N, int64_t D) {
+  RouterSplit r;
+  r.tiles = (int)((N + kRouterTile - 1) / kRouterTile);
+  const int chunks = (int)(D / kRouterChunk);
+  int S = r.tiles >= 256 ? 1 : 256 / r.tiles;
+  if (S > 32) S = 32;
+  if (S > chunks) S = chunks;
+  if (S < 1) S = 1;
+  while (chunks % S != 0) --S;
+  r.S = S;
+  r.Ks = (int)(D / S);
+  return r;
+}
 // Scratch (moe_scratch_size bytes) carved into regions, each 256-byte aligned:
 //   header    : moe_stats (64 B) + magic word
 //   psum      : fp32 [nblk_r][E]   per-router-block sums of the probabilities
-//   blockcnt  : int32 [k][nblk_d][E] per-dispatch-block expert histogram of each slot
-//               (token-major order: one segment [1][nblk_d][E] over all slots)
-//   base      : int32 [k][nblk_d][E] exclusive scan of blockcnt in record order
+//   blockcnt  : int32 [E][k][nblk_d] per-dispatch-block expert histogram of each slot
+//               (token-major order: one segment [E][1][nblk_d] over all slots)
+//   base      : int32 [E][k][nblk_d] exclusive scan of blockcnt in record order
 //   tokdrop   : int32 [nblk_d]     tokens with every slot dropped, per block
 //   load      : int32 [E]          copy of the pre-capacity histogram
 //   partial   : fp32 split-K partial tiles of the bf16 grouped GEMM (bf16 layers only)
+//   rpart     : fp32 [S][N][E] split-K partial router logits (bf16 layers only)
 struct ScratchLayout {
-  size_t header, psum, blockcnt, base, tokdrop, load, partial, total;
+  size_t header, psum, blockcnt, base, tokdrop, load, partial, rpart, total;
   int nblk_r, nblk_d;
 };
 
-inline ScratchLayout scratch_layout(int64_t N, int E, int k, bool bf16) {
+inline ScratchLayout scratch_layout(int64_t N, int64_t D, int E, int k, bool bf16) {
   ScratchLayout s;
   s.nblk_r = (int)((N + kRouterTokens - 1) / kRouterTokens);
   s.nblk_d = (int)((N + kDispatchTokens - 1) / kDispatchTokens);
@@ -46,6 +67,7 @@ inline ScratchLayout scratch_layout(int64_t N, int E, int k, bool bf16) {
   s.tokdrop = o; o = align_up(o + sizeof(int32_t) * (size_t)s.nblk_d, 256);
   s.load = o; o = align_up(o + sizeof(int32_t) * (size_t)E, 256);
   s.partial = o; o = align_up(o + (bf16 ? kGemmPartialBytes : 0), 256);
+  s.rpart = o; o = align_up(o + (bf16 ? sizeof(float) * (size_t)router_split(N, D).S * N * E : 0), 256);
   s.total = o;
   return s;
 }
@@ -63,6 +85,7 @@ struct RouterArgs {
   float* topk_gate;       // [N,k]
   float* psum;            // [nblk_r][E] or null
   uint32_t* psum_magic;   // or null
+  float* rpart;           // [S][N][E] split-K partial logits (null: single-pass router)
   int64_t N;
   int D, E, k, mode;
   int noisy;  // MOE_SECOND_*: 1 = noise on slots >= 1, 2 = noise replaces the logits

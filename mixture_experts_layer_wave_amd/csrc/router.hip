@@ -1,31 +1,37 @@
-// router.hip: fused router for gfx950. fp32 logits x W_r (+ bias), stable softmax over
-// the E experts, register top-k, gates, and per-block partial sums of the probabilities.
+// router.hip: router of the MoE layer for gfx950. fp32 logits x W_r (+ bias), stable
+// softmax over the E experts, register top-k, gates, and per-block partial sums of the
+// probabilities.
 //
-// Method ("第 5 章 model.py 精读·中：MoE 路由与专家", §5.2, §5.2.1, §5.2.3; "MoE 公式到源码对照"
-// §1.1-1.2; "8.1 MoE 系列" §3 for the GShard noisy second choice):
+// Method ("第 5 章 model.py 精读·中：MoE 路由与专家", §5.2, §5.2.1, §5.2.2, §5.2.3; "MoE 公式到源码
+// 对照" §1.1-1.2; "8.1 MoE 系列" §3 for the GShard noisy second choice):
 //   logits = fp32(x) W_r in fp32; p = softmax(logits) with the maximum subtracted;
 //   slots = k largest logits (lower index wins ties), slot 0 the largest; in GShard mode
 //   slots >= 1 use fl32(logit + noise) over the experts not chosen yet; in noisy top-k
-//   gating ("第 5 章 ..." §5.2.2) logit' = fl32(logit + noise) replaces the logits;
+//   gating logit' = fl32(logit + noise) replaces the logits for every later step;
 //   gates = p of the chosen experts (softmax-then-top-k) or softmax over the chosen
 //   logits (top-k-then-softmax, the renormalised form).
 //
-// Design: a workgroup owns 32 tokens and its 8 waves split D into 8 equal ranges. Each
-// wave accumulates the 32 x (32 or 64) logit block of its range with v_mfma_f32_32x32x2_f32
-// (fp32 products, fp32 accumulation): lane l feeds x[token l % 32][k] and
-// W_r[k][expert l % 32] for the k of its half (l / 32), so W_r rows are read coalesced and
-// x rows with 16-byte loads. The 8 partial blocks meet in LDS and are added in a fixed
-// order (wave 0 .. 7), so logits are bit-reproducible. Softmax, selection and gates then
-// run in registers on one lane per token: no cross-lane traffic and no atomics.
+// Two logit paths, one token epilogue (route_token):
+//  * Split-K path (bf16 x, scratch given): workgroups of 8 waves x 32 tokens take one
+//    token tile and one of S equal ranges of D; S is chosen so that about 256 workgroups
+//    run whatever N is (decode included). Products x * W_r are formed on the bf16 matrix
+//    cores without losing fp32 accuracy: each fp32 W_r value is split exactly into three
+//    bf16 pieces (hi + mid + lo, 8 mantissa bits each) when its 64-row chunk is staged in
+//    LDS, x is bf16 already, so every product is exact and v_mfma_f32_32x32x16_bf16
+//    accumulates in fp32. Partial logits [S][N][E] go to scratch; k_router_epi adds them
+//    in split order (fixed, so logits are bit-reproducible) and finishes each token.
+//  * Single-pass path (fp32 x, routing given logits, or no scratch): a workgroup owns 32
+//    tokens, its 8 waves split D and accumulate with v_mfma_f32_32x32x2_f32; the 8
+//    partial blocks meet in LDS and are added in wave order before the epilogue.
 #include "moe_device.h"
 #include "moe_internal.h"
 
 namespace moe {
 namespace {
 
-constexpr int kTM = kRouterTokens;  // tokens per workgroup (32)
+constexpr int kTM = kRouterTokens;  // tokens per single-pass workgroup (32)
 constexpr int kWaves = 8;
-constexpr int kKC = 32;             // K chunk per pipeline step: 16 MFMAs of K = 2
+constexpr int kKC = 32;             // K chunk per pipeline step of the single-pass path
 
 template <int EP>
 __device__ __forceinline__ float pick(const float (&v)[EP], int i) {
@@ -34,6 +40,86 @@ __device__ __forceinline__ float pick(const float (&v)[EP], int i) {
   for (int e = 0; e < EP; ++e) r = (e == i) ? v[e] : r;
   return r;
 }
+
+// Epilogue of one token t < N from its logits l (bias included): noisy top-k gating,
+// softmax into p, optional logits/probs outputs, selection and gates.
+template <int EP>
+__device__ __forceinline__ void route_token(const RouterArgs& a, int64_t t, float (&l)[EP], float (&p)[EP]) {
+  const int E = a.E;
+  if (a.noisy == 2) {
+#pragma unroll
+    for (int e = 0; e < EP; ++e)
+      if (e < E) l[e] += a.noise[t * E + e];  // logit' = fl32(logit + noise)
+  }
+  float mx = l[0];
+#pragma unroll
+  for (int e = 1; e < EP; ++e) mx = (e < E) ? fmaxf(mx, l[e]) : mx;
+  float sum = 0.f;
+#pragma unroll
+  for (int e = 0; e < EP; ++e) {
+    p[e] = (e < E) ? expf(l[e] - mx) : 0.f;
+    sum += p[e];
+  }
+#pragma unroll
+  for (int e = 0; e < EP; ++e) p[e] = p[e] / sum;
+
+  if (a.logits_out) for (int e = 0; e < E; ++e) a.logits_out[t * E + e] = pick(l, e);
+  if (a.probs_out) for (int e = 0; e < E; ++e) a.probs_out[t * E + e] = pick(p, e);
+
+  // noisy values for slots >= 1 (GShard random routing)
+  float z[EP];
+#pragma unroll
+  for (int e = 0; e < EP; ++e) z[e] = l[e];
+  if (a.noisy == 1) {
+#pragma unroll
+    for (int e = 0; e < EP; ++e) z[e] = (e < E) ? l[e] + a.noise[t * E + e] : 0.f;
+  }
+
+  int sel[kMaxK];
+  uint64_t chosen = 0;
+#pragma unroll
+  for (int j = 0; j < kMaxK; ++j) {
+    sel[j] = 0;
+    if (j < a.k) {
+      const bool use_z = (j > 0) && a.noisy == 1;
+      int best = -1;
+      float bv = 0.f;
+#pragma unroll
+      for (int e = 0; e < EP; ++e) {
+        const float v = use_z ? z[e] : l[e];
+        const bool cand = (e < E) && !((chosen >> e) & 1ull);
+        if (cand && (best < 0 || v > bv)) { best = e; bv = v; }
+      }
+      sel[j] = best;
+      chosen |= 1ull << best;
+    }
+  }
+
+  float gt[kMaxK];
+  if (a.mode == 0) {
+#pragma unroll
+    for (int j = 0; j < kMaxK; ++j) gt[j] = (j < a.k) ? pick(p, sel[j]) : 0.f;
+  } else {
+    const float ref = pick(l, sel[0]);
+    float s2 = 0.f;
+#pragma unroll
+    for (int j = 0; j < kMaxK; ++j) {
+      gt[j] = (j < a.k) ? expf(pick(l, sel[j]) - ref) : 0.f;
+      s2 += gt[j];
+    }
+#pragma unroll
+    for (int j = 0; j < kMaxK; ++j) gt[j] = gt[j] / s2;
+  }
+#pragma unroll
+  for (int j = 0; j < kMaxK; ++j) {
+    if (j < a.k) {
+      a.topk_idx[t * a.k + j] = sel[j];
+      a.topk_gate[t * a.k + j] = gt[j];
+    }
+  }
+}
+
+// ---- single-pass path --------------------------------------------------------------
 
 // Raw chunk of kKC x elements (as 16-byte words) and the W_r values one lane needs.
 template <typename XT>
@@ -58,7 +144,7 @@ struct XChunk {
 // NT: 32-expert column tiles (E <= 32 * NT); EP: register array width of the epilogue.
 template <int NT, int EP, typename XT, bool FROM_LOGITS>
 __global__ __launch_bounds__(512) void k_router(const RouterArgs a) {
-  __shared__ float red_s[kWaves][NT][16][64];  // partial logit blocks, lane-contiguous
+  __shared__ float red_s[FROM_LOGITS ? 1 : kWaves][NT][16][64];  // partial logit blocks, lane-contiguous
   __shared__ float ps_s[EP][kTM];
 
   const int tid = threadIdx.x;
@@ -157,78 +243,9 @@ __global__ __launch_bounds__(512) void k_router(const RouterArgs a) {
           if (a.bias != nullptr) v += a.bias[e];
         }
       }
-      if (a.noisy == 2 && e < E && t < a.N) v += a.noise[t * E + e];  // noisy top-k gating: logit'
       l[e] = v;
     }
-    // stable softmax over the E experts
-    float mx = l[0];
-#pragma unroll
-    for (int e = 1; e < EP; ++e) mx = (e < E) ? fmaxf(mx, l[e]) : mx;
-    float sum = 0.f;
-#pragma unroll
-    for (int e = 0; e < EP; ++e) {
-      p[e] = (e < E) ? expf(l[e] - mx) : 0.f;
-      sum += p[e];
-    }
-#pragma unroll
-    for (int e = 0; e < EP; ++e) p[e] = p[e] / sum;
-
-    if (valid) {
-      if (a.logits_out) for (int e = 0; e < E; ++e) a.logits_out[t * E + e] = pick(l, e);
-      if (a.probs_out) for (int e = 0; e < E; ++e) a.probs_out[t * E + e] = pick(p, e);
-
-      // noisy values for slots >= 1 (GShard random routing)
-      float z[EP];
-#pragma unroll
-      for (int e = 0; e < EP; ++e) z[e] = l[e];
-      if (a.noisy == 1) {
-#pragma unroll
-        for (int e = 0; e < EP; ++e) z[e] = (e < E) ? l[e] + a.noise[t * E + e] : 0.f;
-      }
-
-      int sel[kMaxK];
-      uint64_t chosen = 0;
-#pragma unroll
-      for (int j = 0; j < kMaxK; ++j) {
-        sel[j] = 0;
-        if (j < a.k) {
-          const bool use_z = (j > 0) && a.noisy == 1;
-          int best = -1;
-          float bv = 0.f;
-#pragma unroll
-          for (int e = 0; e < EP; ++e) {
-            const float v = use_z ? z[e] : l[e];
-            const bool cand = (e < E) && !((chosen >> e) & 1ull);
-            if (cand && (best < 0 || v > bv)) { best = e; bv = v; }
-          }
-          sel[j] = best;
-          chosen |= 1ull << best;
-        }
-      }
-
-      float gt[kMaxK];
-      if (a.mode == 0) {
-#pragma unroll
-        for (int j = 0; j < kMaxK; ++j) gt[j] = (j < a.k) ? pick(p, sel[j]) : 0.f;
-      } else {
-        const float ref = pick(l, sel[0]);
-        float s2 = 0.f;
-#pragma unroll
-        for (int j = 0; j < kMaxK; ++j) {
-          gt[j] = (j < a.k) ? expf(pick(l, sel[j]) - ref) : 0.f;
-          s2 += gt[j];
-        }
-#pragma unroll
-        for (int j = 0; j < kMaxK; ++j) gt[j] = gt[j] / s2;
-      }
-#pragma unroll
-      for (int j = 0; j < kMaxK; ++j) {
-        if (j < a.k) {
-          a.topk_idx[t * a.k + j] = sel[j];
-          a.topk_gate[t * a.k + j] = gt[j];
-        }
-      }
-    }
+    if (valid) route_token(a, t, l, p);
     if (a.psum) {
 #pragma unroll
       for (int e = 0; e < EP; ++e) ps_s[e][lane] = valid ? p[e] : 0.f;
@@ -245,8 +262,209 @@ __global__ __launch_bounds__(512) void k_router(const RouterArgs a) {
   }
 }
 
+// ---- split-K path (bf16 x) -----------------------------------------------------------
+
+constexpr int kRow = kRouterChunk + 8;  // bf16 per LDS row of a W_r plane (16-byte pad)
+
+// Exact split of an fp32 value into three bf16 pieces: v = hi + mid + lo. Each piece
+// takes the next 8 significant bits; both subtractions are exact.
+__device__ __forceinline__ void split3(float v, uint16_t& hi, uint16_t& mid, uint16_t& lo) {
+  const uint32_t u = __float_as_uint(v);
+  const float r1 = v - __uint_as_float(u & 0xffff0000u);
+  const uint32_t u1 = __float_as_uint(r1);
+  const float r2 = r1 - __uint_as_float(u1 & 0xffff0000u);
+  hi = (uint16_t)(u >> 16);
+  mid = (uint16_t)(u1 >> 16);
+  lo = (uint16_t)(__float_as_uint(r2) >> 16);
+}
+
+// Workgroup (token tile, split): 8 waves x 32 tokens, K range [split Ks, (split+1) Ks).
+template <int NT>
+__global__ __launch_bounds__(512) void k_router_split(const RouterArgs a, RouterSplit rs) {
+  constexpr int EP = 32 * NT;
+  constexpr int KC = kRouterChunk;
+  constexpr int PER = KC * EP / 512;  // W_r values staged per thread and chunk
+  static_assert(PER * 512 == KC * EP, "staging split");
+  __shared__ __attribute__((aligned(16))) uint16_t w_s[2][3][EP][kRow];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = uniform(tid >> 6);
+  const int E = a.E;
+  const int tile = blockIdx.x / rs.S, split = blockIdx.x % rs.S;
+  const int64_t t0 = (int64_t)tile * kRouterTile + 32 * w;
+  const bool active = t0 < a.N;  // wave-uniform: waves past N only help staging
+  const int m = lane & 31, g = lane >> 5;
+  const int kbeg = split * rs.Ks;
+  const int nch = rs.Ks / KC;
+  // Lane (token m, group g) feeds k = 32 g + 8 s + 0..7 of MFMA step s of a chunk; the
+  // W_r operand of the same lane group covers the same k.
+  const int64_t trow = min(t0 + m, a.N - 1);
+  const u32x4* xrow = reinterpret_cast<const u32x4*>(reinterpret_cast<const bf16*>(a.x) + trow * a.D + kbeg + 32 * g);
+
+  // Global loads run two chunks ahead: the W_r rows and x words of chunk c + 2 are
+  // requested while chunk c is multiplied; chunk c + 1 goes to LDS after it.
+  auto fetch_w = [&](int c, float (&wst)[PER]) {  // W_r rows of chunk c into registers
+    const int k0 = kbeg + c * KC;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int q = tid + 512 * i;
+      const int kk = q / EP, e = q % EP;
+      wst[i] = e < E ? a.w_r[(int64_t)(k0 + kk) * E + e] : 0.f;
+    }
+  };
+  auto store_w = [&](int buf, const float (&wst)[PER]) {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int q = tid + 512 * i;
+      const int kk = q / EP, e = q % EP;
+      uint16_t h, md, lo;
+      split3(wst[i], h, md, lo);
+      w_s[buf][0][e][kk] = h;
+      w_s[buf][1][e][kk] = md;
+      w_s[buf][2][e][kk] = lo;
+    }
+  };
+  auto fetch_x = [&](int c, u32x4 (&xa)[4]) {
+    if (active) {
+#pragma unroll
+      for (int s = 0; s < 4; ++s) xa[s] = xrow[c * (KC / 8) + s];
+    }
+  };
+
+  f32x16 acc[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[nt][r] = 0.f;
+
+  float w0[PER], w1[PER], w2[PER];
+  u32x4 x0[4], x1[4], x2[4];
+  fetch_w(0, w0);
+  fetch_x(0, x0);
+  if (nch > 1) {
+    fetch_w(1, w1);
+    fetch_x(1, x1);
+  }
+  store_w(0, w0);
+  __syncthreads();
+  for (int c = 0; c < nch; ++c) {
+    const int buf = c & 1;
+    if (c + 2 < nch) {
+      fetch_w(c + 2, w2);
+      fetch_x(c + 2, x2);
+    }
+    if (active) {
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const bf16x8 xv = __builtin_bit_cast(bf16x8, x0[s]);
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+          for (int pc = 0; pc < 3; ++pc) {
+            const bf16x8 wv = *reinterpret_cast<const bf16x8*>(&w_s[buf][pc][nt * 32 + m][32 * g + 8 * s]);
+            acc[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xv, wv, acc[nt], 0, 0, 0);
+          }
+      }
+    }
+    if (c + 1 < nch) store_w(buf ^ 1, w1);  // that buffer's last readers passed the previous barrier
+    __syncthreads();
+#pragma unroll
+    for (int s = 0; s < 4; ++s) { x0[s] = x1[s]; x1[s] = x2[s]; }
+#pragma unroll
+    for (int i = 0; i < PER; ++i) w1[i] = w2[i];
+  }
+  if (!active) return;
+  // Accumulator element r of a lane holds token row 8 (r / 4) + 4 g + r % 4 and expert
+  // column m of its 32 x 32 block.
+  float* P = a.rpart + (int64_t)split * a.N * E;
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    const int e = nt * 32 + m;
+    if (e >= E) continue;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int64_t t = t0 + 8 * (r / 4) + 4 * g + (r % 4);
+      if (t < a.N) P[t * E + e] = acc[nt][r];
+    }
+  }
+}
+
+// 64 tokens per workgroup. Phase 1: the 256 threads sum the split partials of the
+// 64 x E logits, each in split order (the loads of all items of a thread and of up to
+// 64 / items splits are in flight at once; consecutive threads read consecutive partials). Phase 2: one thread per token adds the
+// bias and runs the token epilogue. Block sums of the probabilities per 32 tokens.
+template <int EP>
+__global__ __launch_bounds__(256) void k_router_epi(const RouterArgs a, RouterSplit rs) {
+  __shared__ float l_s[64][EP + 1];
+  __shared__ float ps_s[EP][64];
+  const int tid = threadIdx.x;
+  const int E = a.E;
+  const int64_t t0 = (int64_t)blockIdx.x * 64;
+  const int ntok = (int)min((int64_t)64, a.N - t0);
+  const int64_t stride = a.N * E;  // floats between consecutive splits
+  constexpr int IT = EP / 4;                  // items (token, expert) per thread: 64 EP / 256
+  constexpr int SB = IT >= 64 ? 1 : 64 / IT;  // splits whose loads are in flight together
+  const int nitem = ntok * E;
+  const float* P = a.rpart + t0 * E + tid;
+  float v[IT];
+#pragma unroll
+  for (int j = 0; j < IT; ++j) v[j] = 0.f;
+  for (int s0 = 0; s0 < rs.S; s0 += SB) {
+    float q[SB][IT];
+#pragma unroll
+    for (int u = 0; u < SB; ++u)
+#pragma unroll
+      for (int j = 0; j < IT; ++j)
+        q[u][j] = (s0 + u < rs.S && tid + 256 * j < nitem) ? P[(int64_t)(s0 + u) * stride + 256 * j] : 0.f;
+#pragma unroll
+    for (int u = 0; u < SB; ++u)
+#pragma unroll
+      for (int j = 0; j < IT; ++j)
+        if (s0 + u < rs.S) v[j] += q[u][j];
+  }
+#pragma unroll
+  for (int j = 0; j < IT; ++j) {
+    const int i = tid + 256 * j;
+    if (i < nitem) l_s[i / E][i % E] = v[j];
+  }
+  __syncthreads();
+  if (tid < 64) {  // wave 0: one token per lane
+    const int64_t t = t0 + tid;
+    const bool valid = tid < ntok;
+    float l[EP], p[EP];
+#pragma unroll
+    for (int e = 0; e < EP; ++e) {
+      l[e] = (valid && e < E) ? l_s[tid][e] + (a.bias != nullptr ? a.bias[e] : 0.f) : 0.f;
+      p[e] = 0.f;
+    }
+    if (valid) route_token(a, t, l, p);
+#pragma unroll
+    for (int e = 0; e < EP; ++e) ps_s[e][tid] = valid ? p[e] : 0.f;
+  }
+  if (a.psum == nullptr) return;  // uniform
+  __syncthreads();
+  if (tid < E) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int64_t blk = 2 * (int64_t)blockIdx.x + h;
+      if (blk * kTM >= a.N) break;
+      float s = 0.f;
+      for (int i = 0; i < kTM; ++i) s += ps_s[tid][h * kTM + i];
+      a.psum[blk * E + tid] = s;
+    }
+  }
+  if (blockIdx.x == 0 && tid == 0 && a.psum_magic) *a.psum_magic = kPsumMagic;
+}
+
 template <int NT, int EP>
 hipError_t launch_ep(const RouterArgs& a, bool bf16_x, hipStream_t s) {
+  if (bf16_x && a.logits_in == nullptr && a.rpart != nullptr && a.D % kRouterChunk == 0) {
+    const RouterSplit rs = router_split(a.N, a.D);
+    hipLaunchKernelGGL((k_router_split<NT>), dim3((unsigned)(rs.tiles * rs.S)), dim3(512), 0, s, a, rs);
+    hipLaunchKernelGGL((k_router_epi<EP>), dim3((unsigned)((a.N + 63) / 64)), dim3(256), 0, s, a, rs);
+    return hipGetLastError();
+  }
   const dim3 grid((unsigned)((a.N + kTM - 1) / kTM)), block(512);
   if (a.logits_in) {
     hipLaunchKernelGGL((k_router<NT, EP, float, true>), grid, block, 0, s, a);

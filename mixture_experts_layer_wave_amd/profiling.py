@@ -66,7 +66,7 @@ def parse_kernel(name: str):
 
 def stage_of(name: str) -> str:
     base, args = parse_kernel(name)
-    if base == "k_router":
+    if base in ("k_router", "k_router_split", "k_router_epi"):
         return "route"
     if base in ("k_dispatch_count", "k_dispatch_scan", "k_dispatch_assign", "k_gather"):
         return "dispatch"

@@ -84,17 +84,24 @@ def test_route_from_identical_logits(orc, N, E, k, dist, mode, noisy):
 
 @pytest.mark.parametrize("name,N,D", [("tiny_fp32", 64, 128), ("mixtral_prefill", 333, 4096),
                                       ("grok1_layer", 129, 6144), ("gshard_capacity", 1000, 2048),
-                                      ("mixtral_decode", 64, 4096)])
-def test_router_logits(orc, name, N, D):
-    cfg = configs.scaled_config(name, N=N, D=D, F=128)
+                                      ("mixtral_decode", 64, 4096), ("mixtral_decode", 1, 4096),
+                                      ("gshard_capacity", 4097, 128), ("switch_top1", 257, 2048),
+                                      ("mixtral_prefill", 70000, 256)])
+@pytest.mark.parametrize("scratch", [False, True], ids=["single_pass", "split_k"])
+def test_router_logits(orc, name, N, D, scratch):
+    """fp32 router logits against the exact ones: the single-pass fp32 MFMA path (no
+    scratch) and, for bf16 x, the split-K path with W_r split into three bf16 pieces."""
+    # clean logits (under noisy top-k gating logits_out would report logit + noise)
+    cfg = configs.scaled_config(name, N=N, D=D, F=128, second_choice="topk")
     inp = inputs.make_inputs(cfg, weights=False)
     d = B.make_desc(cfg)
     E, k = cfg["E"], cfg["k"]
     lout = torch.empty((N, E), dtype=torch.float32, device=DEV)
     idx = torch.empty((N, k), dtype=torch.int32, device=DEV)
     gate = torch.empty((N, k), dtype=torch.float32, device=DEV)
+    sc = torch.empty(B.moe_scratch_size(d), dtype=torch.uint8, device=DEV) if scratch else None
     B.moe_route(d, _dev(inp["x"]), _dev(inp["w_r"]), _dev(inp["logit_bias"]), _dev(inp["noise"]), None, lout, None,
-                idx, gate)
+                idx, gate, sc)
     torch.cuda.synchronize()
     exact = orc.router_logits(inp["x"], inp["w_r"], inp["logit_bias"])
     x64 = inp["x"].double().numpy()
