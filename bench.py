@@ -78,7 +78,7 @@ def cpu_baseline(cfg, inp, sample: int):
     t1 = time.perf_counter()
     toks = np.linspace(0, N - 1, min(sample, N)).astype(np.int64)
     orc.layer_tokens(toks, inp["x"], inp["w1"], inp["w2"], inp["w3"], r.idx, o.dropped, o.gate_eff,
-                     cfg["activation"])
+                     cfg["activation"], scales=(inp["s1"], inp["s2"], inp["s3"]) if "s1" in inp else None)
     t2 = time.perf_counter()
     n = len(toks)
     per_tok = (t1 - t0) / N + (t2 - t1) / n
@@ -131,10 +131,10 @@ def main():
                        v["dropped"], v["gate_eff"], v["token_of_row"], v["x_perm"], sc)
         if ev is not None:
             ev[2].record(stream)
-        B.moe_expert_up(d, v["x_perm"], v["offsets"], v["counts"], layer.w1, layer.w2, v["h"], sc)
+        layer.expert_up(v["x_perm"], v["offsets"], v["counts"], v["h"], sc)
         if ev is not None:
             ev[3].record(stream)
-        B.moe_expert_down(d, v["h"], v["offsets"], v["counts"], layer.w3, v["y_perm"], sc)
+        layer.expert_down(v["h"], v["offsets"], v["counts"], v["y_perm"], sc)
         if ev is not None:
             ev[4].record(stream)
         B.moe_combine(d, v["y_perm"], v["row_of"], v["gate_eff"], layer.y)
@@ -158,9 +158,13 @@ def main():
     A = int(counts.sum())
     active = int((counts > 0).sum())
     es = 2 if cfg["dtype"] == "bf16" else 4
+    q8 = cfg.get("weight_dtype", "same") == "int8"
+    ws = 1 if q8 else es  # bytes per weight element (int8 weights also read 4-byte column scales)
     work = {
-        "expert_up": dict(flops=4.0 * A * D * F, bytes=es * (2.0 * active * D * F + A * D + A * F)),
-        "expert_down": dict(flops=2.0 * A * F * D, bytes=es * (1.0 * active * D * F + A * F + A * D)),
+        "expert_up": dict(flops=4.0 * A * D * F,
+                          bytes=ws * 2.0 * active * D * F + (8.0 * active * F if q8 else 0.0) + es * (A * D + A * F)),
+        "expert_down": dict(flops=2.0 * A * F * D,
+                            bytes=ws * 1.0 * active * D * F + (4.0 * active * D if q8 else 0.0) + es * (A * F + A * D)),
     }
     gemm_ms = stage_ms["expert_up"] + stage_ms["expert_down"]
     gemm_tflops = (work["expert_up"]["flops"] + work["expert_down"]["flops"]) / (gemm_ms * 1e-3) / 1e12
@@ -188,7 +192,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": cfg["dtype"],
+        "dtype": cfg["dtype"] + ("+int8 weights" if q8 else ""),
         "data": "synthetic (seeded normal inputs and random-init expert weights of the workload's shapes)",
         "config": {"workload": cfg["name"], "N": N, "D": D, "F": F, "E": E, "k": k, "routing": cfg["routing_mode"],
                    "second_choice": cfg["second_choice"], "activation": cfg["activation"],

@@ -277,6 +277,34 @@ MOE_API int moe_forward(const moe_desc* desc, const void* x, const float* w_r, c
                 const float* noise, const void* w1, const void* w2, const void* w3, void* y,
                 void* workspace, size_t workspace_bytes, void* stream);
 
+/* ---- weight-only 8-bit experts ------------------------------------------------------
+ * Grok-1 keeps its expert weights 8-bit and dequantises them right before the expert
+ * matmul, weight = weight * scales ([GROK5] §5.3.3 moe_slow_matmul1 and §5.3.4 moe_slow_matmul2). Here:
+ *   W1q, W2q [E,D,F] int8, W3q [E,F,D] int8, with fp32 scales s1, s2 [E,F] and s3 [E,D]:
+ *   the dequantised weight is W[e,k,n] = q[e,k,n] * s[e,n], one scale per expert and
+ *   output column, broadcast over the input dimension (the pages print the scales as
+ *   having the weight's shape; a per-column scale is that array broadcast along K).
+ * The expert FFN then equals moe_expert_ffn on the dequantised weights, up to rounding:
+ * the int8 values are widened exactly to bf16 for the matrix cores, products accumulate
+ * in fp32 and the column scale multiplies the fp32 sum before the activation / store.
+ * desc->dtype must be MOE_DT_BF16 (MOE_E_UNSUPPORTED otherwise); every scale pointer is
+ * required and 16-byte aligned (MOE_E_INVAL). Everything else as for the bf16 entry
+ * points above: arguments, scratch, row ranges, errors. */
+MOE_API int moe_expert_up_q8(const moe_desc* desc, const void* x_perm, const int32_t* offsets,
+                     const int32_t* counts, const int8_t* w1, const float* s1, const int8_t* w2,
+                     const float* s2, void* h, void* scratch, size_t scratch_bytes, void* stream);
+MOE_API int moe_expert_down_q8(const moe_desc* desc, const void* h, const int32_t* offsets,
+                       const int32_t* counts, const int8_t* w3, const float* s3, void* y_perm,
+                       void* scratch, size_t scratch_bytes, void* stream);
+MOE_API int moe_expert_ffn_q8(const moe_desc* desc, const void* x_perm, const int32_t* offsets,
+                      const int32_t* counts, const int8_t* w1, const float* s1, const int8_t* w2,
+                      const float* s2, const int8_t* w3, const float* s3, void* h, void* y_perm,
+                      void* scratch, size_t scratch_bytes, void* stream);
+MOE_API int moe_forward_q8(const moe_desc* desc, const void* x, const float* w_r, const float* logit_bias,
+                   const float* noise, const int8_t* w1, const float* s1, const int8_t* w2,
+                   const float* s2, const int8_t* w3, const float* s3, void* y, void* workspace,
+                   size_t workspace_bytes, void* stream);
+
 /* Reduces the statistics left in `scratch` (or in a moe_forward workspace, whose first
  * moe_scratch_size bytes are the scratch) by the last moe_route + moe_dispatch on it,
  * copies them to *out and SYNCHRONISES `stream`. balance_loss fields are 0 if moe_route

@@ -28,7 +28,8 @@ CAP = {"none": 0, "padded": 1}
 EXPORTED = ["moe_status_string", "moe_capacity", "moe_rows", "moe_scratch_size", "moe_workspace_size",
             "moe_workspace_layout", "moe_route", "moe_dispatch", "moe_expert_ffn", "moe_expert_up",
             "moe_expert_down", "moe_combine",
-            "moe_forward", "moe_read_stats"]
+            "moe_forward", "moe_read_stats", "moe_expert_up_q8", "moe_expert_down_q8", "moe_expert_ffn_q8",
+            "moe_forward_q8"]
 
 
 class MoeError(RuntimeError):
@@ -90,6 +91,10 @@ def lib():
         L.moe_combine.argtypes = [_dp] + [_vp] * 4 + [_vp]
         L.moe_forward.argtypes = [_dp] + [_vp] * 8 + [_vp, ctypes.c_size_t, _vp]
         L.moe_read_stats.argtypes = [_dp, _vp, ctypes.c_size_t, ctypes.POINTER(moe_stats), _vp]
+        L.moe_expert_up_q8.argtypes = [_dp] + [_vp] * 8 + [_vp, ctypes.c_size_t, _vp]
+        L.moe_expert_down_q8.argtypes = [_dp] + [_vp] * 6 + [_vp, ctypes.c_size_t, _vp]
+        L.moe_expert_ffn_q8.argtypes = [_dp] + [_vp] * 11 + [_vp, ctypes.c_size_t, _vp]
+        L.moe_forward_q8.argtypes = [_dp] + [_vp] * 11 + [_vp, ctypes.c_size_t, _vp]
         for f in EXPORTED[1:]:
             getattr(L, f).restype = ctypes.c_int
         _LIB = L
@@ -279,6 +284,60 @@ def moe_forward(d, x, w_r, logit_bias, noise, w1, w2, w3, y, workspace, stream=N
            "moe_forward")
 
 
+# ---- weight-only 8-bit experts: int8 W [E, K, N] with fp32 column scales s [E, N] --------
+
+def _q8(w, s, E, K, N, name):
+    return (_ptr(w, (E, K, N), torch.int8, name), _ptr(s, (E, N), torch.float32, "scales of " + name))
+
+
+def moe_expert_up_q8(d, x_perm, offsets, counts, w1, s1, w2, s2, h, scratch, stream=None):
+    D, F, E = d.D, d.F, d.E
+    rows = moe_rows(d)
+    dt = _tdtype(d)
+    ps, sb = _bytes_ptr(scratch, moe_scratch_size(d), "scratch")
+    _check(lib().moe_expert_up_q8(ctypes.byref(d), _ptr(x_perm, (rows, D), dt, "x_perm"),
+                                  _ptr(offsets, (E + 1,), torch.int32, "offsets"),
+                                  _ptr(counts, (E,), torch.int32, "counts"), *_q8(w1, s1, E, D, F, "w1"),
+                                  *_q8(w2, s2, E, D, F, "w2"), _ptr(h, (rows, F), dt, "h"), ps, sb, _stream(stream)),
+           "moe_expert_up_q8")
+
+
+def moe_expert_down_q8(d, h, offsets, counts, w3, s3, y_perm, scratch, stream=None):
+    D, F, E = d.D, d.F, d.E
+    rows = moe_rows(d)
+    dt = _tdtype(d)
+    ps, sb = _bytes_ptr(scratch, moe_scratch_size(d), "scratch")
+    _check(lib().moe_expert_down_q8(ctypes.byref(d), _ptr(h, (rows, F), dt, "h"),
+                                    _ptr(offsets, (E + 1,), torch.int32, "offsets"),
+                                    _ptr(counts, (E,), torch.int32, "counts"), *_q8(w3, s3, E, F, D, "w3"),
+                                    _ptr(y_perm, (rows, D), dt, "y_perm"), ps, sb, _stream(stream)),
+           "moe_expert_down_q8")
+
+
+def moe_expert_ffn_q8(d, x_perm, offsets, counts, w1, s1, w2, s2, w3, s3, h, y_perm, scratch, stream=None):
+    D, F, E = d.D, d.F, d.E
+    rows = moe_rows(d)
+    dt = _tdtype(d)
+    ps, sb = _bytes_ptr(scratch, moe_scratch_size(d), "scratch")
+    _check(lib().moe_expert_ffn_q8(ctypes.byref(d), _ptr(x_perm, (rows, D), dt, "x_perm"),
+                                   _ptr(offsets, (E + 1,), torch.int32, "offsets"),
+                                   _ptr(counts, (E,), torch.int32, "counts"), *_q8(w1, s1, E, D, F, "w1"),
+                                   *_q8(w2, s2, E, D, F, "w2"), *_q8(w3, s3, E, F, D, "w3"),
+                                   _ptr(h, (rows, F), dt, "h"), _ptr(y_perm, (rows, D), dt, "y_perm"), ps, sb,
+                                   _stream(stream)), "moe_expert_ffn_q8")
+
+
+def moe_forward_q8(d, x, w_r, logit_bias, noise, w1, s1, w2, s2, w3, s3, y, workspace, stream=None):
+    N, D, F, E = d.N, d.D, d.F, d.E
+    dt = _tdtype(d)
+    pw, wb = _bytes_ptr(workspace, moe_workspace_size(d), "workspace")
+    _check(lib().moe_forward_q8(ctypes.byref(d), _ptr(x, (N, D), dt, "x"), _ptr(w_r, (D, E), torch.float32, "w_r"),
+                                _ptr(logit_bias, (E,), torch.float32, "logit_bias", optional=True),
+                                _ptr(noise, (N, E), torch.float32, "noise", optional=(d.second_choice == 0)),
+                                *_q8(w1, s1, E, D, F, "w1"), *_q8(w2, s2, E, D, F, "w2"), *_q8(w3, s3, E, F, D, "w3"),
+                                _ptr(y, (N, D), dt, "y"), pw, wb, _stream(stream)), "moe_forward_q8")
+
+
 def moe_read_stats(d, scratch, stream=None) -> dict:
     ps, sb = _bytes_ptr(scratch, moe_scratch_size(d), "scratch")
     st = moe_stats()
@@ -326,15 +385,33 @@ class MoELayer:
         self.x = inputs["x"].to(dev)
         self.w_r = inputs["w_r"].to(dev)
         self.w1, self.w2, self.w3 = (inputs[n].to(dev) for n in ("w1", "w2", "w3"))
+        self.q8 = cfg.get("weight_dtype", "same") == "int8"  # int8 weights + column scales
+        self.s1, self.s2, self.s3 = ((inputs[n].to(dev) for n in ("s1", "s2", "s3")) if self.q8 else (None,) * 3)
         self.bias = None if inputs.get("logit_bias") is None else inputs["logit_bias"].to(dev)
         self.noise = None if inputs.get("noise") is None else inputs["noise"].to(dev)
         self.y = torch.empty_like(self.x)
         self.ws = torch.empty(moe_workspace_size(self.desc), dtype=torch.uint8, device=dev)
 
     def forward(self, stream=None):
-        moe_forward(self.desc, self.x, self.w_r, self.bias, self.noise, self.w1, self.w2, self.w3, self.y, self.ws,
-                    stream)
+        if self.q8:
+            moe_forward_q8(self.desc, self.x, self.w_r, self.bias, self.noise, self.w1, self.s1, self.w2, self.s2,
+                           self.w3, self.s3, self.y, self.ws, stream)
+        else:
+            moe_forward(self.desc, self.x, self.w_r, self.bias, self.noise, self.w1, self.w2, self.w3, self.y,
+                        self.ws, stream)
         return self.y
+
+    def expert_up(self, x_perm, offsets, counts, h, scratch, stream=None):
+        if self.q8:
+            moe_expert_up_q8(self.desc, x_perm, offsets, counts, self.w1, self.s1, self.w2, self.s2, h, scratch, stream)
+        else:
+            moe_expert_up(self.desc, x_perm, offsets, counts, self.w1, self.w2, h, scratch, stream)
+
+    def expert_down(self, h, offsets, counts, y_perm, scratch, stream=None):
+        if self.q8:
+            moe_expert_down_q8(self.desc, h, offsets, counts, self.w3, self.s3, y_perm, scratch, stream)
+        else:
+            moe_expert_down(self.desc, h, offsets, counts, self.w3, y_perm, scratch, stream)
 
     def views(self):
         return workspace_views(self.desc, self.ws)

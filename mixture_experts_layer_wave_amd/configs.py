@@ -27,6 +27,8 @@ import copy
 #   zipf_s, zipf_beta     per-expert logit bias -beta*s*ln(rank), ranks a seeded
 #                         permutation of 1..E (None = no bias)
 #   noise_std             std of the routing noise [N,E] (None = no noise)
+#   weight_dtype          "same" (W1..W3 in dtype) | "int8" (weight-only 8-bit: int8 W with
+#                         fp32 scales per expert and output column; dtype must be bf16)
 #   seed                  generator seed
 
 CONFIGS = {
@@ -81,11 +83,31 @@ CONFIGS = {
         x_std=1.0, wr_var=1.0 / 2048, w_std=0.02, w3_std=0.02,
         zipf_s=1.0, zipf_beta=1.0, noise_std=1.0, seed=1006,
     ),
+    # Weight-only 8-bit experts ("第 5 章 ..." §5.3.3-5.3.4: Grok-1 dequantises 8-bit expert
+    # weights with scales right before the matmul) on the Mixtral decode and prefill
+    # shapes; weights of about the same std as the bf16 workloads.
+    "mixtral_decode_int8": dict(
+        N=64, D=4096, F=14336, E=8, k=2, dtype="bf16", weight_dtype="int8",
+        routing_mode="topk_softmax", second_choice="topk", activation="silu",
+        capacity_mode="none", capacity_factor=0.0, min_capacity=0,
+        capacity_priority="slot_major", capacity_formula="tokens_k",
+        x_std=1.0, wr_var=1.0 / 4096, w_std=0.02, w3_std=0.02,
+        zipf_s=1.0, zipf_beta=4.0, noise_std=None, seed=1004,
+    ),
+    "mixtral_prefill_int8": dict(
+        N=4096, D=4096, F=14336, E=8, k=2, dtype="bf16", weight_dtype="int8",
+        routing_mode="topk_softmax", second_choice="topk", activation="silu",
+        capacity_mode="none", capacity_factor=0.0, min_capacity=0,
+        capacity_priority="slot_major", capacity_formula="tokens_k",
+        x_std=1.0, wr_var=1.0 / 4096, w_std=0.02, w3_std=0.02,
+        zipf_s=None, zipf_beta=None, noise_std=None, seed=1002,
+    ),
 }
 
 # Order of the workloads as they are numbered in the documentation (1..5), then the
-# routing-variant workload.
-ORDER = ["tiny_fp32", "mixtral_prefill", "grok1_layer", "mixtral_decode", "gshard_capacity", "switch_top1"]
+# routing-variant and int8-weight workloads.
+ORDER = ["tiny_fp32", "mixtral_prefill", "grok1_layer", "mixtral_decode", "gshard_capacity", "switch_top1",
+         "mixtral_decode_int8", "mixtral_prefill_int8"]
 
 
 def get_config(workload: str, **overrides) -> dict:

@@ -52,6 +52,41 @@ __device__ __forceinline__ bf16x8 tr_read_b16x8(const bf16* q, int row_stride) {
   return __builtin_bit_cast(bf16x8, v);
 }
 
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+typedef i32x2 __attribute__((address_space(3))) * lds_i32x2_ptr;
+
+// gfx950 8-bit transposing LDS read: in each 16-lane group, result lane i gets byte i % 8
+// of the 8 bytes addressed by source lanes 2 j + i / 8, j = 0..7. With source lane s
+// pointing at row k0 + s / 2 and column half 8 (s % 2) of a 16-column segment, result
+// lane i holds column i of the segment for rows k0 .. k0 + 7.
+__device__ __forceinline__ i32x2 tr_read_b8x8(const void* q) {
+  return __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2_ptr)(q));
+}
+
+// Eight int8 values (little-endian in two dwords) -> eight bf16, exactly: each byte is
+// biased to unsigned (xor 0x80), converted to fp32 and unbiased; |v| <= 128 is exact in bf16.
+__device__ __forceinline__ bf16x8 i8x8_to_bf16(i32x2 r) {
+  u32x4 o;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const uint32_t u = (uint32_t)r[h] ^ 0x80808080u;
+#pragma unroll
+    for (int pr = 0; pr < 2; ++pr) {
+      const float f0 = (float)((u >> (16 * pr)) & 0xffu) - 128.f;
+      const float f1 = (float)((u >> (16 * pr + 8)) & 0xffu) - 128.f;
+      o[2 * h + pr] = (__float_as_uint(f0) >> 16) | (__float_as_uint(f1) & 0xffff0000u);
+    }
+  }
+  return __builtin_bit_cast(bf16x8, o);
+}
+
+// Chunk swizzle of int8 B rows with CPR 16-byte chunks per row (8 or 16).
+template <int CPR>
+__device__ __forceinline__ int q8_swz(int row) {
+  static_assert(CPR == 8 || CPR == 16, "int8 B rows of 128 or 256 bytes");
+  return CPR == 8 ? 2 * ((row >> 1) & 3) : 2 * (row & 7);
+}
+
 // Direct-to-LDS copy of 16 bytes per lane (global_load_lds_dwordx4): lane l's bytes land
 // at LDS byte address lds_addr + 16 l; lds_addr is wave-uniform and goes through M0.
 // Written as inline asm so the compiler does not treat the in-flight copy as a pending
@@ -87,17 +122,43 @@ __device__ __forceinline__ uint32_t lds_addr_of(const bf16* p) {
 // one have landed (each slice is LOADS copies per wave).
 template <int LOADS>
 __device__ __forceinline__ void wait_for_slice(int ahead) {
-  if (ahead >= 3) wait_vmcnt<3 * LOADS>();
-  else if (ahead == 2) wait_vmcnt<2 * LOADS>();
-  else if (ahead == 1) wait_vmcnt<LOADS>();
-  else wait_vmcnt<0>();
+  switch (ahead) {
+    case 0: wait_vmcnt<0>(); break;
+    case 1: wait_vmcnt<LOADS>(); break;
+    case 2: wait_vmcnt<2 * LOADS>(); break;
+    case 3: wait_vmcnt<3 * LOADS>(); break;
+    case 4: wait_vmcnt<(4 * LOADS < 63 ? 4 * LOADS : 0)>(); break;
+    case 5: wait_vmcnt<(5 * LOADS < 63 ? 5 * LOADS : 0)>(); break;
+    default: wait_vmcnt<(6 * LOADS < 63 ? 6 * LOADS : 0)>(); break;
+  }
 }
 
 // Epilogue of a tile: act(acc W1) * (acc W2) for the gated up-projection (NB = 2), the
 // plain product otherwise, rounded once to bf16. With the operands swapped, accumulator
 // element r of a lane holds row lane % 32 and column 8 (r / 4) + 4 (lane / 32) + r % 4
 // of its 32 x 32 block, so each lane stores 4 consecutive bf16 (8 bytes).
-template <int NB, int ACT, int TM, int TN, int WM, int WN>
+// Output values of 4 consecutive columns (col .. col + 3 of the tile) from the raw
+// accumulators a0 (B0) and a1 (B1): act(a0) * a1 for the gated up-projection, a0 otherwise,
+// each first multiplied by its column scale when the weights are int8.
+template <int NB, int ACT, bool Q8>
+__device__ __forceinline__ bf16x4 epilogue4(const GemmParams& p, const Tile& tl, int col, f32x4 a0, f32x4 a1) {
+  if constexpr (Q8) {
+    const int64_t sc = (int64_t)tl.e * p.N + tl.n0 + col;
+    a0 *= *reinterpret_cast<const f32x4*>(p.S0 + sc);
+    if constexpr (NB == 2) a1 *= *reinterpret_cast<const f32x4*>(p.S1 + sc);
+  }
+  bf16x4 o;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    float v;
+    if constexpr (NB == 2) v = activate<ACT>(a0[u]) * a1[u];
+    else v = a0[u];
+    o[u] = (bf16)v;
+  }
+  return o;
+}
+
+template <int NB, int ACT, int TM, int TN, int WM, int WN, bool Q8>
 __device__ __forceinline__ void store_tile(const f32x16 (&acc)[NB][TM][TN], const Tile& tl, const GemmParams& p,
                                            int wm, int wn, int lane) {
   const int N = p.N;
@@ -111,15 +172,13 @@ __device__ __forceinline__ void store_tile(const f32x16 (&acc)[NB][TM][TN], cons
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int col = wn * WN + 32 * j + 8 * q + 4 * (lane >> 5);
-        bf16x4 o;
+        f32x4 a0, a1;
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-          float v;
-          if constexpr (NB == 2) v = activate<ACT>(acc[0][i][j][4 * q + u]) * acc[1][i][j][4 * q + u];
-          else v = acc[0][i][j][4 * q + u];
-          o[u] = (bf16)v;
+          a0[u] = acc[0][i][j][4 * q + u];
+          a1[u] = acc[NB - 1][i][j][4 * q + u];
         }
-        *reinterpret_cast<bf16x4*>(Cg + (int64_t)row * N + col) = o;
+        *reinterpret_cast<bf16x4*>(Cg + (int64_t)row * N + col) = epilogue4<NB, ACT, Q8>(p, tl, col, a0, a1);
       }
   }
 }
@@ -147,24 +206,33 @@ __device__ __forceinline__ SkPlan sk_plan(int T, int G, int nk) {
 // groups: group g (of NACC / 4 per lane) of wave w, lane l at float4 index
 // ((slot * 8 + w) * NACC / 4 + g) * 64 + l, with g = ((m * TM + i) * TN + j) * 4 + q
 // holding accumulator elements 4q .. 4q + 3 of block (m, i, j).
-template <int BM, int BNF, int NB>
+// Wave grid of a workgroup (8 waves): 2 x 4 (rows x columns), or 1 x 8 for 64 x 256 tiles
+// of int8 weights, where every wave then converts distinct weight columns.
+template <int BM, int BNF, bool Q8>
+struct WaveGrid {
+  static constexpr int WGM = (Q8 && BM == 64 && BNF == 256) ? 1 : 2;
+  static constexpr int WGN = 8 / WGM;
+};
+
+template <int BM, int BNF, int NB, bool Q8 = false>
 struct Frag {
-  static constexpr int WM = BM / 2, WN = BNF / 4, TM = WM / 32, TN = WN / 32;
+  static constexpr int WGN = WaveGrid<BM, BNF, Q8>::WGN;
+  static constexpr int WM = BM / WaveGrid<BM, BNF, Q8>::WGM, WN = BNF / WGN, TM = WM / 32, TN = WN / 32;
   static constexpr int NACC = NB * TM * TN * 16;
   static constexpr int G4 = TM * TN * 4;       // 16-byte groups per matrix per lane
   static constexpr int ITEMS = 8 * G4 * 64;    // fix-up threads per tile
 };
 
-template <int BM, int BNF, int NB>
+template <int BM, int BNF, int NB, bool Q8>
 __device__ __forceinline__ f32x4* slot_base(const GemmParams& p, int64_t slot, int wid) {
-  return reinterpret_cast<f32x4*>(p.partial) + (slot * 8 + wid) * (Frag<BM, BNF, NB>::NACC / 4) * 64;
+  return reinterpret_cast<f32x4*>(p.partial) + (slot * 8 + wid) * (Frag<BM, BNF, NB, Q8>::NACC / 4) * 64;
 }
 
 // Fix-up thread `it` of a tile: sums the 16-byte groups (one per matrix) of the slots that
 // next_slot() yields, in order, applies the epilogue and stores 4 bf16 of one row.
-template <int BM, int BNF, int NB, int ACT, typename Slots>
+template <int BM, int BNF, int NB, int ACT, bool Q8, typename Slots>
 __device__ __forceinline__ void fixup_item(const GemmParams& p, const Tile& tl, int it, Slots next_slot) {
-  using FR = Frag<BM, BNF, NB>;
+  using FR = Frag<BM, BNF, NB, Q8>;
   const int w = it / (FR::G4 * 64), rem = it % (FR::G4 * 64);
   const int g = rem / 64, lane = rem % 64;
   f32x4 acc[NB];
@@ -172,48 +240,44 @@ __device__ __forceinline__ void fixup_item(const GemmParams& p, const Tile& tl, 
   for (int m = 0; m < NB; ++m) acc[m] = f32x4{0.f, 0.f, 0.f, 0.f};
   int64_t slot;
   while (next_slot(slot)) {
-    const f32x4* P = slot_base<BM, BNF, NB>(p, slot, w) + lane;
+    const f32x4* P = slot_base<BM, BNF, NB, Q8>(p, slot, w) + lane;
 #pragma unroll
     for (int m = 0; m < NB; ++m) acc[m] += P[(m * FR::G4 + g) * 64];
   }
   const int q = g % 4, ij = g / 4, i = ij / FR::TN, j = ij % FR::TN;
-  const int row = (w >> 2) * FR::WM + 32 * i + (lane & 31);
+  const int row = (w / FR::WGN) * FR::WM + 32 * i + (lane & 31);
   if (row >= tl.mcount) return;
-  const int col = (w & 3) * FR::WN + 32 * j + 8 * q + 4 * (lane >> 5);
-  bf16x4 o;
-#pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    float v;
-    if constexpr (NB == 2) v = activate<ACT>(acc[0][u]) * acc[1][u];
-    else v = acc[0][u];
-    o[u] = (bf16)v;
-  }
+  const int col = (w % FR::WGN) * FR::WN + 32 * j + 8 * q + 4 * (lane >> 5);
   bf16* C = reinterpret_cast<bf16*>(p.C) + (tl.row_base + row) * p.N + tl.n0 + col;
-  *reinterpret_cast<bf16x4*>(C) = o;
+  *reinterpret_cast<bf16x4*>(C) = epilogue4<NB, ACT, Q8>(p, tl, col, acc[0], acc[NB - 1]);
 }
 
 // STREAMK = false: persistent full tiles per XCD share, tail round split along K.
 // STREAMK = true : stream-K; the (tile, K slice) list is cut into equal contiguous ranges,
 //                  one per workgroup; a tile cut by a range boundary leaves fp32 partials
 //                  (slot 2w for the workgroup's first tile, 2w + 1 for its last).
-template <int BM, int BNF, int NB, int ACT, int BK, int STAGES, bool STREAMK>
+template <int BM, int BNF, int NB, int ACT, int BK, int STAGES, bool STREAMK, bool Q8>
 __global__ __launch_bounds__(512, 1) void k_gemm_bf16(const GemmParams p) {
   // BK: K slice per pipeline stage; STAGES: LDS ring depth (STAGES-1 slices in flight).
-  constexpr int WM = BM / 2, WN = BNF / 4;  // wave tile per matrix
+  // Q8: B0/B1 are int8 with per-column scales S0/S1 (weight-only 8-bit experts).
+  constexpr int WB = Q8 ? 1 : 2;            // bytes per B element
+  constexpr int WGN = WaveGrid<BM, BNF, Q8>::WGN;
+  constexpr int WM = BM / WaveGrid<BM, BNF, Q8>::WGM, WN = BNF / WGN;  // wave tile per matrix
   constexpr int TM = WM / 32, TN = WN / 32;
-  constexpr int A_EL = BM * BK, B_EL = BK * BNF;
-  constexpr int STAGE = A_EL + NB * B_EL;
+  constexpr int A_EL = BM * BK, B_BYTES = BK * BNF * WB;
+  constexpr int STAGE = A_EL + NB * B_BYTES / 2;    // bf16 elements per ring stage
   constexpr int A_CP = A_EL * 2 / 1024 / 8;         // 1 KB copies per wave per slice
-  constexpr int B_CPM = B_EL * 2 / 1024;            // 1 KB copies per matrix per slice
+  constexpr int B_CPM = B_BYTES / 1024;             // 1 KB copies per matrix per slice
   constexpr int B_CP = NB * B_CPM / 8;              // B copies per wave per slice
   constexpr int LOADS = A_CP + B_CP;
-  constexpr int B_RPC = 1024 / (BNF * 2);           // B rows per copy
-  constexpr int B_CPR = BNF / 8;                    // 16-byte chunks per B row
+  constexpr int B_RPC = 1024 / (BNF * WB);          // B rows per copy
+  constexpr int B_CPR = BNF * WB / 16;              // 16-byte chunks per B row
   constexpr int A_CPR = BK / 8;                     // 16-byte chunks per A row
   constexpr int A_RPB = 128 / BK;                   // A rows per 256 bytes (64 banks)
   constexpr int A_RPC = 512 / BK;                   // A rows per 1 KB copy
   static_assert((BM == 256 || BM == 64) && (BNF == 128 || BNF == 256) && (BK == 32 || BK == 64), "tile shape");
-  static_assert(STAGES >= 2 && STAGES <= 5 && STAGES * STAGE * 2 <= 160 * 1024, "LDS ring");
+  static_assert(!Q8 || BK == 64, "int8 tiles: 64-deep slices");
+  static_assert(STAGES >= 2 && STAGES <= 8 && STAGES * STAGE * 2 <= 160 * 1024, "LDS ring");
   static_assert(A_CP >= 1 && B_CP >= 1 && TM >= 1 && TN >= 1 && (NB * B_CPM) % 8 == 0, "tile shape");
 
   __shared__ __attribute__((aligned(1024))) bf16 ring[STAGES * STAGE];
@@ -221,7 +285,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm_bf16(const GemmParams p) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wid = uniform(tid >> 6);
-  const int wm = wid >> 2, wn = wid & 3;
+  const int wm = wid / WGN, wn = wid % WGN;
   const int K = p.K, N = p.N;
   const int nk = K / BK;
 
@@ -236,10 +300,16 @@ __global__ __launch_bounds__(512, 1) void k_gemm_bf16(const GemmParams p) {
   //   A [BM][BK]: row r, logical chunk c (8 elements) at physical chunk c ^ f(r),
   //               f(r) = (r / A_RPB) % A_CPR, so 16 consecutive rows hit 16 bank groups.
   //   B [BK][BNF]: row k, logical 32-byte segment g at physical segment g ^ (2 (k % 4)).
+  //   B int8 [BK][BNF]: row k (BNF bytes), logical 16-byte chunk c at physical chunk
+  //               c ^ q8_swz(k), q8_swz(k) = 2 ((k / 2) % 4) for 128-byte rows and 2 (k % 8)
+  //               for 256-byte rows: the 8 rows x 2 chunks of one 8-bit transposing read
+  //               by two 16-lane groups then fill 16 distinct bank groups.
   // Fragment addresses (constant per lane):
   //   A: lane -> row (lane % 32) of each 32-row block, k chunk 2 kk + lane / 32.
   //   B: transposing read; 16-lane group G -> column half (G & 1), k-half (G >> 1); lane s
   //      of the group supplies row s / 4 and columns 4 (s % 4) .. +3 of a 4 x 16 block.
+  //   B int8: 8-bit transposing read; group G -> columns 16 (G & 1) .. +15 of the 32-column
+  //      block, rows 8 (G >> 1) .. +7; lane s supplies row s / 2, column half s % 2.
   const int a_row = wm * WM + (lane & 31);
   const int a_swz = ((lane & 31) / A_RPB) % A_CPR;
   const int G = lane >> 4, s16 = lane & 15;
@@ -307,16 +377,18 @@ __global__ __launch_bounds__(512, 1) void k_gemm_bf16(const GemmParams p) {
       const int lc = (lane % A_CPR) ^ ((row / A_RPB) % A_CPR);
       a_src[q] = Ag + (int64_t)min(row, mlast) * K + 8 * lc;
     }
-    const bf16* b_src[B_CP];
+    const char* b_src[B_CP];  // byte addresses
 #pragma unroll
     for (int q = 0; q < B_CP; ++q) {
       const int c = B_CP * wid + q;
       const int m = c / B_CPM;
       const int row = B_RPC * (c % B_CPM) + lane / B_CPR;
       const int pc = lane % B_CPR;
-      const int lc = 2 * ((pc >> 1) ^ (2 * (row & 3))) + (pc & 1);
-      const bf16* Bm = reinterpret_cast<const bf16*>(m == 0 ? p.B0 : p.B1);
-      b_src[q] = Bm + boff + (int64_t)row * N + 8 * lc;
+      int lc;
+      if constexpr (Q8) lc = pc ^ q8_swz<B_CPR>(row);
+      else lc = 2 * ((pc >> 1) ^ (2 * (row & 3))) + (pc & 1);
+      const char* Bm = reinterpret_cast<const char*>(m == 0 ? p.B0 : p.B1);
+      b_src[q] = Bm + (boff + (int64_t)row * N) * WB + 16 * lc;
     }
 
     const int nku = ke - kb;  // K slices of this unit
@@ -327,7 +399,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm_bf16(const GemmParams p) {
       for (int q = 0; q < A_CP; ++q) load_lds16(a_src[q] + k0, (uint32_t)uniform(base + (A_CP * wid + q) * 1024));
 #pragma unroll
       for (int q = 0; q < B_CP; ++q)
-        load_lds16(b_src[q] + (int64_t)k0 * N, (uint32_t)uniform(base + A_EL * 2 + (B_CP * wid + q) * 1024));
+        load_lds16(b_src[q] + (int64_t)k0 * N * WB, (uint32_t)uniform(base + A_EL * 2 + (B_CP * wid + q) * 1024));
     };
 
     f32x16 acc[NB][TM][TN];
@@ -360,9 +432,18 @@ __global__ __launch_bounds__(512, 1) void k_gemm_bf16(const GemmParams p) {
 #pragma unroll
         for (int m = 0; m < NB; ++m)
 #pragma unroll
-          for (int j = 0; j < TN; ++j)
-            bfr[kk][m][j] = tr_read_b16x8(As + A_EL + m * B_EL + (kk * 16 + b_row) * BNF +
-                                              16 * ((b_seg + 2 * j) ^ b_swz) + b_in, BNF);
+          for (int j = 0; j < TN; ++j) {
+            if constexpr (Q8) {
+              const char* Bs = reinterpret_cast<const char*>(As + A_EL) + m * B_BYTES;
+              const int row = kk * 16 + 8 * (G >> 1) + (s16 >> 1);
+              const int chunk = (wn * WN + 32 * j) / 16 + (G & 1);
+              bfr[kk][m][j] =
+                  i8x8_to_bf16(tr_read_b8x8(Bs + row * BNF + 16 * (chunk ^ q8_swz<B_CPR>(row)) + 8 * (s16 & 1)));
+            } else {
+              bfr[kk][m][j] = tr_read_b16x8(As + A_EL + m * (B_BYTES / 2) + (kk * 16 + b_row) * BNF +
+                                                16 * ((b_seg + 2 * j) ^ b_swz) + b_in, BNF);
+            }
+          }
       }
 #pragma unroll
       for (int kk = 0; kk < BK / 16; ++kk)
@@ -379,7 +460,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm_bf16(const GemmParams p) {
 
     if (pslot >= 0) {
       // A K piece of a tile: keep the raw fp32 accumulators for the fix-up.
-      f32x4* P = slot_base<BM, BNF, NB>(p, pslot, wid) + lane;
+      f32x4* P = slot_base<BM, BNF, NB, Q8>(p, pslot, wid) + lane;
 #pragma unroll
       for (int m = 0; m < NB; ++m)
 #pragma unroll
@@ -391,7 +472,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm_bf16(const GemmParams p) {
               P[(((m * TM + i) * TN + j) * 4 + q) * 64] =
                   f32x4{acc[m][i][j][4 * q], acc[m][i][j][4 * q + 1], acc[m][i][j][4 * q + 2], acc[m][i][j][4 * q + 3]};
     } else {
-      store_tile<NB, ACT, TM, TN, WM, WN>(acc, tl, p, wm, wn, lane);
+      store_tile<NB, ACT, TM, TN, WM, WN, Q8>(acc, tl, p, wm, wn, lane);
     }
   }
 }
@@ -401,9 +482,9 @@ __global__ __launch_bounds__(512, 1) void k_gemm_bf16(const GemmParams p) {
 // shares are numbered in XCD order. Repeats the GEMM's schedule arithmetic from counts[]
 // so both kernels agree on the split. Every wave handles 64 consecutive threads of one
 // tile (ITEMS is a multiple of 64), so the tile lookup stays wave-uniform.
-template <int BM, int BNF, int NB, int ACT, int BK>
+template <int BM, int BNF, int NB, int ACT, int BK, bool Q8>
 __global__ __launch_bounds__(256) void k_gemm_tail_reduce(const GemmParams p, int nslot) {
-  using FR = Frag<BM, BNF, NB>;
+  using FR = Frag<BM, BNF, NB, Q8>;
   const int nk = p.K / BK;
   const TileScan ts = tile_scan<BM>(p);
   int total = 0;
@@ -426,7 +507,7 @@ __global__ __launch_bounds__(256) void k_gemm_tail_reduce(const GemmParams p, in
     Tile tl;
     if (!tile_of<BM, BNF>(p, ts, sh.lo + sh.rounds * nslot + i, tl)) continue;
     int piece = 0;
-    fixup_item<BM, BNF, NB, ACT>(p, tl, it, [&](int64_t& slot) {
+    fixup_item<BM, BNF, NB, ACT, Q8>(p, tl, it, [&](int64_t& slot) {
       if (piece >= sh.S) return false;
       slot = (int64_t)x * nslot + (int64_t)piece * sh.tail + i;
       ++piece;
@@ -438,9 +519,9 @@ __global__ __launch_bounds__(256) void k_gemm_tail_reduce(const GemmParams p, in
 // Stream-K fix-up: for every stream-K tile cut by a range boundary, sums the partials of
 // the workgroups that share it in workgroup order and stores the tile. Grid-stride over
 // (stream-K tile, fix-up thread), wave-uniform tiles as above.
-template <int BM, int BNF, int NB, int ACT, int BK>
+template <int BM, int BNF, int NB, int ACT, int BK, bool Q8>
 __global__ __launch_bounds__(256) void k_gemm_streamk_reduce(const GemmParams p, int grid) {
-  using FR = Frag<BM, BNF, NB>;
+  using FR = Frag<BM, BNF, NB, Q8>;
   const int nk = p.K / BK;
   const TileScan ts = tile_scan<BM>(p);
   const SkPlan sk = sk_plan(ts.total, grid, nk);
@@ -452,7 +533,7 @@ __global__ __launch_bounds__(256) void k_gemm_streamk_reduce(const GemmParams p,
     Tile tl;
     if (!tile_of<BM, BNF>(p, ts, sk.dp + ls, tl)) continue;
     int64_t w = wa;
-    fixup_item<BM, BNF, NB, ACT>(p, tl, it, [&](int64_t& slot) {
+    fixup_item<BM, BNF, NB, ACT, Q8>(p, tl, it, [&](int64_t& slot) {
       for (; w <= wb; ++w) {
         const int64_t b0 = sk_begin(w, sk.W, grid);
         if (sk_begin(w + 1, sk.W, grid) <= b0) continue;  // empty range (fewer items than workgroups)
@@ -481,11 +562,11 @@ int persistent_grid(int64_t tiles_bound) {
   return (int)g;
 }
 
-template <int BM, int BNF, int NB, int ACT, int BK, int STAGES, bool STREAMK>
+template <int BM, int BNF, int NB, int ACT, int BK, int STAGES, bool STREAMK, bool Q8>
 hipError_t launch_act(const GemmParams& p, int64_t bound, hipStream_t s) {
   // fp32 partial tiles: 8 waves x NACC accumulators x 64 lanes per slot; stream-K uses two
   // slots per workgroup, the tail split one.
-  using FR = Frag<BM, BNF, NB>;
+  using FR = Frag<BM, BNF, NB, Q8>;
   constexpr size_t kSlotBytes = (size_t)8 * FR::NACC * 64 * sizeof(float);
   static_assert((STREAMK ? 2 : 1) * kGemmPartialUnits * kSlotBytes <= kGemmPartialBytes, "partial scratch");
   // Fix-up grid: at most `grid` split tiles (tail tiles < one round; stream-K tiles < G).
@@ -497,29 +578,30 @@ hipError_t launch_act(const GemmParams& p, int64_t bound, hipStream_t s) {
   if constexpr (STREAMK) {
     // Every compute unit takes an equal share of the K slices.
     const int grid = persistent_grid(1 << 30);
-    hipLaunchKernelGGL((k_gemm_bf16<BM, BNF, NB, ACT, BK, STAGES, true>), dim3(grid), dim3(512), 0, s, p);
-    hipLaunchKernelGGL((k_gemm_streamk_reduce<BM, BNF, NB, ACT, BK>), dim3(fixup_grid(grid)), dim3(256), 0, s, p,
+    hipLaunchKernelGGL((k_gemm_bf16<BM, BNF, NB, ACT, BK, STAGES, true, Q8>), dim3(grid), dim3(512), 0, s, p);
+    hipLaunchKernelGGL((k_gemm_streamk_reduce<BM, BNF, NB, ACT, BK, Q8>), dim3(fixup_grid(grid)), dim3(256), 0, s, p,
                        grid);
   } else {
     const int grid = persistent_grid(bound);
-    hipLaunchKernelGGL((k_gemm_bf16<BM, BNF, NB, ACT, BK, STAGES, false>), dim3(grid), dim3(512), 0, s, p);
+    hipLaunchKernelGGL((k_gemm_bf16<BM, BNF, NB, ACT, BK, STAGES, false, Q8>), dim3(grid), dim3(512), 0, s, p);
     if (p.partial != nullptr)
-      hipLaunchKernelGGL((k_gemm_tail_reduce<BM, BNF, NB, ACT, BK>), dim3(fixup_grid(grid)), dim3(256), 0, s, p,
+      hipLaunchKernelGGL((k_gemm_tail_reduce<BM, BNF, NB, ACT, BK, Q8>), dim3(fixup_grid(grid)), dim3(256), 0, s, p,
                          grid / kXcds);
   }
   return hipGetLastError();
 }
 
-template <int BM, int BNF, int NB, int BK = MOE_GEMM_BK, int STAGES = MOE_GEMM_STAGES, bool STREAMK = false>
+template <int BM, int BNF, int NB, int BK = MOE_GEMM_BK, int STAGES = MOE_GEMM_STAGES, bool STREAMK = false,
+          bool Q8 = false>
 hipError_t launch_bf16(const GemmParams& p, int act, int64_t mtiles, hipStream_t s) {
   const int64_t bound = mtiles * p.n_tiles;
   if (bound <= 0) return hipSuccess;
   if constexpr (NB == 2) {
-    if (act == ACT_SILU) return launch_act<BM, BNF, 2, ACT_SILU, BK, STAGES, STREAMK>(p, bound, s);
-    if (act == ACT_GELU_ERF) return launch_act<BM, BNF, 2, ACT_GELU_ERF, BK, STAGES, STREAMK>(p, bound, s);
-    return launch_act<BM, BNF, 2, ACT_GELU_TANH, BK, STAGES, STREAMK>(p, bound, s);
+    if (act == ACT_SILU) return launch_act<BM, BNF, 2, ACT_SILU, BK, STAGES, STREAMK, Q8>(p, bound, s);
+    if (act == ACT_GELU_ERF) return launch_act<BM, BNF, 2, ACT_GELU_ERF, BK, STAGES, STREAMK, Q8>(p, bound, s);
+    return launch_act<BM, BNF, 2, ACT_GELU_TANH, BK, STAGES, STREAMK, Q8>(p, bound, s);
   } else {
-    return launch_act<BM, BNF, 1, ACT_SILU, BK, STAGES, STREAMK>(p, bound, s);
+    return launch_act<BM, BNF, 1, ACT_SILU, BK, STAGES, STREAMK, Q8>(p, bound, s);
   }
 }
 
@@ -541,6 +623,22 @@ bool skinny(const FfnArgs& a) { return a.partial != nullptr && a.max_rows_per_ex
 
 hipError_t launch_expert_up(const FfnArgs& a, bool bf16_io, hipStream_t s) {
   if (!bf16_io) return launch_gemm_f32(a, true, s);
+  if (a.s1 != nullptr) {
+    // int8 weights: 128-column tiles; the halved B bytes per slice allow deeper rings.
+    GemmParams p{a.x_perm, a.w1, a.w2, a.h, a.offsets, a.counts, a.E, a.D, a.F, a.F / 128, a.rows, a.partial,
+                 kSplitMax, a.s1, a.s2};
+    if (skinny(a)) {
+      // 64-row tiles, 256 columns per matrix, waves 1 x 8: each wave widens distinct
+      // weight columns, so the int8 -> bf16 conversion is not repeated across waves.
+      p.split_max = 1;
+      if (a.F % 256 == 0) {
+        p.n_tiles = a.F / 256;
+        return launch_bf16<kSkinnyRows, 256, 2, 64, 4, true, true>(p, a.act, max_m_tiles(a, kSkinnyRows), s);
+      }
+      return launch_bf16<kSkinnyRows, 128, 2, 64, 6, true, true>(p, a.act, max_m_tiles(a, kSkinnyRows), s);
+    }
+    return launch_bf16<256, 128, 2, 64, 3, false, true>(p, a.act, max_m_tiles(a, 256), s);
+  }
   if (skinny(a)) {
     constexpr int BNF = MOE_SKINNY_BNF;
     GemmParams p{a.x_perm, a.w1, a.w2, a.h, a.offsets, a.counts, a.E, a.D, a.F, a.F / BNF, a.rows, a.partial, 1};
@@ -557,6 +655,19 @@ hipError_t launch_expert_up(const FfnArgs& a, bool bf16_io, hipStream_t s) {
 
 hipError_t launch_expert_down(const FfnArgs& a, bool bf16_io, hipStream_t s) {
   if (!bf16_io) return launch_gemm_f32(a, false, s);
+  if (a.s3 != nullptr) {
+    GemmParams p{a.h, a.w3, nullptr, a.y_perm, a.offsets, a.counts, a.E, a.F, a.D, a.D / 128, a.rows, a.partial,
+                 kSplitMax, a.s3, nullptr};
+    if (skinny(a)) {
+      p.split_max = 1;
+      if (a.D % 256 == 0) {
+        p.n_tiles = a.D / 256;
+        return launch_bf16<kSkinnyRows, 256, 1, 64, 6, true, true>(p, a.act, max_m_tiles(a, kSkinnyRows), s);
+      }
+      return launch_bf16<kSkinnyRows, 128, 1, 64, 8, true, true>(p, a.act, max_m_tiles(a, kSkinnyRows), s);
+    }
+    return launch_bf16<256, 128, 1, 64, 4, false, true>(p, a.act, max_m_tiles(a, 256), s);
+  }
   if (skinny(a)) {
     GemmParams p{a.h, a.w3, nullptr, a.y_perm, a.offsets, a.counts, a.E, a.F, a.D, a.D / 128, a.rows, a.partial, 1};
     return launch_bf16<kSkinnyRows, 128, 1, 64, 4, true>(p, a.act, max_m_tiles(a, kSkinnyRows), s);

@@ -27,6 +27,8 @@ struct GemmParams {
   int64_t rows;     // rows of A and C: tiles never touch rows outside [0, rows)
   float* partial;   // split-K partial tiles (null: no split)
   int split_max;    // most K splits of one tile
+  const float* S0;  // [E, N] column scales of int8 B0 (weight-only 8-bit experts; else null)
+  const float* S1;  // [E, N] column scales of int8 B1
 };
 
 struct Tile {

@@ -137,10 +137,18 @@ int do_dispatch(const moe_desc* d, const void* x, const int32_t* idx, const floa
   return status_of(launch_gather(g, st));
 }
 
+// Column scales of int8 expert weights (all null: weights in the layer dtype).
+struct Scales {
+  const float* s1;
+  const float* s2;
+  const float* s3;
+};
+
 FfnArgs ffn_args(const moe_desc* d, int64_t C, int64_t rows, const void* x_perm, const int32_t* offsets,
                  const int32_t* counts, const void* w1, const void* w2, const void* w3, void* h, void* y_perm,
-                 void* scratch) {
+                 void* scratch, Scales sc) {
   FfnArgs a{};
+  a.s1 = sc.s1; a.s2 = sc.s2; a.s3 = sc.s3;
   if (d->dtype == MOE_DT_BF16) a.partial = at<float>(scratch, scratch_layout(d->N, d->D, d->E, d->k, true).partial);
   a.x_perm = x_perm; a.offsets = offsets; a.counts = counts; a.w1 = w1; a.w2 = w2; a.w3 = w3;
   a.h = h; a.y_perm = y_perm; a.rows = rows;
@@ -151,13 +159,14 @@ FfnArgs ffn_args(const moe_desc* d, int64_t C, int64_t rows, const void* x_perm,
 
 // which: 1 = up only, 2 = down only, 3 = both
 int do_ffn(const moe_desc* d, const void* x_perm, const int32_t* offsets, const int32_t* counts, const void* w1,
-           const void* w2, const void* w3, void* h, void* y_perm, void* scratch, int which, hipStream_t st) {
+           const void* w2, const void* w3, void* h, void* y_perm, void* scratch, int which, hipStream_t st,
+           Scales sc = Scales{nullptr, nullptr, nullptr}) {
   int64_t C, rows;
   int rc = capacity_of(d, &C);
   if (rc) return rc;
   rc = rows_of(d, &rows);
   if (rc) return rc;
-  const FfnArgs a = ffn_args(d, C, rows, x_perm, offsets, counts, w1, w2, w3, h, y_perm, scratch);
+  const FfnArgs a = ffn_args(d, C, rows, x_perm, offsets, counts, w1, w2, w3, h, y_perm, scratch, sc);
   const bool bf = d->dtype == MOE_DT_BF16;
   if (which & 1) {
     if (launch_expert_up(a, bf, st) != hipSuccess) return MOE_E_HIP;
@@ -313,9 +322,79 @@ int moe_combine(const moe_desc* d, const void* y_perm, const int32_t* row_of, co
   return do_combine(d, y_perm, row_of, gate_eff, y, (hipStream_t)stream);
 }
 
+// Checks shared by the int8-weight entry points: bf16 activations, scales present.
+static int check_q8(const moe_desc* d, const void* sa, const void* sb) {
+  if (d->dtype != MOE_DT_BF16) return MOE_E_UNSUPPORTED;
+  if (!sa || !aligned16(sa) || (sb != nullptr && !aligned16(sb))) return MOE_E_INVAL;
+  return MOE_OK;
+}
+
+static int forward_impl(const moe_desc* d, const void* x, const float* w_r, const float* logit_bias,
+                        const float* noise, const void* w1, const void* w2, const void* w3, void* y, void* workspace,
+                        size_t workspace_bytes, void* stream, Scales sc);
+
 int moe_forward(const moe_desc* d, const void* x, const float* w_r, const float* logit_bias, const float* noise,
                 const void* w1, const void* w2, const void* w3, void* y, void* workspace, size_t workspace_bytes,
                 void* stream) {
+  return forward_impl(d, x, w_r, logit_bias, noise, w1, w2, w3, y, workspace, workspace_bytes, stream,
+                      Scales{nullptr, nullptr, nullptr});
+}
+
+int moe_forward_q8(const moe_desc* d, const void* x, const float* w_r, const float* logit_bias, const float* noise,
+                   const int8_t* w1, const float* s1, const int8_t* w2, const float* s2, const int8_t* w3,
+                   const float* s3, void* y, void* workspace, size_t workspace_bytes, void* stream) {
+  int rc = check_desc(d);
+  if (rc) return rc;
+  if ((rc = check_q8(d, s1, s2)) != MOE_OK || (rc = check_q8(d, s3, nullptr)) != MOE_OK) return rc;
+  return forward_impl(d, x, w_r, logit_bias, noise, w1, w2, w3, y, workspace, workspace_bytes, stream,
+                      Scales{s1, s2, s3});
+}
+
+int moe_expert_up_q8(const moe_desc* d, const void* x_perm, const int32_t* offsets, const int32_t* counts,
+                     const int8_t* w1, const float* s1, const int8_t* w2, const float* s2, void* h, void* scratch,
+                     size_t scratch_bytes, void* stream) {
+  int rc = check_desc(d);
+  if (rc) return rc;
+  if ((rc = check_q8(d, s1, s2)) != MOE_OK) return rc;
+  REQUIRE(x_perm); REQUIRE(offsets); REQUIRE(counts); REQUIRE(w1); REQUIRE(w2); REQUIRE(h);
+  if (!s2) return MOE_E_INVAL;
+  if (!scratch || !aligned16(scratch)) return MOE_E_WORKSPACE;
+  if (scratch_bytes < scratch_layout(d->N, d->D, d->E, d->k, true).total) return MOE_E_WORKSPACE;
+  return do_ffn(d, x_perm, offsets, counts, w1, w2, nullptr, h, nullptr, scratch, 1, (hipStream_t)stream,
+                Scales{s1, s2, nullptr});
+}
+
+int moe_expert_down_q8(const moe_desc* d, const void* h, const int32_t* offsets, const int32_t* counts,
+                       const int8_t* w3, const float* s3, void* y_perm, void* scratch, size_t scratch_bytes,
+                       void* stream) {
+  int rc = check_desc(d);
+  if (rc) return rc;
+  if ((rc = check_q8(d, s3, nullptr)) != MOE_OK) return rc;
+  REQUIRE(h); REQUIRE(offsets); REQUIRE(counts); REQUIRE(w3); REQUIRE(y_perm);
+  if (!scratch || !aligned16(scratch)) return MOE_E_WORKSPACE;
+  if (scratch_bytes < scratch_layout(d->N, d->D, d->E, d->k, true).total) return MOE_E_WORKSPACE;
+  return do_ffn(d, nullptr, offsets, counts, nullptr, nullptr, w3, const_cast<void*>(h), y_perm, scratch, 2,
+                (hipStream_t)stream, Scales{nullptr, nullptr, s3});
+}
+
+int moe_expert_ffn_q8(const moe_desc* d, const void* x_perm, const int32_t* offsets, const int32_t* counts,
+                      const int8_t* w1, const float* s1, const int8_t* w2, const float* s2, const int8_t* w3,
+                      const float* s3, void* h, void* y_perm, void* scratch, size_t scratch_bytes, void* stream) {
+  int rc = check_desc(d);
+  if (rc) return rc;
+  if ((rc = check_q8(d, s1, s2)) != MOE_OK || (rc = check_q8(d, s3, nullptr)) != MOE_OK) return rc;
+  REQUIRE(x_perm); REQUIRE(offsets); REQUIRE(counts); REQUIRE(w1); REQUIRE(w2); REQUIRE(w3); REQUIRE(h);
+  REQUIRE(y_perm);
+  if (!s2) return MOE_E_INVAL;
+  if (!scratch || !aligned16(scratch)) return MOE_E_WORKSPACE;
+  if (scratch_bytes < scratch_layout(d->N, d->D, d->E, d->k, true).total) return MOE_E_WORKSPACE;
+  return do_ffn(d, x_perm, offsets, counts, w1, w2, w3, h, y_perm, scratch, 3, (hipStream_t)stream,
+                Scales{s1, s2, s3});
+}
+
+static int forward_impl(const moe_desc* d, const void* x, const float* w_r, const float* logit_bias,
+                        const float* noise, const void* w1, const void* w2, const void* w3, void* y, void* workspace,
+                        size_t workspace_bytes, void* stream, Scales sc) {
   int rc = check_desc(d);
   if (rc) return rc;
   REQUIRE(x); REQUIRE(w_r); OPTIONAL(logit_bias); REQUIRE(w1); REQUIRE(w2); REQUIRE(w3); REQUIRE(y);
@@ -337,7 +416,7 @@ int moe_forward(const moe_desc* d, const void* x, const float* w_r, const float*
                    at<void>(ws, L.x_perm), at<void>(ws, L.scratch), st);
   if (rc) return rc;
   rc = do_ffn(d, at<void>(ws, L.x_perm), at<int32_t>(ws, L.offsets), at<int32_t>(ws, L.counts), w1, w2, w3,
-              at<void>(ws, L.h), at<void>(ws, L.y_perm), at<void>(ws, L.scratch), 3, st);
+              at<void>(ws, L.h), at<void>(ws, L.y_perm), at<void>(ws, L.scratch), 3, st, sc);
   if (rc) return rc;
   return do_combine(d, at<void>(ws, L.y_perm), at<int32_t>(ws, L.row_of), at<float>(ws, L.gate_eff), y, st);
 }

@@ -143,9 +143,12 @@ struct FfnArgs {
   const void* x_perm;       // [rows,D]
   const int32_t* offsets;   // [E+1]
   const int32_t* counts;    // [E]
-  const void* w1;           // [E,D,F]
+  const void* w1;           // [E,D,F] (bf16 / fp32, or int8 when s1 is set)
   const void* w2;           // [E,D,F]
   const void* w3;           // [E,F,D]
+  const float* s1;          // [E,F] int8 column scales of w1 (null: w1 in the layer dtype)
+  const float* s2;          // [E,F]
+  const float* s3;          // [E,D]
   void* h;                  // [rows,F]
   void* y_perm;             // [rows,D]
   int64_t rows;             // rows of the expert buffers

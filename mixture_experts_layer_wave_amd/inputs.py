@@ -14,7 +14,8 @@ from concurrent.futures import ThreadPoolExecutor
 import numpy as np
 import torch
 
-_TENSOR_ID = {"x": 1, "w_r": 2, "w1": 3, "w2": 4, "w3": 5, "rank": 6, "noise": 7, "logits": 8}
+_TENSOR_ID = {"x": 1, "w_r": 2, "w1": 3, "w2": 4, "w3": 5, "rank": 6, "noise": 7, "logits": 8,
+              "s1": 9, "s2": 10, "s3": 11}
 
 
 def _rng(seed: int, name: str, sub: int = 0) -> np.random.Generator:
@@ -48,6 +49,25 @@ def _expert_stack(seed: int, name: str, E: int, shape, std: float, dtype: str) -
     return out
 
 
+def _int8_stack(seed: int, name: str, E: int, shape) -> torch.Tensor:
+    """int8 weights drawn uniformly from [-127, 127] (std about 73.3)."""
+    out = torch.empty((E, *shape), dtype=torch.int8)
+
+    def one(e):
+        out[e].copy_(torch.from_numpy(_rng(seed, name, e).integers(-127, 128, size=shape, dtype=np.int8)))
+
+    with ThreadPoolExecutor(_threads()) as ex:
+        list(ex.map(one, range(E)))
+    return out
+
+
+def _scales(seed: int, name: str, E: int, n: int, std: float) -> torch.Tensor:
+    """Per-(expert, column) scales: std / 73.3 times a factor uniform in [0.5, 1.5], so the
+    weights q * s have about the requested std."""
+    f = _rng(seed, name).random(size=(E, n), dtype=np.float32) + np.float32(0.5)
+    return torch.from_numpy((f * np.float32(std / 73.3)).astype(np.float32))
+
+
 def zipf_bias(cfg: dict) -> torch.Tensor | None:
     """Per-expert logit bias b_e = -beta * s * ln(r_e), ranks r a seeded permutation."""
     if cfg.get("zipf_s") is None:
@@ -65,7 +85,15 @@ def make_inputs(cfg: dict, weights: bool = True) -> dict:
     out = {"cfg": dict(cfg)}
     out["x"] = _store(_normal(s, "x", (N, D), cfg["x_std"]), dt)
     out["w_r"] = torch.from_numpy(_normal(s, "w_r", (D, E), float(cfg["wr_var"]) ** 0.5))
-    if weights:
+    if weights and cfg.get("weight_dtype", "same") == "int8":
+        # weight-only 8-bit experts: int8 values and fp32 scales per (expert, output column)
+        out["w1"] = _int8_stack(s, "w1", E, (D, F))
+        out["w2"] = _int8_stack(s, "w2", E, (D, F))
+        out["w3"] = _int8_stack(s, "w3", E, (F, D))
+        out["s1"] = _scales(s, "s1", E, F, cfg["w_std"])
+        out["s2"] = _scales(s, "s2", E, F, cfg["w_std"])
+        out["s3"] = _scales(s, "s3", E, D, cfg["w3_std"])
+    elif weights:
         out["w1"] = _expert_stack(s, "w1", E, (D, F), cfg["w_std"], dt)
         out["w2"] = _expert_stack(s, "w2", E, (D, F), cfg["w_std"], dt)
         out["w3"] = _expert_stack(s, "w3", E, (F, D), cfg["w3_std"], dt)

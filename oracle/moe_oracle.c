@@ -57,6 +57,17 @@ static double elem(const void* base, int dtype, int64_t i) {
   return (double)((const float*)base)[i];
 }
 
+/* Expert weight W[e][r][c] of an [E][R][C] stack. dtype 0/1: the stored value. dtype 2:
+ * weight-only 8-bit, the int8 value times the scale of its expert and output column,
+ * s[e][c] (the dequantisation weight = weight * scales of [GROK5] §5.3.3-5.3.4; one scale per
+ * expert and output column, broadcast over the input dimension). */
+#define W_INT8 2
+static double wel(const void* w, const float* s, int dtype, int64_t e, int64_t r, int64_t c, int64_t R, int64_t C) {
+  const int64_t i = (e * R + r) * C + c;
+  if (dtype == W_INT8) return (double)((const int8_t*)w)[i] * (double)s[e * C + c];
+  return elem(w, dtype, i);
+}
+
 /* ---- activations ([GROK5] §5.3.5, §5.3.5.1; [BOOK12] §12.1) ------------------------ */
 
 #define ACT_SILU 0
@@ -265,18 +276,18 @@ void oracle_drop_rule(int64_t N, int32_t k, const double* gate, const uint8_t* d
 
 /* ---- step 8: one expert on one token ([BOOK12] §12.1; [GROK5] §5.3.5) ----------------- */
 
-/* h[f] = act(sum_d x_d W1[e,d,f]) * (sum_d x_d W2[e,d,f]); W1, W2 are [E,D,F]. */
+/* h[f] = act(sum_d x_d W1[e,d,f]) * (sum_d x_d W2[e,d,f]); W1, W2 are [E,D,F]
+ * (s1, s2: [E,F] scales when w_dtype is int8, else unused). */
 int oracle_expert_hidden(int64_t D, int64_t F, int w_dtype, int act, const double* x,
-                         const void* w1, const void* w2, int32_t e, double* h) {
+                         const void* w1, const float* s1, const void* w2, const float* s2, int32_t e, double* h) {
   double* h1 = (double*)calloc((size_t)F, sizeof(double));
   double* h2 = (double*)calloc((size_t)F, sizeof(double));
   if (!h1 || !h2) { free(h1); free(h2); return ORACLE_EINVAL; }
-  const int64_t base_up = (int64_t)e * D * F;
   for (int64_t d = 0; d < D; ++d) {
     const double xd = x[d];
     for (int64_t f = 0; f < F; ++f) {
-      h1[f] += xd * elem(w1, w_dtype, base_up + d * F + f);
-      h2[f] += xd * elem(w2, w_dtype, base_up + d * F + f);
+      h1[f] += xd * wel(w1, s1, w_dtype, e, d, f, D, F);
+      h2[f] += xd * wel(w2, s2, w_dtype, e, d, f, D, F);
     }
   }
   for (int64_t f = 0; f < F; ++f) h[f] = oracle_act(act, h1[f]) * h2[f];
@@ -284,17 +295,18 @@ int oracle_expert_hidden(int64_t D, int64_t F, int w_dtype, int act, const doubl
   return ORACLE_OK;
 }
 
-/* out[d] = sum_f h_f W3[e,f,d] with h from oracle_expert_hidden; W3 is [E,F,D]. */
-int oracle_expert_ffn(int64_t D, int64_t F, int w_dtype, int act, const double* x,
-                      const void* w1, const void* w2, const void* w3, int32_t e, double* out) {
+/* out[d] = sum_f h_f W3[e,f,d] with h from oracle_expert_hidden; W3 is [E,F,D]
+ * (s3: [E,D] scales when w_dtype is int8). */
+int oracle_expert_ffn(int64_t D, int64_t F, int w_dtype, int act, const double* x, const void* w1,
+                      const float* s1, const void* w2, const float* s2, const void* w3, const float* s3,
+                      int32_t e, double* out) {
   double* h = (double*)malloc(sizeof(double) * (size_t)F);
   if (!h) return ORACLE_EINVAL;
-  if (oracle_expert_hidden(D, F, w_dtype, act, x, w1, w2, e, h) != ORACLE_OK) { free(h); return ORACLE_EINVAL; }
+  if (oracle_expert_hidden(D, F, w_dtype, act, x, w1, s1, w2, s2, e, h) != ORACLE_OK) { free(h); return ORACLE_EINVAL; }
   for (int64_t d = 0; d < D; ++d) out[d] = 0.0;
-  const int64_t base_dn = (int64_t)e * F * D;
   for (int64_t f = 0; f < F; ++f) {
     const double u = h[f];
-    for (int64_t d = 0; d < D; ++d) out[d] += u * elem(w3, w_dtype, base_dn + f * D + d);
+    for (int64_t d = 0; d < D; ++d) out[d] += u * wel(w3, s3, w_dtype, e, f, d, F, D);
   }
   free(h);
   return ORACLE_OK;
@@ -303,14 +315,16 @@ int oracle_expert_ffn(int64_t D, int64_t F, int w_dtype, int act, const double* 
 /* Expert outputs for a list of expert-buffer rows: out[i,:] = f_{e_i}(xrows[i,:]) and
  * hid[i,:] = the hidden vector h (either output may be NULL). */
 int oracle_expert_rows(int64_t n, int64_t D, int64_t F, int w_dtype, int act, const double* xrows,
-                       const int32_t* experts, const void* w1, const void* w2, const void* w3,
-                       double* hid, double* out) {
+                       const int32_t* experts, const void* w1, const float* s1, const void* w2, const float* s2,
+                       const void* w3, const float* s3, double* hid, double* out) {
   int bad = 0;
 #pragma omp parallel for schedule(dynamic, 1) reduction(| : bad)
   for (int64_t i = 0; i < n; ++i) {
-    if (hid && oracle_expert_hidden(D, F, w_dtype, act, xrows + i * D, w1, w2, experts[i], hid + i * F) != ORACLE_OK)
+    if (hid && oracle_expert_hidden(D, F, w_dtype, act, xrows + i * D, w1, s1, w2, s2, experts[i], hid + i * F) !=
+                   ORACLE_OK)
       bad = 1;
-    if (out && oracle_expert_ffn(D, F, w_dtype, act, xrows + i * D, w1, w2, w3, experts[i], out + i * D) != ORACLE_OK)
+    if (out && oracle_expert_ffn(D, F, w_dtype, act, xrows + i * D, w1, s1, w2, s2, w3, s3, experts[i],
+                                 out + i * D) != ORACLE_OK)
       bad = 1;
   }
   return bad ? ORACLE_EINVAL : ORACLE_OK;
@@ -335,9 +349,10 @@ void oracle_combine(int64_t N, int64_t D, int32_t k, const double* y_perm, const
 /* y[i,:] = sum over kept slots j of token t = toks[i], in slot order, of
  * gate_eff[t,j] * f_{idx[t,j]}(x_t); 0 when every slot is dropped. */
 int oracle_layer_tokens(int64_t n_tok, const int64_t* toks, int64_t N, int64_t D, int64_t F,
-                        int32_t E, int32_t k, int dtype, int act, const void* x,
-                        const void* w1, const void* w2, const void* w3, const int32_t* idx,
-                        const uint8_t* dropped, const double* gate_eff, double* y) {
+                        int32_t E, int32_t k, int dtype, int w_dtype, int act, const void* x,
+                        const void* w1, const float* s1, const void* w2, const float* s2, const void* w3,
+                        const float* s3, const int32_t* idx, const uint8_t* dropped, const double* gate_eff,
+                        double* y) {
   int bad = 0;
 #pragma omp parallel for schedule(dynamic, 1) reduction(| : bad)
   for (int64_t i = 0; i < n_tok; ++i) {
@@ -351,7 +366,7 @@ int oracle_layer_tokens(int64_t n_tok, const int64_t* toks, int64_t N, int64_t D
       if (dropped && dropped[t * k + j]) continue;
       const int32_t e = idx[t * k + j];
       if (e < 0 || e >= E) { bad = 1; break; }
-      if (oracle_expert_ffn(D, F, dtype, act, xt, w1, w2, w3, e, fo) != ORACLE_OK) { bad = 1; break; }
+      if (oracle_expert_ffn(D, F, w_dtype, act, xt, w1, s1, w2, s2, w3, s3, e, fo) != ORACLE_OK) { bad = 1; break; }
       const double g = gate_eff[t * k + j];
       for (int64_t d = 0; d < D; ++d) y[i * D + d] += g * fo[d];
     }

@@ -76,7 +76,20 @@ def _dtype_code(a: np.ndarray) -> int:
         return 1
     if a.dtype == np.float32:
         return 0
-    raise TypeError(f"oracle element type must be fp32 or bf16, got {a.dtype}")
+    if a.dtype == np.int8:
+        return 2
+    raise TypeError(f"oracle element type must be fp32, bf16 or int8 (weights), got {a.dtype}")
+
+
+def _scales(w, s, name):
+    """Scales [E, C] of an int8 weight stack [E, R, C] (None for fp32/bf16 weights)."""
+    if w.dtype != np.int8:
+        return None
+    if s is None:
+        raise ValueError(f"int8 {name} needs its scales")
+    sh = _host(s, np.float32)
+    assert sh.shape == (w.shape[0], w.shape[2]), (name, sh.shape, w.shape)
+    return sh
 
 
 @dataclass
@@ -118,14 +131,15 @@ class Oracle:
         L.oracle_drop_rule.restype = None
         L.oracle_drop_rule.argtypes = [_i64, _i32, _vp, _vp, _vp]
         L.oracle_expert_ffn.restype = _int
-        L.oracle_expert_ffn.argtypes = [_i64, _i64, _int, _int, _vp, _vp, _vp, _vp, _i32, _vp]
+        L.oracle_expert_ffn.argtypes = [_i64, _i64, _int, _int, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp]
         L.oracle_expert_rows.restype = _int
-        L.oracle_expert_rows.argtypes = [_i64, _i64, _i64, _int, _int, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
+        L.oracle_expert_rows.argtypes = [_i64, _i64, _i64, _int, _int, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                         _vp, _vp]
         L.oracle_combine.restype = None
         L.oracle_combine.argtypes = [_i64, _i64, _i32, _vp, _vp, _vp, _vp]
         L.oracle_layer_tokens.restype = _int
-        L.oracle_layer_tokens.argtypes = [_i64, _vp, _i64, _i64, _i64, _i32, _i32, _int, _int,
-                                          _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
+        L.oracle_layer_tokens.argtypes = [_i64, _vp, _i64, _i64, _i64, _i32, _i32, _int, _int, _int,
+                                          _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
         L.oracle_balance.restype = None
         L.oracle_balance.argtypes = [_i64, _i32, _i32, _vp, _vp, _vp, _vp, _vp]
         self.lib = L
@@ -200,28 +214,34 @@ class Oracle:
         return Dispatch(C, load, counts, offsets, row_of, dropped, gate_eff)
 
     # -- experts / layer ------------------------------------------------------------------
-    def expert_ffn(self, x_row, w1, w2, w3, e: int, act: str) -> np.ndarray:
+    def expert_ffn(self, x_row, w1, w2, w3, e: int, act: str, scales=None) -> np.ndarray:
+        """f_e(x) for one row. scales = (s1, s2, s3) when the weights are int8."""
         xr = _host(x_row, np.float64)
         a, b, c = _host(w1), _host(w2), _host(w3)
+        s1, s2, s3 = (_scales(a, scales and scales[0], "w1"), _scales(b, scales and scales[1], "w2"),
+                      _scales(c, scales and scales[2], "w3"))
         E, D, F = a.shape
         out = np.empty(D, np.float64)
-        rc = self.lib.oracle_expert_ffn(D, F, _dtype_code(a), ACT[act], _ptr(xr), _ptr(a), _ptr(b), _ptr(c),
-                                        int(e), _ptr(out))
+        rc = self.lib.oracle_expert_ffn(D, F, _dtype_code(a), ACT[act], _ptr(xr), _ptr(a), _ptr(s1), _ptr(b), _ptr(s2),
+                                        _ptr(c), _ptr(s3), int(e), _ptr(out))
         if rc != 0:
             raise ValueError("oracle_expert_ffn failed")
         return out
 
-    def expert_rows(self, xrows, experts, w1, w2, w3, act: str, want_hidden=True, want_out=True):
-        """(h, f) for expert-buffer rows: h[i] = act(x_i W1_e) * (x_i W2_e), f[i] = h[i] W3_e."""
+    def expert_rows(self, xrows, experts, w1, w2, w3, act: str, want_hidden=True, want_out=True, scales=None):
+        """(h, f) for expert-buffer rows: h[i] = act(x_i W1_e) * (x_i W2_e), f[i] = h[i] W3_e.
+        scales = (s1, s2, s3) when the weights are int8 (W = q * s[e, column])."""
         xr = _host(xrows, np.float64)
         ex = _host(experts, np.int32)
         a, b, c = _host(w1), _host(w2), _host(w3)
+        s1, s2, s3 = (_scales(a, scales and scales[0], "w1"), _scales(b, scales and scales[1], "w2"),
+                      _scales(c, scales and scales[2], "w3"))
         n, D = xr.shape
         F = a.shape[2]
         hid = np.empty((n, F), np.float64) if want_hidden else None
         out = np.empty((n, D), np.float64) if want_out else None
-        rc = self.lib.oracle_expert_rows(n, D, F, _dtype_code(a), ACT[act], _ptr(xr), _ptr(ex), _ptr(a), _ptr(b),
-                                         _ptr(c), _ptr(hid), _ptr(out))
+        rc = self.lib.oracle_expert_rows(n, D, F, _dtype_code(a), ACT[act], _ptr(xr), _ptr(ex), _ptr(a), _ptr(s1),
+                                         _ptr(b), _ptr(s2), _ptr(c), _ptr(s3), _ptr(hid), _ptr(out))
         if rc != 0:
             raise ValueError("oracle_expert_rows failed")
         return hid, out
@@ -236,11 +256,13 @@ class Oracle:
         self.lib.oracle_combine(N, D, k, _ptr(yp), _ptr(ro), _ptr(ge), _ptr(y))
         return y
 
-    def layer_tokens(self, tokens, x, w1, w2, w3, idx, dropped, gate_eff, act: str) -> np.ndarray:
-        """y rows of the listed tokens (fp64)."""
+    def layer_tokens(self, tokens, x, w1, w2, w3, idx, dropped, gate_eff, act: str, scales=None) -> np.ndarray:
+        """y rows of the listed tokens (fp64). scales = (s1, s2, s3) when the weights are int8."""
         toks = np.ascontiguousarray(np.asarray(tokens, np.int64))
         xh = _host(x)
         a, b, c = _host(w1), _host(w2), _host(w3)
+        s1, s2, s3 = (_scales(a, scales and scales[0], "w1"), _scales(b, scales and scales[1], "w2"),
+                      _scales(c, scales and scales[2], "w3"))
         ih = _host(idx, np.int32)
         dh = _host(dropped, np.uint8)
         gh = _host(gate_eff, np.float64)
@@ -248,12 +270,12 @@ class Oracle:
         E, D2, F = a.shape
         assert D2 == D and c.shape == (E, F, D)
         k = ih.shape[1]
-        if _dtype_code(xh) != _dtype_code(a):
-            raise TypeError("x and expert weights must share one element type")
+        if _dtype_code(a) != 2 and _dtype_code(xh) != _dtype_code(a):
+            raise TypeError("x and expert weights must share one element type (or the weights are int8)")
         y = np.empty((len(toks), D), np.float64)
-        rc = self.lib.oracle_layer_tokens(len(toks), _ptr(toks), N, D, F, E, k, _dtype_code(a), ACT[act],
-                                          _ptr(xh), _ptr(a), _ptr(b), _ptr(c), _ptr(ih), _ptr(dh), _ptr(gh),
-                                          _ptr(y))
+        rc = self.lib.oracle_layer_tokens(len(toks), _ptr(toks), N, D, F, E, k, _dtype_code(xh), _dtype_code(a),
+                                          ACT[act], _ptr(xh), _ptr(a), _ptr(s1), _ptr(b), _ptr(s2), _ptr(c), _ptr(s3),
+                                          _ptr(ih), _ptr(dh), _ptr(gh), _ptr(y))
         if rc != 0:
             raise ValueError("oracle_layer_tokens failed")
         return y

@@ -524,4 +524,60 @@ def pin_expert_rows_library(orc):
         _close(out[i], h @ w3[e].astype(np.float64), rtol=1e-12, atol=1e-14)
 
 
+def _int8_case(seed, E=3, D=8, F=12):
+    rng = np.random.default_rng(seed)
+    q1 = rng.integers(-128, 128, (E, D, F)).astype(np.int8)
+    q2 = rng.integers(-128, 128, (E, D, F)).astype(np.int8)
+    q3 = rng.integers(-128, 128, (E, F, D)).astype(np.int8)
+    s1 = (rng.random((E, F)) * 0.02 / 64).astype(np.float32)
+    s2 = (rng.random((E, F)) * 0.02 / 64).astype(np.float32)
+    s3 = (rng.random((E, D)) * 0.02 / 64).astype(np.float32)
+    return (q1, q2, q3), (s1, s2, s3)
+
+
+def pin_int8_weights_library(orc):
+    """Weight-only 8-bit experts ([GROK5] §5.3.3-5.3.4, weight = weight * scales): rows and layer
+    outputs equal numpy matmuls with the dequantised weights q[e,k,n] * s[e,n], with
+    scipy activations; every int8 value (-128..127) occurs."""
+    (q1, q2, q3), (s1, s2, s3) = _int8_case(5)
+    assert q1.min() == -128 and q1.max() == 127
+    rng = np.random.default_rng(6)
+    x = rng.standard_normal((7, 8)).astype(np.float32)
+    w1 = q1.astype(np.float64) * s1[:, None, :]
+    w2 = q2.astype(np.float64) * s2[:, None, :]
+    w3 = q3.astype(np.float64) * s3[:, None, :]
+    experts = np.array([2, 0, 1, 1, 2, 0, 1], np.int32)
+    hid, out = orc.expert_rows(x, experts, q1, q2, q3, "silu", scales=(s1, s2, s3))
+    for i, e in enumerate(experts):
+        h1 = x[i].astype(np.float64) @ w1[e]
+        h = h1 * scipy.special.expit(h1) * (x[i].astype(np.float64) @ w2[e])
+        _close(hid[i], h, rtol=1e-12, atol=1e-16)
+        _close(out[i], h @ w3[e], rtol=1e-12, atol=1e-16)
+    # the layer: Grok-1's dense all-experts + one-hot formula on the dequantised weights
+    lg = rng.standard_normal((7, 3))
+    r = orc.route(lg, 2, "softmax_topk")
+    d = orc.dispatch(r.idx, r.gate, 3, None, False)
+    y = orc.layer_tokens(np.arange(7), x, q1, q2, q3, r.idx, d.dropped, d.gate_eff, "gelu_erf", scales=(s1, s2, s3))
+    ref = dense_onehot_layer(dense_all_experts(x, w1, w2, w3, "gelu_erf"), r.idx, d.gate_eff, d.dropped)
+    _close(y, ref, rtol=1e-11, atol=1e-15)
+
+
+def pin_int8_scale_axis(orc):
+    """The scale belongs to the output column: scaling column n of W by c_n scales output
+    column n of the projection by c_n ((x W) diag(c) = x (W diag(c))), checked by
+    doubling one column's scale of W3, and it is per expert."""
+    (q1, q2, q3), (s1, s2, s3) = _int8_case(8)
+    x = np.random.default_rng(9).standard_normal((1, 8)).astype(np.float32)
+    base = orc.expert_ffn(x[0], q1, q2, q3, 1, "silu", scales=(s1, s2, s3))
+    t3 = s3.copy()
+    t3[1, 5] *= 2.0
+    mod = orc.expert_ffn(x[0], q1, q2, q3, 1, "silu", scales=(s1, s2, t3))
+    want = base.copy()
+    want[5] *= 2.0
+    _close(mod, want, rtol=1e-14, atol=0.0)
+    t3 = s3.copy()
+    t3[0, 5] *= 2.0  # another expert's scale: no change
+    _close(orc.expert_ffn(x[0], q1, q2, q3, 1, "silu", scales=(s1, s2, t3)), base, rtol=0.0)
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_") and callable(v)]

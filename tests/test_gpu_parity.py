@@ -198,7 +198,12 @@ FFN_CASES = [
 
 @pytest.mark.parametrize("dt,act,D,F,E,counts", FFN_CASES)
 @pytest.mark.parametrize("layout", ["ragged", "padded"])
-def test_expert_ffn_from_identical_rows(orc, dt, act, D, F, E, counts, layout):
+@pytest.mark.parametrize("wq", ["same", "int8"])
+def test_expert_ffn_from_identical_rows(orc, dt, act, D, F, E, counts, layout, wq):
+    """Grouped GEMMs against the oracle's expert rows, from identical buffers; wq = int8:
+    weight-only 8-bit experts (int8 weights, fp32 column scales)."""
+    if wq == "int8" and dt != "bf16":
+        pytest.skip("int8 weights go with bf16 activations")
     counts = np.array(counts, np.int64)
     if layout == "ragged":
         N = int(counts.sum())  # k = 1: rows = N
@@ -214,8 +219,9 @@ def test_expert_ffn_from_identical_rows(orc, dt, act, D, F, E, counts, layout):
     d = B.make_desc(cfg)
     rows = B.moe_rows(d)
     wcfg = dict(cfg, seed=31 + D + F, x_std=1.0, wr_var=1.0 / D, w_std=0.05 if dt == "bf16" else (1.0 / D) ** 0.5,
-                w3_std=0.05 if dt == "bf16" else (1.0 / F) ** 0.5, noise_std=None, zipf_s=None)
+                w3_std=0.05 if dt == "bf16" else (1.0 / F) ** 0.5, noise_std=None, zipf_s=None, weight_dtype=wq)
     w = inputs.make_inputs(wcfg)
+    sc = (w["s1"], w["s2"], w["s3"]) if wq == "int8" else None
     xp = inputs.make_rows(rows, D, seed=D + rows, dtype=dt)
     x_perm = xp.to(DEV)
     h = torch.full((rows, F), 3.0, dtype=xp.dtype, device=DEV)
@@ -223,11 +229,16 @@ def test_expert_ffn_from_identical_rows(orc, dt, act, D, F, E, counts, layout):
     scratch = torch.empty(B.moe_scratch_size(d), dtype=torch.uint8, device=DEV)
     t_off = torch.from_numpy(offsets.astype(np.int32)).to(DEV)
     t_cnt = torch.from_numpy(counts.astype(np.int32)).to(DEV)
-    B.moe_expert_ffn(d, x_perm, t_off, t_cnt, w["w1"].to(DEV), w["w2"].to(DEV), w["w3"].to(DEV), h, y_perm, scratch)
+    if wq == "int8":
+        B.moe_expert_ffn_q8(d, x_perm, t_off, t_cnt, w["w1"].to(DEV), sc[0].to(DEV), w["w2"].to(DEV), sc[1].to(DEV),
+                            w["w3"].to(DEV), sc[2].to(DEV), h, y_perm, scratch)
+    else:
+        B.moe_expert_ffn(d, x_perm, t_off, t_cnt, w["w1"].to(DEV), w["w2"].to(DEV), w["w3"].to(DEV), h, y_perm,
+                         scratch)
     torch.cuda.synchronize()
     sel = np.concatenate([np.arange(offsets[e], offsets[e] + counts[e]) for e in range(E)])
     experts = np.concatenate([np.full(counts[e], e) for e in range(E)]).astype(np.int32)
-    hid, out = orc.expert_rows(xp.float().numpy()[sel], experts, w["w1"], w["w2"], w["w3"], act)
+    hid, out = orc.expert_rows(xp.float().numpy()[sel], experts, w["w1"], w["w2"], w["w3"], act, scales=sc)
     tol_h = 8e-3 if dt == "bf16" else 1e-5
     assert_rows_close(host(h)[sel], hid, tol_h, "h")
     assert_rows_close(host(y_perm)[sel], out, TOL_Y[dt], "y_perm")
@@ -336,7 +347,7 @@ def _check_layer(orc, cfg, sample=None, max_amb=16):
     else:
         toks = np.array([t for t in sample if tok_ok[t]], np.int64)
     y_ref = orc.layer_tokens(toks, inp["x"], inp["w1"], inp["w2"], inp["w3"], r.idx, o.dropped, o.gate_eff,
-                             cfg["activation"])
+                             cfg["activation"], scales=(inp["s1"], inp["s2"], inp["s3"]) if "s1" in inp else None)
     y = host(layer.y)[toks]
     err = assert_rows_close(y, y_ref, TOL_Y[cfg["dtype"]], "layer output")
     zero = np.all(o.dropped[toks] == 1, axis=1)
@@ -362,6 +373,9 @@ MID = [
                           capacity_formula="tokens", capacity_factor=1.5, name="gshard_token_major"),
     configs.scaled_config("mixtral_prefill", N=300, D=128, F=256, k=2, second_choice="noisy_all", noise_std=0.5,
                           name="mixtral_noisy_all"),
+    configs.scaled_config("mixtral_decode_int8", N=64, D=512, F=384),
+    configs.scaled_config("mixtral_prefill_int8", N=700, D=256, F=512),
+    configs.scaled_config("gshard_capacity", N=900, D=128, F=256, E=16, weight_dtype="int8", name="gshard_int8"),
 ]
 
 
@@ -370,8 +384,11 @@ def test_layer_mid_size(orc, cfg):
     _check_layer(orc, cfg)
 
 
-def test_layer_bitwise_reproducible_and_equal_to_steps(orc):
-    cfg = configs.scaled_config("gshard_capacity", N=1000, D=256, F=384, E=16)
+@pytest.mark.parametrize("cfg", [configs.scaled_config("gshard_capacity", N=1000, D=256, F=384, E=16),
+                                 configs.scaled_config("gshard_capacity", N=1000, D=256, F=384, E=16,
+                                                       weight_dtype="int8", name="gshard_int8")],
+                         ids=lambda c: c["name"])
+def test_layer_bitwise_reproducible_and_equal_to_steps(orc, cfg):
     inp = inputs.make_inputs(cfg)
     layer = B.MoELayer(cfg, inp)
     y1 = layer.forward().clone()
@@ -387,8 +404,8 @@ def test_layer_bitwise_reproducible_and_equal_to_steps(orc):
     out, _ = _run_dispatch(d, layer.x, idx, gate)
     h = torch.empty((rows, F), dtype=layer.x.dtype, device=DEV)
     yp = torch.empty((rows, D), dtype=layer.x.dtype, device=DEV)
-    B.moe_expert_up(d, out["x_perm"], out["offsets"], out["counts"], layer.w1, layer.w2, h, sc)
-    B.moe_expert_down(d, h, out["offsets"], out["counts"], layer.w3, yp, sc)
+    layer.expert_up(out["x_perm"], out["offsets"], out["counts"], h, sc)
+    layer.expert_down(h, out["offsets"], out["counts"], yp, sc)
     y3 = torch.empty_like(y1)
     B.moe_combine(d, yp, out["row_of"], out["gate_eff"], y3)
     torch.cuda.synchronize()
@@ -480,6 +497,19 @@ def test_workload_switch_top1(orc):
     extra = gone[:: max(1, len(gone) // 8)][:8].tolist() + kept[:: max(1, len(kept) // 8)][:8].tolist()
     res = _check_layer(orc, cfg, sample=_spread(cfg["N"], 16, extra=extra))
     assert res["layer"].stats()["capacity"] == C
+
+
+@pytest.mark.slow
+def test_workload_mixtral_decode_int8(orc):
+    res = _check_layer(orc, configs.get_config("mixtral_decode_int8"))
+    load = res["dispatch"].load
+    assert (load == 0).sum() >= 1 and (load > 0).sum() >= 2, f"decode workload must leave an expert empty: {load}"
+
+
+@pytest.mark.slow
+def test_workload_mixtral_prefill_int8(orc):
+    cfg = configs.get_config("mixtral_prefill_int8")
+    _check_layer(orc, cfg, sample=_spread(cfg["N"], 24, extra=(1, 4095)))
 
 
 @pytest.mark.slow

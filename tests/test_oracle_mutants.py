@@ -25,8 +25,14 @@ MUTANTS = {
     "switch_capacity_with_k": ("ceil(((double)N / (double)E) * cf)", "ceil(((double)N / (double)E) * cf * (double)k)"),
     "switch_capacity_floor": ("ceil(((double)N / (double)E) * cf)", "floor(((double)N / (double)E) * cf)"),
     "noise_all_ignored": ("if (noisy == NOISE_ALL)\n      for (int32_t e = 0; e < E; ++e) l32[e] = l32[e] + noise[t * E + e];", ";"),
-    "w3_transposed": ("out[d] += u * elem(w3, w_dtype, base_dn + f * D + d);",
-                      "out[d] += u * elem(w3, w_dtype, base_dn + d * F + f);"),
+    "w3_transposed": ("out[d] += u * wel(w3, s3, w_dtype, e, f, d, F, D);",
+                      "out[d] += u * wel(w3, s3, w_dtype, e, d, f, D, F);"),
+    "int8_scale_by_row": ("return (double)((const int8_t*)w)[i] * (double)s[e * C + c];",
+                          "return (double)((const int8_t*)w)[i] * (double)s[e * C + (r % C)];"),
+    "int8_unsigned": ("return (double)((const int8_t*)w)[i] * (double)s[e * C + c];",
+                      "return (double)((const uint8_t*)w)[i] * (double)s[e * C + c];"),
+    "int8_scale_other_expert": ("return (double)((const int8_t*)w)[i] * (double)s[e * C + c];",
+                                "return (double)((const int8_t*)w)[i] * (double)s[c];"),
     "silu_sign": ("if (kind == ACT_SILU) return z / (1.0 + exp(-z));", "if (kind == ACT_SILU) return z / (1.0 + exp(z));"),
     "gelu_scale": ("return 0.5 * z * (1.0 + erf(z / sqrt(2.0)));", "return 0.5 * z * (1.0 + erf(z));"),
     "act_on_w2_branch": ("h[f] = oracle_act(act, h1[f]) * h2[f];", "h[f] = h1[f] * oracle_act(act, h2[f]);"),
@@ -34,8 +40,7 @@ MUTANTS = {
                            "y[t * D + d] = gate_eff[t * k + j] * y_perm[r * D + d];"),
     "combine_gate_slot0": ("y[t * D + d] += gate_eff[t * k + j] * y_perm[r * D + d];",
                            "y[t * D + d] += gate_eff[t * k] * y_perm[r * D + d];"),
-    "rows_wrong_expert": ("xrows + i * D, w1, w2, w3, experts[i], out + i * D)",
-                          "xrows + i * D, w1, w2, w3, experts[0], out + i * D)"),
+    "rows_wrong_expert": ("w3, s3, experts[i],", "w3, s3, experts[0],"),
     "noise_on_slot0": ("val[e] = (j > 0 && noisy == NOISE_SECOND) ?", "val[e] = (noisy == NOISE_SECOND) ?"),
     "noise_second_on_all": ("val[e] = (j > 0 && noisy == NOISE_SECOND) ?", "val[e] = (j > 0 && noisy) ?"),
     "balance_f_div_n": ("b += ((double)load[e] / ((double)N * (double)k)) * P[e];", "b += ((double)load[e] / (double)N) * P[e];"),
