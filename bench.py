@@ -37,7 +37,7 @@ def parse():
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--workload", default="mixtral_prefill")
-    p.add_argument("--cpu-sample", type=int, default=768, help="tokens in the oracle's timed FFN sample")
+    p.add_argument("--cpu-sample", type=int, default=2048, help="tokens in the oracle's timed FFN sample")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--copy-mib", type=int, default=0,
                    help="instead of the bench: run a plain device copy of this many MiB `steps` times "
