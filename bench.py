@@ -60,11 +60,24 @@ def traffic_from_profiles(workload: str, kernel_stage: str):
     return None if st is None else st.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(cfg, inp, sample: int):
-    """The fp64 oracle (as it stands) on a bounded sample of the same workload."""
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(cfg, inp, sample: int, sample_1t: int = 64):
+    """The fp64 oracle (as it stands) on a bounded sample of the same workload, on all
+    host threads and (a smaller sample) on one thread."""
     import numpy as np
     from oracle import default_oracle
     orc = default_oracle()
+    threads = orc.set_threads(int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1)))
     N = cfg["N"]
     t0 = time.perf_counter()
     logits = orc.router_logits(inp["x"], inp["w_r"], inp["logit_bias"])
@@ -76,17 +89,29 @@ def cpu_baseline(cfg, inp, sample: int):
          if padded else None)
     o = orc.dispatch(r.idx, r.gate, cfg["E"], C, padded, token_major=cfg["capacity_priority"] == "token_major")
     t1 = time.perf_counter()
+    scales = (inp["s1"], inp["s2"], inp["s3"]) if "s1" in inp else None
     toks = np.linspace(0, N - 1, min(sample, N)).astype(np.int64)
     orc.layer_tokens(toks, inp["x"], inp["w1"], inp["w2"], inp["w3"], r.idx, o.dropped, o.gate_eff,
-                     cfg["activation"], scales=(inp["s1"], inp["s2"], inp["s3"]) if "s1" in inp else None)
+                     cfg["activation"], scales=scales)
     t2 = time.perf_counter()
     n = len(toks)
     per_tok = (t1 - t0) / N + (t2 - t1) / n
-    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    # one thread, on the first tokens of the same sample
+    orc.set_threads(1)
+    toks1 = toks[: min(sample_1t, n)]
+    t3 = time.perf_counter()
+    orc.layer_tokens(toks1, inp["x"], inp["w1"], inp["w2"], inp["w3"], r.idx, o.dropped, o.gate_eff,
+                     cfg["activation"], scales=scales)
+    t4 = time.perf_counter()
+    orc.set_threads(threads)
+    per_tok_1 = (t1 - t0) * threads / N + (t4 - t3) / len(toks1)
     return {"value": 1.0 / per_tok, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "cpu": _cpu_model(), "nproc": os.cpu_count(),
+            "value_1thread": 1.0 / per_tok_1,
             "sample": f"router+softmax+top-k+dispatch of all {N} tokens ({t1 - t0:.2f} s), expert FFN + combine "
                       f"of {n} evenly spaced tokens ({t2 - t1:.2f} s); rate = 1 / (route time per token + "
-                      f"FFN time per token)"}
+                      f"FFN time per token). value_1thread: FFN of the first {len(toks1)} of those tokens on one "
+                      f"thread ({t4 - t3:.2f} s), routing time scaled by the thread count"}
 
 
 def main():
@@ -152,8 +177,36 @@ def main():
     t1 = time.perf_counter()
     elapsed = t1 - t0
 
-    stage_ms = {s: float(np.mean([events[i][j].elapsed_time(events[i][j + 1]) for i in range(args.steps)]))
-                for j, s in enumerate(STAGES)}
+    stage_t = {s: np.array([events[i][j].elapsed_time(events[i][j + 1]) for i in range(args.steps)])
+               for j, s in enumerate(STAGES)}
+    stage_ms = {s: float(np.mean(t)) for s, t in stage_t.items()}
+    stage_pct = {s: {"p10": float(np.percentile(t, 10)), "median": float(np.median(t)),
+                     "p90": float(np.percentile(t, 90))} for s, t in stage_t.items()}
+
+    # Small stages again, each after writing a 512 MB buffer so the last-level cache holds
+    # none of their inputs (the timed steps above give the warm numbers).
+    flush = torch.empty(512 * 2 ** 20, dtype=torch.uint8, device=dev)
+    small = {
+        "route": lambda: B.moe_route(d, layer.x, layer.w_r, layer.bias, layer.noise, None, None, None, v["topk_idx"],
+                                     v["topk_gate"], sc),
+        "dispatch": lambda: B.moe_dispatch(d, layer.x, v["topk_idx"], v["topk_gate"], v["load"], v["counts"],
+                                           v["offsets"], v["row_of"], v["dropped"], v["gate_eff"], v["token_of_row"],
+                                           v["x_perm"], sc),
+        "combine": lambda: B.moe_combine(d, v["y_perm"], v["row_of"], v["gate_eff"], layer.y),
+    }
+    cold_ms = {}
+    for name, fn in small.items():
+        ts = []
+        for _ in range(5):
+            flush.fill_(1)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        cold_ms[name] = float(np.median(ts))
+    del flush
     counts = v["counts"].cpu().numpy().astype(np.int64)
     A = int(counts.sum())
     active = int((counts > 0).sum())
@@ -201,6 +254,8 @@ def main():
                          "useful_flops": work["expert_up"]["flops"] + work["expert_down"]["flops"],
                          "accepted_rows": A, "active_experts": active},
         "stages_ms": stage_ms,
+        "stages_ms_pct": stage_pct,
+        "stages_ms_cold": cold_ms,
         "roofline": roof,
         "cpu_baseline": None,
     }

@@ -34,12 +34,19 @@
  * Parity pins for every function live in tests/test_oracle_pins.py.
  */
 #include <math.h>
+#include <omp.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
 
 #define ORACLE_OK 0
 #define ORACLE_EINVAL (-1)
+
+/* Host threads used by the parallel loops (the arithmetic is the same for any count). */
+int oracle_set_threads(int n) {
+  if (n > 0) omp_set_num_threads(n);
+  return omp_get_max_threads();
+}
 
 /* ---- exact widening of the stored element types ---------------------------------- */
 

@@ -140,9 +140,15 @@ class Oracle:
         L.oracle_layer_tokens.restype = _int
         L.oracle_layer_tokens.argtypes = [_i64, _vp, _i64, _i64, _i64, _i32, _i32, _int, _int, _int,
                                           _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
+        L.oracle_set_threads.restype = _int
+        L.oracle_set_threads.argtypes = [_int]
         L.oracle_balance.restype = None
         L.oracle_balance.argtypes = [_i64, _i32, _i32, _vp, _vp, _vp, _vp, _vp]
         self.lib = L
+
+    def set_threads(self, n: int = 0) -> int:
+        """Host threads of the parallel loops (n <= 0: leave as is); returns the count in use."""
+        return self.lib.oracle_set_threads(int(n))
 
     # -- activations -------------------------------------------------------------------
     def act(self, kind: str, z: float) -> float:
