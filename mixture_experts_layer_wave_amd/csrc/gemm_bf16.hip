@@ -8,24 +8,25 @@
 // for the rows r of each expert e (rows [offsets[e], offsets[e] + counts[e])).
 //
 // Design.
-//  * Work unit: a BM x (NB * BNF) output tile of one expert, computed by 4 waves (2 x 2);
-//    each wave owns a 128 x 128 accumulator block (NB matrices x 128 rows x BNF/2 columns)
-//    of fp32 MFMA accumulators, 256 per lane. The up projection has NB = 2: the W1 and W2
-//    tiles of the same columns sit side by side, so act(.) * (.) is formed in registers
-//    and h is stored once in bf16.
+//  * Work unit: a BM x (NB * BNF) output tile of one expert, computed by 8 waves. For
+//    BM = 256 the waves form a 2 x 4 grid and each owns a 128-row block of fp32 MFMA
+//    accumulators (128 per lane). The up projection has NB = 2: the W1 and W2 tiles of the
+//    same columns sit side by side, so act(.) * (.) is formed in registers and h is stored
+//    once in bf16.
 //  * v_mfma_f32_32x32x16_bf16 with the operands swapped (weights as the first operand),
 //    so each lane ends with 4 consecutive output columns of one row and stores 8 bytes.
-//  * K loop over 64-wide slices, double-buffered in LDS. A (K contiguous) is read with
-//    ds_read_b128 from rows padded by 16 bytes. B (weights stored N contiguous) keeps its
-//    natural layout and is fed to the MFMA by the gfx950 transposing read
-//    ds_read_b64_tr_b16; rows are padded to 64 bytes modulo 256 so the four rows of a
-//    transposing read land in distinct banks. Fragments of the next 16-wide step are read
-//    while the current step's MFMAs issue. Global loads of slice k+2 are issued as soon as
-//    slice k+1 is written to LDS.
+//  * K loop over BK-wide slices in a ring of STAGES LDS buffers, filled by direct
+//    global-to-LDS copies (global_load_lds_dwordx4) that need no staging registers. A (K
+//    contiguous) is read with ds_read_b128; B (weights stored N contiguous) keeps its
+//    natural layout and is turned into MFMA operands by the gfx950 transposing read
+//    ds_read_b64_tr_b16 (ds_read_b64_tr_b8 plus an exact widening for int8 weights).
+//    Both LDS tiles are unpadded and XOR-swizzled so these reads are bank-conflict free.
 //  * Persistent, XCD-aware schedule: the grid is a multiple of 8 workgroups; workgroup b
 //    runs on XCD b mod 8 and walks a contiguous eighth of the tile list, so the tiles
 //    sharing one expert's activations and weight columns run concurrently inside one
-//    XCD's L2.
+//    XCD's L2. The last partial round is split along K; a fix-up kernel sums the pieces in
+//    a fixed order. With at most 64 rows per expert (decode), 64-row tiles and stream-K
+//    spread the weight stream evenly over all compute units.
 #include "gemm_common.h"
 
 namespace moe {
