@@ -22,6 +22,10 @@
 //   assign : the same ballots give each record's rank inside its block; position =
 //            base + rank. Rows, drop mask and gates after the drop rule are written.
 // The gather then copies token rows into the expert buffers with 16-byte vector moves.
+// Small batches (at most one 256-token block, e.g. decode) take one fused kernel instead:
+// every workgroup rebuilds the whole routing table in LDS (the same ballots and scan, a few
+// hundred records), workgroup 0 writes the metadata, and each workgroup gathers its share
+// of the rows, so the stage is one launch with the same results.
 #include "moe_device.h"
 #include "moe_internal.h"
 
@@ -288,6 +292,132 @@ __global__ __launch_bounds__(256) void k_dispatch_assign(const DispatchArgs a) {
   if (tid == 0) a.tokdrop[blockIdx.x] = drop_s[0] + drop_s[1] + drop_s[2] + drop_s[3];
 }
 
+// Copy of one expert-buffer row by one wave: token t's row of x, or zeros (t < 0).
+template <int VB>
+__device__ __forceinline__ void gather_row(const GatherArgs& a, int64_t r, int64_t t, int lane) {
+  const int64_t row_bytes = (int64_t)a.D * a.elem_bytes;
+  const int nvec = (int)(row_bytes / VB);
+  u32x4* dst = reinterpret_cast<u32x4*>(reinterpret_cast<char*>(a.x_perm) + r * row_bytes);
+  if (t >= 0 && t < a.N) {
+    const u32x4* src = reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(a.x) + t * row_bytes);
+    for (int i = lane; i < nvec; i += 64) dst[i] = src[i];
+  } else {
+    const u32x4 z = {0u, 0u, 0u, 0u};
+    for (int i = lane; i < nvec; i += 64) dst[i] = z;
+  }
+}
+
+// Fused dispatch of at most kDispatchTokens tokens (one token per thread) and at most
+// kSmallRows buffer rows. Every workgroup computes the same positions: per segment (slot,
+// or all slots when token-major) the ballot ranks inside each wave, then for each expert a
+// running sum over (segment, wave) gives the first position of each wave's records, as the
+// three-pass path does over (segment, block).
+__global__ __launch_bounds__(256) void k_dispatch_small(const DispatchArgs a, const GatherArgs g) {
+  __shared__ int cnt_s[kMaxK][4][kMaxE];
+  __shared__ int base_s[kMaxK][4][kMaxE];
+  __shared__ int cap_s[kMaxE];
+  __shared__ int off_s[kMaxE + 1];
+  __shared__ int tor_s[kSmallRows];
+  __shared__ int drop_s[4];
+  const int tid = threadIdx.x;
+  const int w = tid >> 6, lane = tid & 63;
+  const int t = tid;
+  const bool valid = t < a.N;
+  const bool writer = blockIdx.x == 0;
+  const int nseg = a.token_major ? 1 : a.k;
+
+  int e[kMaxK], rank[kMaxK];
+  load_experts(a, t, valid, e);
+  if (a.token_major) {
+    wave_match_tokens(e, a.k, a.E, cnt_s[0], rank);
+  } else {
+#pragma unroll
+    for (int j = 0; j < kMaxK; ++j)
+      if (j < a.k) wave_match(e[j], a.E, cnt_s[j], rank[j]);
+  }
+  for (int r = tid; r < g.rows; r += 256) tor_s[r] = -1;
+  __syncthreads();
+  if (tid < a.E) {
+    int run = 0;
+    for (int sg = 0; sg < nseg; ++sg)
+      for (int ww = 0; ww < 4; ++ww) {
+        base_s[sg][ww][tid] = run;
+        run += cnt_s[sg][ww][tid];
+      }
+    const int c = (a.C < 0 || run < a.C) ? run : (int)a.C;
+    cap_s[tid] = c;
+    if (writer) {
+      a.load[tid] = run;
+      a.load_copy[tid] = run;
+      a.counts[tid] = c;
+    }
+  }
+  __syncthreads();
+  if (w == 0) {
+    const int c = lane < a.E ? cap_s[lane] : 0;
+    const int incl = wave_incl_scan(c);
+    if (lane < a.E) off_s[lane] = a.padded ? (int)((int64_t)lane * a.C) : incl - c;
+    if (lane == 63) off_s[a.E] = a.padded ? (int)((int64_t)a.E * a.C) : incl;
+  }
+  __syncthreads();
+  if (writer && tid <= a.E) a.offsets[tid] = off_s[tid];
+
+  int row[kMaxK];
+  bool kept[kMaxK];
+#pragma unroll
+  for (int j = 0; j < kMaxK; ++j) {
+    row[j] = -1;
+    kept[j] = false;
+    if (j < a.k && e[j] >= 0) {
+      const int pos = base_s[a.token_major ? 0 : j][w][e[j]] + rank[j];
+      kept[j] = (a.C < 0) || (pos < a.C);
+      if (kept[j]) {
+        row[j] = off_s[e[j]] + pos;
+        tor_s[row[j]] = t;
+      }
+    }
+  }
+
+  bool all_dropped = false;
+  if (valid) {
+    float gt[kMaxK];
+    float all = 0.f, ksum = 0.f;
+    int nk = 0;
+#pragma unroll
+    for (int j = 0; j < kMaxK; ++j) {
+      gt[j] = (j < a.k) ? a.topk_gate[t * a.k + j] : 0.f;
+      if (j < a.k) {
+        all += gt[j];
+        if (kept[j]) { ksum += gt[j]; nk += 1; }
+      }
+    }
+    all_dropped = (nk == 0);
+    if (writer) {
+#pragma unroll
+      for (int j = 0; j < kMaxK; ++j) {
+        if (j < a.k) {
+          float ge;
+          if (nk == a.k) ge = gt[j];
+          else if (nk == 0 || !kept[j]) ge = 0.f;
+          else ge = gt[j] * all / ksum;
+          a.row_of[t * a.k + j] = row[j];
+          a.dropped[t * a.k + j] = kept[j] ? 0 : 1;
+          a.gate_eff[t * a.k + j] = ge;
+        }
+      }
+    }
+  }
+  const uint64_t m = __ballot(all_dropped);
+  if (lane == 0) drop_s[w] = __popcll(m);
+  __syncthreads();
+  if (writer) {
+    if (tid == 0) a.tokdrop[0] = drop_s[0] + drop_s[1] + drop_s[2] + drop_s[3];
+    for (int r = tid; r < g.rows; r += 256) a.token_of_row[r] = tor_s[r];
+  }
+  for (int64_t r = (int64_t)blockIdx.x * 4 + w; r < g.rows; r += (int64_t)gridDim.x * 4)
+    gather_row<16>(g, r, tor_s[r], lane);
+}
+
 // One wave per expert-buffer row: copy the token's row or write zeros for padding.
 template <int VB>  // bytes per vector move
 __global__ __launch_bounds__(256) void k_gather(const GatherArgs a) {
@@ -300,18 +430,9 @@ __global__ __launch_bounds__(256) void k_gather(const GatherArgs a) {
     const int64_t e = r / a.C;
     valid = (r - e * a.C) < a.counts[e];
   }
-  const int64_t row_bytes = (int64_t)a.D * a.elem_bytes;
-  const int nvec = (int)(row_bytes / VB);
-  u32x4* dst = reinterpret_cast<u32x4*>(reinterpret_cast<char*>(a.x_perm) + r * row_bytes);
   const int64_t t = valid ? (int64_t)a.token_of_row[r] : -1;
-  if (t >= 0 && t < a.N) {
-    const u32x4* src = reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(a.x) + t * row_bytes);
-    for (int i = lane; i < nvec; i += 64) dst[i] = src[i];
-  } else {
-    const u32x4 z = {0u, 0u, 0u, 0u};
-    for (int i = lane; i < nvec; i += 64) dst[i] = z;
-    if (lane == 0) a.token_of_row[r] = -1;
-  }
+  gather_row<VB>(a, r, t, lane);
+  if (!(t >= 0 && t < a.N) && lane == 0) a.token_of_row[r] = -1;
 }
 
 // Statistics of the last route + dispatch, reduced in a fixed order (double precision).
@@ -361,6 +482,14 @@ hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(k_dispatch_count, dim3(a.nblk), dim3(256), 0, s, a);
   hipLaunchKernelGGL(k_dispatch_scan, dim3(1), dim3(64 * kScanWaves), 0, s, a);
   hipLaunchKernelGGL(k_dispatch_assign, dim3(a.nblk), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_dispatch_small(const DispatchArgs& a, const GatherArgs& g, hipStream_t s) {
+  if (a.N > kDispatchTokens || g.rows > kSmallRows) return hipErrorInvalidValue;
+  int64_t grid = (g.rows + 3) / 4;
+  grid = grid < 1 ? 1 : (grid > 256 ? 256 : grid);
+  hipLaunchKernelGGL(k_dispatch_small, dim3((unsigned)grid), dim3(256), 0, s, a, g);
   return hipGetLastError();
 }
 

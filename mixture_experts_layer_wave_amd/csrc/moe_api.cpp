@@ -128,12 +128,13 @@ int do_dispatch(const moe_desc* d, const void* x, const int32_t* idx, const floa
   const bool padded = d->capacity_mode == MOE_CAP_PADDED;
   a.C = padded ? C : -1;
   a.padded = padded;
-  hipError_t e = launch_dispatch(a, st);
-  if (e != hipSuccess) return MOE_E_HIP;
   GatherArgs g{};
   g.x = x; g.token_of_row = token_of_row; g.counts = counts; g.x_perm = x_perm;
   g.rows = rows; g.N = d->N; g.D = (int)d->D; g.elem_bytes = (int)esize(d);
   g.C = padded ? C : -1; g.padded = padded;
+  if (d->N <= kDispatchTokens && rows <= kSmallRows) return status_of(launch_dispatch_small(a, g, st));
+  hipError_t e = launch_dispatch(a, st);
+  if (e != hipSuccess) return MOE_E_HIP;
   return status_of(launch_gather(g, st));
 }
 

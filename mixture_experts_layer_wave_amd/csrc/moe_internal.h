@@ -12,6 +12,7 @@ constexpr int kRouterTokens = 32;     // tokens per router partial-sum block (ps
 constexpr int kRouterTile = 256;      // tokens per split-K router workgroup (8 waves x 32)
 constexpr int kRouterChunk = 64;      // K per pipeline step of the split-K router
 constexpr int kDispatchTokens = 256;  // tokens per dispatch workgroup
+constexpr int kSmallRows = 4096;       // most buffer rows of the fused one-launch dispatch
 constexpr int kMaxE = 64;
 constexpr int kMaxK = 8;
 constexpr uint32_t kPsumMagic = 0x5053554du;  // marks valid router partial sums
@@ -126,6 +127,7 @@ struct GatherArgs {
   int padded;
 };
 hipError_t launch_gather(const GatherArgs& a, hipStream_t s);
+hipError_t launch_dispatch_small(const DispatchArgs& a, const GatherArgs& g, hipStream_t s);
 
 struct StatsArgs {
   const float* psum;

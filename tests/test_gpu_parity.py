@@ -122,6 +122,9 @@ DISPATCH_CASES = [
     (700, 16, 4, 2.0, "padded", 0.5, 1), (513, 4, 4, 0.0, "padded", 0.3, 0), (300, 64, 8, 1.0, "none", 0.0, 0),
     (999, 8, 1, 3.0, "padded", 2.0, 0), (128, 2, 2, 0.0, "padded", 0.01, 1), (50, 64, 2, 0.0, "padded", 10.0, 0),
     (2000, 16, 2, 1.0, "padded", 1.0, 0), (1025, 8, 4, 1.5, "padded", 0.7, 2),
+    # at most 256 tokens: one fused launch while the buffer has at most 4096 rows, else
+    # the three-pass path
+    (64, 8, 2, 4.0, "none", 0.0, 0), (256, 64, 8, 1.0, "padded", 2.0, 0), (200, 64, 8, 1.0, "padded", 30.0, 0),
 ]
 
 
@@ -413,6 +416,8 @@ def test_layer_bitwise_reproducible_and_equal_to_steps(orc, cfg):
 
 
 @pytest.mark.parametrize("cfg", [configs.scaled_config("gshard_capacity", N=1000, D=256, F=384, E=16),
+                                 configs.scaled_config("gshard_capacity", N=200, D=256, F=384, E=16,
+                                                       name="gshard_capacity_fused_dispatch"),
                                  configs.scaled_config("mixtral_prefill", N=333, D=256, F=512),
                                  configs.scaled_config("switch_top1", N=1000, D=256, F=384)],
                          ids=lambda c: c["name"])
