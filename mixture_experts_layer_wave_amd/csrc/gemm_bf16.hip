@@ -670,7 +670,21 @@ hipError_t launch_expert_down(const FfnArgs& a, bool bf16_io, hipStream_t s) {
     return launch_bf16<256, 128, 1, 64, 4, false, true>(p, a.act, max_m_tiles(a, 256), s);
   }
   if (skinny(a)) {
-    GemmParams p{a.h, a.w3, nullptr, a.y_perm, a.offsets, a.counts, a.E, a.F, a.D, a.D / 128, a.rows, a.partial, 1};
+#ifndef MOE_SKINNY_DOWN_BNF
+#define MOE_SKINNY_DOWN_BNF 256
+#endif
+#ifndef MOE_SKINNY_DOWN_BK
+#define MOE_SKINNY_DOWN_BK 64
+#endif
+#ifndef MOE_SKINNY_DOWN_STAGES
+#define MOE_SKINNY_DOWN_STAGES 4
+#endif
+    constexpr int BNF = MOE_SKINNY_DOWN_BNF;
+    GemmParams p{a.h, a.w3, nullptr, a.y_perm, a.offsets, a.counts, a.E, a.F, a.D, a.D / BNF, a.rows, a.partial, 1};
+    if (a.D % BNF == 0)
+      return launch_bf16<kSkinnyRows, BNF, 1, MOE_SKINNY_DOWN_BK, MOE_SKINNY_DOWN_STAGES, true>(
+          p, a.act, max_m_tiles(a, kSkinnyRows), s);
+    p.n_tiles = a.D / 128;
     return launch_bf16<kSkinnyRows, 128, 1, 64, 4, true>(p, a.act, max_m_tiles(a, kSkinnyRows), s);
   }
   constexpr int BM = 256;

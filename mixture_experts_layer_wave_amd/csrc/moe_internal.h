@@ -28,12 +28,15 @@ inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 struct RouterSplit {
   int tiles, S, Ks;
 };
+#ifndef MOE_ROUTER_SMAX
+#define MOE_ROUTER_SMAX 32
+#endif
 inline RouterSplit router_split(int64_t N, int64_t D) {
   RouterSplit r;
   r.tiles = (int)((N + kRouterTile - 1) / kRouterTile);
   const int chunks = (int)(D / kRouterChunk);
   int S = r.tiles >= 256 ? 1 : 256 / r.tiles;
-  if (S > 32) S = 32;
+  if (S > MOE_ROUTER_SMAX) S = MOE_ROUTER_SMAX;
   if (S > chunks) S = chunks;
   if (S < 1) S = 1;
   while (chunks % S != 0) --S;

@@ -194,6 +194,7 @@ FFN_CASES = [
     ("bf16", "silu", 256, 384, 4, [30, 0, 20, 14]),         # <= 64 rows per expert: stream-K path
     ("bf16", "gelu_erf", 512, 256, 8, [1, 2, 3, 4, 5, 6, 7, 8]),
     ("bf16", "silu", 4096, 512, 3, [64, 0, 0]),
+    ("bf16", "gelu_tanh", 384, 256, 3, [17, 64, 0]),        # stream-K, D not a multiple of 256
     ("f32", "silu", 128, 256, 4, [30, 33, 0, 65]),
     ("f32", "gelu_erf", 256, 128, 3, [64, 1, 100]),
 ]
