@@ -39,6 +39,8 @@ def parse():
     p.add_argument("--workload", default="mixtral_prefill")
     p.add_argument("--cpu-sample", type=int, default=2048, help="tokens in the oracle's timed FFN sample")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cold-reps", type=int, default=5,
+                   help="cold-cache runs of each small stage before the warm-up (0: none)")
     p.add_argument("--copy-mib", type=int, default=0,
                    help="instead of the bench: run a plain device copy of this many MiB `steps` times "
                         "(calibration of the HBM byte counters)")
@@ -166,6 +168,32 @@ def main():
         if ev is not None:
             ev[5].record(stream)
 
+    step()  # every stage's inputs exist from here on
+    # Small stages alone, each after writing a 512 MB buffer so the last-level cache holds
+    # none of their inputs (the timed steps below give the warm numbers). Run before the
+    # warm-up so the timed steps are the last calls of every kernel.
+    flush = torch.empty(512 * 2 ** 20, dtype=torch.uint8, device=dev)
+    small = {
+        "route": lambda: B.moe_route(d, layer.x, layer.w_r, layer.bias, layer.noise, None, None, None, v["topk_idx"],
+                                     v["topk_gate"], sc),
+        "dispatch": lambda: B.moe_dispatch(d, layer.x, v["topk_idx"], v["topk_gate"], v["load"], v["counts"],
+                                           v["offsets"], v["row_of"], v["dropped"], v["gate_eff"], v["token_of_row"],
+                                           v["x_perm"], sc),
+        "combine": lambda: B.moe_combine(d, v["y_perm"], v["row_of"], v["gate_eff"], layer.y),
+    }
+    cold_ms = {}
+    for name, fn in (small.items() if args.cold_reps > 0 else ()):
+        ts = []
+        for _ in range(args.cold_reps):
+            flush.fill_(1)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        cold_ms[name] = float(np.median(ts))
+    del flush
     for _ in range(args.warmup):
         step()
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
@@ -183,30 +211,6 @@ def main():
     stage_pct = {s: {"p10": float(np.percentile(t, 10)), "median": float(np.median(t)),
                      "p90": float(np.percentile(t, 90))} for s, t in stage_t.items()}
 
-    # Small stages again, each after writing a 512 MB buffer so the last-level cache holds
-    # none of their inputs (the timed steps above give the warm numbers).
-    flush = torch.empty(512 * 2 ** 20, dtype=torch.uint8, device=dev)
-    small = {
-        "route": lambda: B.moe_route(d, layer.x, layer.w_r, layer.bias, layer.noise, None, None, None, v["topk_idx"],
-                                     v["topk_gate"], sc),
-        "dispatch": lambda: B.moe_dispatch(d, layer.x, v["topk_idx"], v["topk_gate"], v["load"], v["counts"],
-                                           v["offsets"], v["row_of"], v["dropped"], v["gate_eff"], v["token_of_row"],
-                                           v["x_perm"], sc),
-        "combine": lambda: B.moe_combine(d, v["y_perm"], v["row_of"], v["gate_eff"], layer.y),
-    }
-    cold_ms = {}
-    for name, fn in small.items():
-        ts = []
-        for _ in range(5):
-            flush.fill_(1)
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-            fn()
-            e1.record(stream)
-            torch.cuda.synchronize()
-            ts.append(e0.elapsed_time(e1))
-        cold_ms[name] = float(np.median(ts))
-    del flush
     counts = v["counts"].cpu().numpy().astype(np.int64)
     A = int(counts.sum())
     active = int((counts > 0).sum())
