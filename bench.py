@@ -3,9 +3,10 @@
 A step is one pass of the whole hot path over one batch of seeded synthetic input that
 is already resident in HBM: router (fp32 logits, softmax, top-k, gates) -> dispatch
 (histogram, capacity slots, drop rule, gather) -> gated up-projection grouped GEMM ->
-down-projection grouped GEMM -> combine. W untimed warm-up steps, then exactly K timed
-steps between two device synchronisations. HIP events recorded on the launch stream
-between the stages give each stage's average duration inside the timed region.
+down-projection grouped GEMM -> combine, as one moe_forward call. W untimed warm-up steps,
+then exactly K timed steps between two device synchronisations give the throughput.
+K more steps through the per-stage entry points (the same kernels), with HIP events
+recorded on the launch stream between the stages, give each stage's duration.
 
 Prints one JSON line: tokens/s, the roofline of the dominant kernel, and the fp64 CPU
 oracle timed on a bounded sample of the same workload on the host cores.
@@ -195,15 +196,33 @@ def main():
         cold_ms[name] = float(np.median(ts))
     del flush
     for _ in range(args.warmup):
+        layer.forward()
         step()
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+    # Timed: exactly K passes of the layer, one moe_forward call each, between two device
+    # synchronisations; an event pair around each call gives its spread.
+    fev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(events[i])
+        fev[i][0].record(stream)
+        layer.forward()
+        fev[i][1].record(stream)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     elapsed = t1 - t0
+    fwd_t = np.array([a.elapsed_time(b) for a, b in fev])
+    forward_ms = {"mean": float(np.mean(fwd_t)), "p10": float(np.percentile(fwd_t, 10)),
+                  "median": float(np.median(fwd_t)), "p90": float(np.percentile(fwd_t, 90))}
+
+    # Stage breakdown: K more passes through the per-stage entry points (the same kernels),
+    # with events between the stages.
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    ts0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    staged_ms_per_step = (time.perf_counter() - ts0) / args.steps * 1e3
 
     stage_t = {s: np.array([events[i][j].elapsed_time(events[i][j + 1]) for i in range(args.steps)])
                for j, s in enumerate(STAGES)}
@@ -257,6 +276,8 @@ def main():
         "grouped_gemm": {"tflops": gemm_tflops, "frac_bf16_peak": gemm_tflops / PEAK_BF16_TFLOPS,
                          "useful_flops": work["expert_up"]["flops"] + work["expert_down"]["flops"],
                          "accepted_rows": A, "active_experts": active},
+        "forward_ms": forward_ms,
+        "staged_ms_per_step": staged_ms_per_step,
         "stages_ms": stage_ms,
         "stages_ms_pct": stage_pct,
         "stages_ms_cold": cold_ms,
