@@ -28,6 +28,7 @@
 // of the rows, so the stage is one launch with the same results.
 #include "moe_device.h"
 #include "moe_internal.h"
+#include "route_token.h"
 
 namespace moe {
 namespace {
@@ -312,7 +313,9 @@ __device__ __forceinline__ void gather_row(const GatherArgs& a, int64_t r, int64
 // or all slots when token-major) the ballot ranks inside each wave, then for each expert a
 // running sum over (segment, wave) gives the first position of each wave's records, as the
 // three-pass path does over (segment, block).
-__global__ __launch_bounds__(256) void k_dispatch_small(const DispatchArgs a, const GatherArgs g) {
+// e[j] / gt[j]: the experts (-1: none) and gates of this thread's token t = threadIdx.x.
+__device__ __forceinline__ void dispatch_small_body(const DispatchArgs& a, const GatherArgs& g, int (&e)[kMaxK],
+                                                    const float (&gt)[kMaxK]) {
   __shared__ int cnt_s[kMaxK][4][kMaxE];
   __shared__ int base_s[kMaxK][4][kMaxE];
   __shared__ int cap_s[kMaxE];
@@ -326,8 +329,7 @@ __global__ __launch_bounds__(256) void k_dispatch_small(const DispatchArgs a, co
   const bool writer = blockIdx.x == 0;
   const int nseg = a.token_major ? 1 : a.k;
 
-  int e[kMaxK], rank[kMaxK];
-  load_experts(a, t, valid, e);
+  int rank[kMaxK];
   if (a.token_major) {
     wave_match_tokens(e, a.k, a.E, cnt_s[0], rank);
   } else {
@@ -380,12 +382,10 @@ __global__ __launch_bounds__(256) void k_dispatch_small(const DispatchArgs a, co
 
   bool all_dropped = false;
   if (valid) {
-    float gt[kMaxK];
     float all = 0.f, ksum = 0.f;
     int nk = 0;
 #pragma unroll
     for (int j = 0; j < kMaxK; ++j) {
-      gt[j] = (j < a.k) ? a.topk_gate[t * a.k + j] : 0.f;
       if (j < a.k) {
         all += gt[j];
         if (kept[j]) { ksum += gt[j]; nk += 1; }
@@ -416,6 +416,83 @@ __global__ __launch_bounds__(256) void k_dispatch_small(const DispatchArgs a, co
   }
   for (int64_t r = (int64_t)blockIdx.x * 4 + w; r < g.rows; r += (int64_t)gridDim.x * 4)
     gather_row<16>(g, r, tor_s[r], lane);
+}
+
+__global__ __launch_bounds__(256) void k_dispatch_small(const DispatchArgs a, const GatherArgs g) {
+  const int64_t t = threadIdx.x;
+  const bool valid = t < a.N;
+  int e[kMaxK];
+  float gt[kMaxK];
+  load_experts(a, t, valid, e);
+#pragma unroll
+  for (int j = 0; j < kMaxK; ++j) gt[j] = (valid && j < a.k) ? a.topk_gate[t * a.k + j] : 0.f;
+  dispatch_small_body(a, g, e, gt);
+}
+
+// Route epilogue and dispatch of at most kDispatchTokens tokens in one launch (the layer's
+// forward with bf16 x): every workgroup adds the S split-K partial logits of every token
+// in split order and runs the token epilogue, as k_router_epi does, then dispatches as
+// k_dispatch_small. Workgroup 0 also stores the selection, the gates and the probability
+// block sums, so the results equal those of the separate router and dispatch calls.
+template <int EP>
+__global__ __launch_bounds__(256) void k_route_dispatch_small(const RouterArgs ra, int S, const DispatchArgs a,
+                                                              const GatherArgs g) {
+  __shared__ float l_s[kDispatchTokens][EP + 1];
+  __shared__ float ps_s[EP][kDispatchTokens];
+  const int tid = threadIdx.x;
+  const int E = ra.E;
+  const int64_t items = ra.N * E;
+  const int64_t stride = ra.N * E;  // floats between consecutive splits
+  constexpr int SB = 32;  // splits whose loads are in flight together
+  for (int64_t it = tid; it < items; it += 256) {
+    float v = 0.f;
+    for (int s0 = 0; s0 < S; s0 += SB) {
+      float q[SB];
+#pragma unroll
+      for (int u = 0; u < SB; ++u) q[u] = s0 + u < S ? ra.rpart[(int64_t)(s0 + u) * stride + it] : 0.f;
+#pragma unroll
+      for (int u = 0; u < SB; ++u)
+        if (s0 + u < S) v += q[u];
+    }
+    l_s[it / E][it % E] = v;
+  }
+  __syncthreads();
+  const int64_t t = tid;
+  const bool valid = t < ra.N;
+  int e[kMaxK];
+  float gt[kMaxK];
+#pragma unroll
+  for (int j = 0; j < kMaxK; ++j) { e[j] = -1; gt[j] = 0.f; }
+  {
+    float l[EP], p[EP];
+#pragma unroll
+    for (int x = 0; x < EP; ++x) {
+      l[x] = (valid && x < E) ? l_s[tid][x] + (ra.bias != nullptr ? ra.bias[x] : 0.f) : 0.f;
+      p[x] = 0.f;
+    }
+    if (valid) {
+      route_token(ra, t, l, p, e, gt);
+      if (blockIdx.x == 0) store_topk(ra, t, e, gt);
+    }
+#pragma unroll
+    for (int x = 0; x < EP; ++x) ps_s[x][tid] = valid ? p[x] : 0.f;
+  }
+#pragma unroll
+  for (int j = 0; j < kMaxK; ++j)
+    if (j >= a.k) e[j] = -1;
+  if (ra.psum != nullptr) {
+    __syncthreads();
+    // block sums of the probabilities per kRouterTokens tokens, in token order
+    if (blockIdx.x == 0 && tid < E) {
+      for (int64_t blk = 0; blk * kRouterTokens < ra.N; ++blk) {
+        float sum = 0.f;
+        for (int i = 0; i < kRouterTokens; ++i) sum += ps_s[tid][blk * kRouterTokens + i];
+        ra.psum[blk * E + tid] = sum;
+      }
+    }
+    if (blockIdx.x == 0 && tid == 0 && ra.psum_magic) *ra.psum_magic = kPsumMagic;
+  }
+  dispatch_small_body(a, g, e, gt);
 }
 
 // One wave per expert-buffer row: copy the token's row or write zeros for padding.
@@ -490,6 +567,19 @@ hipError_t launch_dispatch_small(const DispatchArgs& a, const GatherArgs& g, hip
   int64_t grid = (g.rows + 3) / 4;
   grid = grid < 1 ? 1 : (grid > 256 ? 256 : grid);
   hipLaunchKernelGGL(k_dispatch_small, dim3((unsigned)grid), dim3(256), 0, s, a, g);
+  return hipGetLastError();
+}
+
+hipError_t launch_route_dispatch_small(const RouterArgs& ra, const DispatchArgs& a, const GatherArgs& g,
+                                       hipStream_t s) {
+  if (a.N > kDispatchTokens || g.rows > kSmallRows || ra.E > 16 || ra.rpart == nullptr || ra.logits_out != nullptr ||
+      ra.probs_out != nullptr)
+    return hipErrorInvalidValue;
+  const RouterSplit rs = router_split(ra.N, ra.D);
+  int64_t grid = (g.rows + 3) / 4;
+  grid = grid < 1 ? 1 : (grid > 256 ? 256 : grid);
+  if (ra.E <= 8) hipLaunchKernelGGL((k_route_dispatch_small<8>), dim3((unsigned)grid), dim3(256), 0, s, ra, rs.S, a, g);
+  else hipLaunchKernelGGL((k_route_dispatch_small<16>), dim3((unsigned)grid), dim3(256), 0, s, ra, rs.S, a, g);
   return hipGetLastError();
 }
 

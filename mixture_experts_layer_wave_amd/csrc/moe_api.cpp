@@ -87,9 +87,9 @@ T* at(void* base, size_t off) { return reinterpret_cast<T*>(reinterpret_cast<cha
 
 // ---- step bodies (arguments already validated) ----------------------------------------
 
-int do_route(const moe_desc* d, const void* x, const float* w_r, const float* bias, const float* noise,
-             const float* logits_in, float* logits_out, float* probs_out, int32_t* idx, float* gate,
-             void* scratch, hipStream_t st) {
+RouterArgs router_args(const moe_desc* d, const void* x, const float* w_r, const float* bias, const float* noise,
+                       const float* logits_in, float* logits_out, float* probs_out, int32_t* idx, float* gate,
+                       void* scratch) {
   RouterArgs a{};
   a.x = x; a.w_r = w_r; a.bias = bias;
   a.noise = d->second_choice != MOE_SECOND_TOPK ? noise : nullptr;
@@ -103,12 +103,49 @@ int do_route(const moe_desc* d, const void* x, const float* w_r, const float* bi
   }
   a.N = d->N; a.D = (int)d->D; a.E = d->E; a.k = d->k;
   a.mode = d->routing_mode; a.noisy = d->second_choice;
+  return a;
+}
+
+int do_route(const moe_desc* d, const void* x, const float* w_r, const float* bias, const float* noise,
+             const float* logits_in, float* logits_out, float* probs_out, int32_t* idx, float* gate,
+             void* scratch, hipStream_t st) {
+  const RouterArgs a = router_args(d, x, w_r, bias, noise, logits_in, logits_out, probs_out, idx, gate, scratch);
   return status_of(launch_router(a, d->dtype == MOE_DT_BF16, st));
+}
+
+// Router of the forward pass followed by its dispatch. A batch of at most kDispatchTokens
+// tokens with bf16 x (E <= 16, buffer of at most kSmallRows rows) takes two launches: the
+// split-K logit kernel, then one kernel that finishes the routing and dispatches.
+int do_dispatch(const moe_desc* d, const void* x, const int32_t* idx, const float* gate, int32_t* load,
+                int32_t* counts, int32_t* offsets, int32_t* row_of, uint8_t* dropped, float* gate_eff,
+                int32_t* token_of_row, void* x_perm, void* scratch, hipStream_t st,
+                const RouterArgs* route = nullptr);
+
+int do_route_dispatch(const moe_desc* d, const void* x, const float* w_r, const float* bias, const float* noise,
+                      int32_t* idx, float* gate, int32_t* load, int32_t* counts, int32_t* offsets, int32_t* row_of,
+                      uint8_t* dropped, float* gate_eff, int32_t* token_of_row, void* x_perm, void* scratch,
+                      hipStream_t st) {
+  int64_t rows;
+  int rc = rows_of(d, &rows);
+  if (rc) return rc;
+  const RouterArgs ra = router_args(d, x, w_r, bias, noise, nullptr, nullptr, nullptr, idx, gate, scratch);
+  const bool fused = d->dtype == MOE_DT_BF16 && d->N <= kDispatchTokens && rows <= kSmallRows && d->E <= 16 &&
+                     d->D % kRouterChunk == 0 && ra.rpart != nullptr;
+  if (!fused) {
+    rc = status_of(launch_router(ra, d->dtype == MOE_DT_BF16, st));
+    if (rc) return rc;
+    return do_dispatch(d, x, idx, gate, load, counts, offsets, row_of, dropped, gate_eff, token_of_row, x_perm,
+                       scratch, st);
+  }
+  rc = status_of(launch_router_split(ra, st));
+  if (rc) return rc;
+  return do_dispatch(d, x, idx, gate, load, counts, offsets, row_of, dropped, gate_eff, token_of_row, x_perm, scratch,
+                     st, &ra);
 }
 
 int do_dispatch(const moe_desc* d, const void* x, const int32_t* idx, const float* gate, int32_t* load,
                 int32_t* counts, int32_t* offsets, int32_t* row_of, uint8_t* dropped, float* gate_eff,
-                int32_t* token_of_row, void* x_perm, void* scratch, hipStream_t st) {
+                int32_t* token_of_row, void* x_perm, void* scratch, hipStream_t st, const RouterArgs* route) {
   int64_t C, rows;
   int rc = capacity_of(d, &C);
   if (rc) return rc;
@@ -132,6 +169,7 @@ int do_dispatch(const moe_desc* d, const void* x, const int32_t* idx, const floa
   g.x = x; g.token_of_row = token_of_row; g.counts = counts; g.x_perm = x_perm;
   g.rows = rows; g.N = d->N; g.D = (int)d->D; g.elem_bytes = (int)esize(d);
   g.C = padded ? C : -1; g.padded = padded;
+  if (route != nullptr) return status_of(launch_route_dispatch_small(*route, a, g, st));
   if (d->N <= kDispatchTokens && rows <= kSmallRows) return status_of(launch_dispatch_small(a, g, st));
   hipError_t e = launch_dispatch(a, st);
   if (e != hipSuccess) return MOE_E_HIP;
@@ -408,13 +446,10 @@ static int forward_impl(const moe_desc* d, const void* x, const float* w_r, cons
   if (workspace_bytes < L.total) return MOE_E_WORKSPACE;
   hipStream_t st = (hipStream_t)stream;
   void* ws = workspace;
-  rc = do_route(d, x, w_r, logit_bias, noise, nullptr, nullptr, nullptr, at<int32_t>(ws, L.topk_idx),
-                at<float>(ws, L.topk_gate), at<void>(ws, L.scratch), st);
-  if (rc) return rc;
-  rc = do_dispatch(d, x, at<int32_t>(ws, L.topk_idx), at<float>(ws, L.topk_gate), at<int32_t>(ws, L.load),
-                   at<int32_t>(ws, L.counts), at<int32_t>(ws, L.offsets), at<int32_t>(ws, L.row_of),
-                   at<uint8_t>(ws, L.dropped), at<float>(ws, L.gate_eff), at<int32_t>(ws, L.token_of_row),
-                   at<void>(ws, L.x_perm), at<void>(ws, L.scratch), st);
+  rc = do_route_dispatch(d, x, w_r, logit_bias, noise, at<int32_t>(ws, L.topk_idx), at<float>(ws, L.topk_gate),
+                         at<int32_t>(ws, L.load), at<int32_t>(ws, L.counts), at<int32_t>(ws, L.offsets),
+                         at<int32_t>(ws, L.row_of), at<uint8_t>(ws, L.dropped), at<float>(ws, L.gate_eff),
+                         at<int32_t>(ws, L.token_of_row), at<void>(ws, L.x_perm), at<void>(ws, L.scratch), st);
   if (rc) return rc;
   rc = do_ffn(d, at<void>(ws, L.x_perm), at<int32_t>(ws, L.offsets), at<int32_t>(ws, L.counts), w1, w2, w3,
               at<void>(ws, L.h), at<void>(ws, L.y_perm), at<void>(ws, L.scratch), 3, st, sc);

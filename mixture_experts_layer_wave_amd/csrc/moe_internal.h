@@ -95,6 +95,9 @@ struct RouterArgs {
   int noisy;  // MOE_SECOND_*: 1 = noise on slots >= 1, 2 = noise replaces the logits
 };
 hipError_t launch_router(const RouterArgs& a, bool bf16_x, hipStream_t s);
+// Only the split-K logit kernel (bf16 x): partial logits [S][N][E] in a.rpart, S from
+// router_split(N, D); the epilogue is left to the caller.
+hipError_t launch_router_split(const RouterArgs& a, hipStream_t s);
 
 // ---- dispatch -----------------------------------------------------------------------
 struct DispatchArgs {
@@ -131,6 +134,10 @@ struct GatherArgs {
 };
 hipError_t launch_gather(const GatherArgs& a, hipStream_t s);
 hipError_t launch_dispatch_small(const DispatchArgs& a, const GatherArgs& g, hipStream_t s);
+// Router epilogue (from the split-K partial logits in ra.rpart) and dispatch in one launch:
+// N <= kDispatchTokens, rows <= kSmallRows, E <= 16, no logits/probs outputs.
+hipError_t launch_route_dispatch_small(const RouterArgs& ra, const DispatchArgs& a, const GatherArgs& g,
+                                       hipStream_t s);
 
 struct StatsArgs {
   const float* psum;

@@ -1,0 +1,106 @@
+// route_token.h: the router's per-token epilogue (softmax, selection, gates), shared by
+// the router kernels and the fused small-batch route + dispatch kernel.
+// (Internal header of the HIP library; not part of the C ABI.)
+//
+// Method ("第 5 章 model.py 精读·中：MoE 路由与专家", §5.2, §5.2.1, §5.2.2, §5.2.3; "MoE 公式到源码
+// 对照" §1.1-1.2; "8.1 MoE 系列" §3 for the GShard noisy second choice).
+#pragma once
+
+#include "moe_device.h"
+#include "moe_internal.h"
+
+namespace moe {
+
+template <int EP>
+__device__ __forceinline__ float pick(const float (&v)[EP], int i) {
+  float r = 0.f;
+#pragma unroll
+  for (int e = 0; e < EP; ++e) r = (e == i) ? v[e] : r;
+  return r;
+}
+
+// Epilogue of one token t < N from its logits l (bias included): noisy top-k gating,
+// softmax into p, optional logits/probs outputs, the k selected experts (sel, slot 0
+// first) and their gates (gt).
+template <int EP>
+__device__ __forceinline__ void route_token(const RouterArgs& a, int64_t t, float (&l)[EP], float (&p)[EP],
+                                            int (&sel)[kMaxK], float (&gt)[kMaxK]) {
+  const int E = a.E;
+  if (a.noisy == 2) {
+#pragma unroll
+    for (int e = 0; e < EP; ++e)
+      if (e < E) l[e] += a.noise[t * E + e];  // logit' = fl32(logit + noise)
+  }
+  float mx = l[0];
+#pragma unroll
+  for (int e = 1; e < EP; ++e) mx = (e < E) ? fmaxf(mx, l[e]) : mx;
+  float sum = 0.f;
+#pragma unroll
+  for (int e = 0; e < EP; ++e) {
+    p[e] = (e < E) ? expf(l[e] - mx) : 0.f;
+    sum += p[e];
+  }
+#pragma unroll
+  for (int e = 0; e < EP; ++e) p[e] = p[e] / sum;
+
+  if (a.logits_out) for (int e = 0; e < E; ++e) a.logits_out[t * E + e] = pick(l, e);
+  if (a.probs_out) for (int e = 0; e < E; ++e) a.probs_out[t * E + e] = pick(p, e);
+
+  // noisy values for slots >= 1 (GShard random routing)
+  float z[EP];
+#pragma unroll
+  for (int e = 0; e < EP; ++e) z[e] = l[e];
+  if (a.noisy == 1) {
+#pragma unroll
+    for (int e = 0; e < EP; ++e) z[e] = (e < E) ? l[e] + a.noise[t * E + e] : 0.f;
+  }
+
+  uint64_t chosen = 0;
+#pragma unroll
+  for (int j = 0; j < kMaxK; ++j) {
+    sel[j] = 0;
+    if (j < a.k) {
+      const bool use_z = (j > 0) && a.noisy == 1;
+      int best = -1;
+      float bv = 0.f;
+#pragma unroll
+      for (int e = 0; e < EP; ++e) {
+        const float v = use_z ? z[e] : l[e];
+        const bool cand = (e < E) && !((chosen >> e) & 1ull);
+        if (cand && (best < 0 || v > bv)) { best = e; bv = v; }
+      }
+      sel[j] = best;
+      chosen |= 1ull << best;
+    }
+  }
+
+  if (a.mode == 0) {
+#pragma unroll
+    for (int j = 0; j < kMaxK; ++j) gt[j] = (j < a.k) ? pick(p, sel[j]) : 0.f;
+  } else {
+    const float ref = pick(l, sel[0]);
+    float s2 = 0.f;
+#pragma unroll
+    for (int j = 0; j < kMaxK; ++j) {
+      gt[j] = (j < a.k) ? expf(pick(l, sel[j]) - ref) : 0.f;
+      s2 += gt[j];
+    }
+#pragma unroll
+    for (int j = 0; j < kMaxK; ++j) gt[j] = gt[j] / s2;
+  }
+}
+
+// Stores the selection and gates of token t.
+__device__ __forceinline__ void store_topk(const RouterArgs& a, int64_t t, const int (&sel)[kMaxK],
+                                           const float (&gt)[kMaxK]) {
+#pragma unroll
+  for (int j = 0; j < kMaxK; ++j) {
+    if (j < a.k) {
+      a.topk_idx[t * a.k + j] = sel[j];
+      a.topk_gate[t * a.k + j] = gt[j];
+    }
+  }
+}
+
+
+}  // namespace moe

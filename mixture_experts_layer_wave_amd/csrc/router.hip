@@ -25,6 +25,7 @@
 //    partial blocks meet in LDS and are added in wave order before the epilogue.
 #include "moe_device.h"
 #include "moe_internal.h"
+#include "route_token.h"
 
 namespace moe {
 namespace {
@@ -32,92 +33,6 @@ namespace {
 constexpr int kTM = kRouterTokens;  // tokens per single-pass workgroup (32)
 constexpr int kWaves = 8;
 constexpr int kKC = 32;             // K chunk per pipeline step of the single-pass path
-
-template <int EP>
-__device__ __forceinline__ float pick(const float (&v)[EP], int i) {
-  float r = 0.f;
-#pragma unroll
-  for (int e = 0; e < EP; ++e) r = (e == i) ? v[e] : r;
-  return r;
-}
-
-// Epilogue of one token t < N from its logits l (bias included): noisy top-k gating,
-// softmax into p, optional logits/probs outputs, selection and gates.
-template <int EP>
-__device__ __forceinline__ void route_token(const RouterArgs& a, int64_t t, float (&l)[EP], float (&p)[EP]) {
-  const int E = a.E;
-  if (a.noisy == 2) {
-#pragma unroll
-    for (int e = 0; e < EP; ++e)
-      if (e < E) l[e] += a.noise[t * E + e];  // logit' = fl32(logit + noise)
-  }
-  float mx = l[0];
-#pragma unroll
-  for (int e = 1; e < EP; ++e) mx = (e < E) ? fmaxf(mx, l[e]) : mx;
-  float sum = 0.f;
-#pragma unroll
-  for (int e = 0; e < EP; ++e) {
-    p[e] = (e < E) ? expf(l[e] - mx) : 0.f;
-    sum += p[e];
-  }
-#pragma unroll
-  for (int e = 0; e < EP; ++e) p[e] = p[e] / sum;
-
-  if (a.logits_out) for (int e = 0; e < E; ++e) a.logits_out[t * E + e] = pick(l, e);
-  if (a.probs_out) for (int e = 0; e < E; ++e) a.probs_out[t * E + e] = pick(p, e);
-
-  // noisy values for slots >= 1 (GShard random routing)
-  float z[EP];
-#pragma unroll
-  for (int e = 0; e < EP; ++e) z[e] = l[e];
-  if (a.noisy == 1) {
-#pragma unroll
-    for (int e = 0; e < EP; ++e) z[e] = (e < E) ? l[e] + a.noise[t * E + e] : 0.f;
-  }
-
-  int sel[kMaxK];
-  uint64_t chosen = 0;
-#pragma unroll
-  for (int j = 0; j < kMaxK; ++j) {
-    sel[j] = 0;
-    if (j < a.k) {
-      const bool use_z = (j > 0) && a.noisy == 1;
-      int best = -1;
-      float bv = 0.f;
-#pragma unroll
-      for (int e = 0; e < EP; ++e) {
-        const float v = use_z ? z[e] : l[e];
-        const bool cand = (e < E) && !((chosen >> e) & 1ull);
-        if (cand && (best < 0 || v > bv)) { best = e; bv = v; }
-      }
-      sel[j] = best;
-      chosen |= 1ull << best;
-    }
-  }
-
-  float gt[kMaxK];
-  if (a.mode == 0) {
-#pragma unroll
-    for (int j = 0; j < kMaxK; ++j) gt[j] = (j < a.k) ? pick(p, sel[j]) : 0.f;
-  } else {
-    const float ref = pick(l, sel[0]);
-    float s2 = 0.f;
-#pragma unroll
-    for (int j = 0; j < kMaxK; ++j) {
-      gt[j] = (j < a.k) ? expf(pick(l, sel[j]) - ref) : 0.f;
-      s2 += gt[j];
-    }
-#pragma unroll
-    for (int j = 0; j < kMaxK; ++j) gt[j] = gt[j] / s2;
-  }
-#pragma unroll
-  for (int j = 0; j < kMaxK; ++j) {
-    if (j < a.k) {
-      a.topk_idx[t * a.k + j] = sel[j];
-      a.topk_gate[t * a.k + j] = gt[j];
-    }
-  }
-}
 
 // ---- single-pass path --------------------------------------------------------------
 
@@ -245,7 +160,12 @@ __global__ __launch_bounds__(512) void k_router(const RouterArgs a) {
       }
       l[e] = v;
     }
-    if (valid) route_token(a, t, l, p);
+    if (valid) {
+      int sel[kMaxK];
+      float gt[kMaxK];
+      route_token(a, t, l, p, sel, gt);
+      store_topk(a, t, sel, gt);
+    }
     if (a.psum) {
 #pragma unroll
       for (int e = 0; e < EP; ++e) ps_s[e][lane] = valid ? p[e] : 0.f;
@@ -438,7 +358,12 @@ __global__ __launch_bounds__(256) void k_router_epi(const RouterArgs a, RouterSp
       l[e] = (valid && e < E) ? l_s[tid][e] + (a.bias != nullptr ? a.bias[e] : 0.f) : 0.f;
       p[e] = 0.f;
     }
-    if (valid) route_token(a, t, l, p);
+    if (valid) {
+      int sel[kMaxK];
+      float gt[kMaxK];
+      route_token(a, t, l, p, sel, gt);
+      store_topk(a, t, sel, gt);
+    }
 #pragma unroll
     for (int e = 0; e < EP; ++e) ps_s[e][tid] = valid ? p[e] : 0.f;
   }
@@ -477,6 +402,15 @@ hipError_t launch_ep(const RouterArgs& a, bool bf16_x, hipStream_t s) {
 }
 
 }  // namespace
+
+hipError_t launch_router_split(const RouterArgs& a, hipStream_t s) {
+  if (a.rpart == nullptr || a.logits_in != nullptr || a.D % kRouterChunk != 0) return hipErrorInvalidValue;
+  const RouterSplit rs = router_split(a.N, a.D);
+  const dim3 grid((unsigned)(rs.tiles * rs.S));
+  if (a.E <= 32) hipLaunchKernelGGL((k_router_split<1>), grid, dim3(512), 0, s, a, rs);
+  else hipLaunchKernelGGL((k_router_split<2>), grid, dim3(512), 0, s, a, rs);
+  return hipGetLastError();
+}
 
 hipError_t launch_router(const RouterArgs& a, bool bf16_x, hipStream_t s) {
   if (a.E <= 8) return launch_ep<1, 8>(a, bf16_x, s);

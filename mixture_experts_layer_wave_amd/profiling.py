@@ -68,7 +68,8 @@ def stage_of(name: str) -> str:
     base, args = parse_kernel(name)
     if base in ("k_router", "k_router_split", "k_router_epi"):
         return "route"
-    if base in ("k_dispatch_count", "k_dispatch_scan", "k_dispatch_assign", "k_gather", "k_dispatch_small"):
+    if base in ("k_dispatch_count", "k_dispatch_scan", "k_dispatch_assign", "k_gather", "k_dispatch_small",
+                "k_route_dispatch_small"):
         return "dispatch"
     if base in ("k_gemm_bf16", "k_gemm_tail_reduce", "k_gemm_streamk_reduce") and len(args) >= 3:
         return "expert_up" if args[2] == 2 else "expert_down"

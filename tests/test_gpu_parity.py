@@ -388,10 +388,18 @@ def test_layer_mid_size(orc, cfg):
     _check_layer(orc, cfg)
 
 
-@pytest.mark.parametrize("cfg", [configs.scaled_config("gshard_capacity", N=1000, D=256, F=384, E=16),
-                                 configs.scaled_config("gshard_capacity", N=1000, D=256, F=384, E=16,
-                                                       weight_dtype="int8", name="gshard_int8")],
-                         ids=lambda c: c["name"])
+@pytest.mark.parametrize("cfg", [
+    configs.scaled_config("gshard_capacity", N=1000, D=256, F=384, E=16),
+    configs.scaled_config("gshard_capacity", N=1000, D=256, F=384, E=16, weight_dtype="int8", name="gshard_int8"),
+    # at most 256 tokens, E <= 16, bf16: the forward finishes the routing inside the dispatch kernel
+    configs.scaled_config("mixtral_decode", N=64, D=512, F=384),
+    configs.scaled_config("mixtral_decode_int8", N=64, D=512, F=384),
+    configs.scaled_config("gshard_capacity", N=200, D=256, F=384, E=16, name="gshard_small"),
+    configs.scaled_config("switch_top1", N=150, D=256, F=384, name="switch_small"),
+    configs.scaled_config("mixtral_prefill", N=256, D=256, F=256, routing_mode="softmax_topk", activation="gelu_erf",
+                          name="prefill_256"),
+    configs.scaled_config("mixtral_prefill", N=257, D=256, F=256, name="prefill_257"),
+], ids=lambda c: c["name"])
 def test_layer_bitwise_reproducible_and_equal_to_steps(orc, cfg):
     inp = inputs.make_inputs(cfg)
     layer = B.MoELayer(cfg, inp)
@@ -414,6 +422,16 @@ def test_layer_bitwise_reproducible_and_equal_to_steps(orc, cfg):
     B.moe_combine(d, yp, out["row_of"], out["gate_eff"], y3)
     torch.cuda.synchronize()
     assert torch.equal(y1, y3)
+    # the forward's routing and dispatch intermediates equal the separate calls' bit for bit
+    v = layer.views()
+    assert torch.equal(v["topk_idx"], idx) and torch.equal(v["topk_gate"], gate)
+    for name in ("load", "counts", "offsets", "row_of", "dropped", "gate_eff", "token_of_row", "x_perm"):
+        assert torch.equal(v[name], out[name]), name
+    # and so do the statistics (probability block sums from the router, counts from dispatch)
+    B.moe_dispatch(d, layer.x, idx, gate, out["load"], out["counts"], out["offsets"], out["row_of"], out["dropped"],
+                   out["gate_eff"], out["token_of_row"], out["x_perm"], sc)
+    torch.cuda.synchronize()
+    assert layer.stats() == B.moe_read_stats(d, sc)
 
 
 @pytest.mark.parametrize("cfg", [configs.scaled_config("gshard_capacity", N=1000, D=256, F=384, E=16),
