@@ -40,6 +40,7 @@ def parse():
     p.add_argument("--workload", default="mixtral_prefill")
     p.add_argument("--cpu-sample", type=int, default=2048, help="tokens in the oracle's timed FFN sample")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-graph", action="store_true", help="skip the HIP-graph replay measurement")
     p.add_argument("--cold-reps", type=int, default=5,
                    help="cold-cache runs of each small stage before the warm-up (0: none)")
     p.add_argument("--copy-mib", type=int, default=0,
@@ -224,6 +225,30 @@ def main():
     torch.cuda.synchronize()
     staged_ms_per_step = (time.perf_counter() - ts0) / args.steps * 1e3
 
+    # The same forward captured once in a HIP graph and replayed K times (launch overhead
+    # of the individual kernels removed); reported beside the eager throughput.
+    graph = None
+    if not args.no_graph:
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            layer.forward()
+        stream.wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            layer.forward()
+        for _ in range(args.warmup):
+            g.replay()
+        torch.cuda.synchronize()
+        tg0 = time.perf_counter()
+        for _ in range(args.steps):
+            g.replay()
+        torch.cuda.synchronize()
+        gms = (time.perf_counter() - tg0) / args.steps * 1e3
+        graph = {"ms_per_step": gms, "tokens_per_s": N / (gms * 1e-3)}
+        del g
+
     stage_t = {s: np.array([events[i][j].elapsed_time(events[i][j + 1]) for i in range(args.steps)])
                for j, s in enumerate(STAGES)}
     stage_ms = {s: float(np.mean(t)) for s, t in stage_t.items()}
@@ -278,6 +303,7 @@ def main():
                          "accepted_rows": A, "active_experts": active},
         "forward_ms": forward_ms,
         "staged_ms_per_step": staged_ms_per_step,
+        "graph_replay": graph,
         "stages_ms": stage_ms,
         "stages_ms_pct": stage_pct,
         "stages_ms_cold": cold_ms,
