@@ -27,6 +27,8 @@
 //    XCD's L2. The last partial round is split along K; a fix-up kernel sums the pieces in
 //    a fixed order. With at most 64 rows per expert (decode), 64-row tiles and stream-K
 //    spread the weight stream evenly over all compute units.
+#include <type_traits>
+
 #include "gemm_common.h"
 
 namespace moe {
@@ -393,11 +395,13 @@ __global__ __launch_bounds__(512, 1) void k_gemm_bf16(const GemmParams p) {
     }
 
     const int nku = ke - kb;  // K slices of this unit
-    auto issue_slice = [&](int kt) {
+    auto issue_slice = [&](int kt, bool with_a) {
       const int k0 = (kb + kt) * BK;
       const int base = ring_addr + (kt % STAGES) * STAGE * 2;
+      if (with_a) {
 #pragma unroll
-      for (int q = 0; q < A_CP; ++q) load_lds16(a_src[q] + k0, (uint32_t)uniform(base + (A_CP * wid + q) * 1024));
+        for (int q = 0; q < A_CP; ++q) load_lds16(a_src[q] + k0, (uint32_t)uniform(base + (A_CP * wid + q) * 1024));
+      }
 #pragma unroll
       for (int q = 0; q < B_CP; ++q)
         load_lds16(b_src[q] + (int64_t)k0 * N * WB, (uint32_t)uniform(base + A_EL * 2 + (B_CP * wid + q) * 1024));
@@ -413,15 +417,26 @@ __global__ __launch_bounds__(512, 1) void k_gemm_bf16(const GemmParams p) {
 #pragma unroll
           for (int r = 0; r < 16; ++r) acc[m][i][j][r] = 0.f;
 
+    // K loop, in two copies. The plain one serves every tile but one kind: the only m-tile
+    // of an expert with fewer than BM rows (common with many small experts). In its copy, a
+    // wave whose A copies cover no valid row skips them and a wave whose accumulator rows
+    // all lie past the count skips its LDS reads and MFMAs; the stale LDS rows feed only
+    // accumulator rows that are never stored.
+    auto k_loop = [&](auto lone_tile) {
+      constexpr bool LONE = decltype(lone_tile)::value;
+      const bool a_live = !LONE || A_RPC * A_CP * wid < tl.mcount;
+      const bool c_live = !LONE || wm * WM < tl.mcount;
 #pragma unroll
     for (int st = 0; st < STAGES - 1; ++st)
-      if (st < nku) issue_slice(st);
+      if (st < nku) issue_slice(st, a_live);
 
     for (int kt = 0; kt < nku; ++kt) {
-      // Slice kt has landed once at most (slices issued after it) * LOADS copies remain.
-      wait_for_slice<LOADS>(min(STAGES - 2, nku - 1 - kt));
+      // Slice kt has landed once at most (slices issued after it) * (copies per slice) remain.
+      if (a_live) wait_for_slice<LOADS>(min(STAGES - 2, nku - 1 - kt));
+      else wait_for_slice<B_CP>(min(STAGES - 2, nku - 1 - kt));
       barrier_no_fence();  // slice kt visible to every wave; slice kt-1 fully consumed
-      if (kt + STAGES - 1 < nku) issue_slice(kt + STAGES - 1);
+      if (kt + STAGES - 1 < nku) issue_slice(kt + STAGES - 1, a_live);
+      if (!c_live) continue;
 
       const bf16* As = ring + (kt % STAGES) * STAGE;
       bf16x8 af[BK / 16][TM], bfr[BK / 16][NB][TN];
@@ -455,6 +470,13 @@ __global__ __launch_bounds__(512, 1) void k_gemm_bf16(const GemmParams p) {
 #pragma unroll
             for (int i = 0; i < TM; ++i)
               acc[m][i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[kk][m][j], af[kk][i], acc[m][i][j], 0, 0, 0);
+    }
+    };
+    if constexpr (STREAMK) {
+      k_loop(std::false_type{});
+    } else {
+      if (tl.m0 == 0 && tl.mcount < BM) k_loop(std::true_type{});
+      else k_loop(std::false_type{});
     }
     wait_vmcnt<0>();
     __syncthreads();  // every wave done reading the ring before the next tile refills it
