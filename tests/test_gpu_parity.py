@@ -542,3 +542,11 @@ def test_workload_grok1_layer(orc):
     res = _check_layer(orc, cfg, sample=_spread(cfg["N"], 12, extra=(8191,)))
     gsum = host(res["layer"].views()["topk_gate"]).sum(axis=1)
     assert np.all(gsum < 1.0)
+
+
+@pytest.mark.slow
+def test_mixtral_shape_eight_times_the_batch(orc):
+    # N = 32768 tokens (65536 rows, ~126 persistent rounds of the up-projection, buffers of
+    # 0.5-1.9 GB): schedule, row offsets and scratch at the largest batch tested here.
+    cfg = configs.scaled_config("mixtral_prefill", N=32768, D=4096, F=14336, name="mixtral_prefill_n32768")
+    _check_layer(orc, cfg, sample=_spread(cfg["N"], 10, extra=(1, 32767)))
