@@ -30,7 +30,7 @@ from collections import defaultdict
 PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 
-STAGE_ORDER = ["route", "dispatch", "expert_up", "expert_down", "expert_ffn", "combine", "stats", "other"]
+STAGE_ORDER = ["route", "dispatch", "expert_up", "expert_down", "expert_ffn", "combine", "stats", "forward", "other"]
 
 
 def source_hash() -> str:
@@ -68,9 +68,10 @@ def stage_of(name: str) -> str:
     base, args = parse_kernel(name)
     if base in ("k_router", "k_router_split", "k_router_epi"):
         return "route"
-    if base in ("k_dispatch_count", "k_dispatch_scan", "k_dispatch_assign", "k_gather", "k_dispatch_small",
-                "k_route_dispatch_small"):
+    if base in ("k_dispatch_count", "k_dispatch_scan", "k_dispatch_assign", "k_gather", "k_dispatch_small"):
         return "dispatch"
+    if base == "k_route_dispatch_small":  # launched by moe_forward only (route epilogue + dispatch)
+        return "forward"
     if base in ("k_gemm_bf16", "k_gemm_tail_reduce", "k_gemm_streamk_reduce") and len(args) >= 3:
         return "expert_up" if args[2] == 2 else "expert_down"
     if base == "k_gemm_f32":
@@ -137,8 +138,9 @@ def cmd_stats(a):
     stage, stage_last = defaultdict(float), defaultdict(float)
     lines = [f"# Kernel durations: {a.title}", "", "Command:", "", "```", a.cmd, "```", "",
              f"Kernel sources hash: `{source_hash()}`", "",
-             f"`avg` is over every call (warm-up included); `timed avg` over the last {a.last} calls, the "
-             "timed steps of the run." if a.last else "", "",
+             f"`avg` is over every call (warm-up included); `timed avg` over the last {a.last} calls: for the "
+             "stage kernels, the per-stage loop of bench.py whose HIP events give `bench events` below "
+             "(kernels that only moe_forward launches: its timed loop)." if a.last else "", "",
              "| kernel | stage | calls | avg us | timed avg us | min us | max us | grid x wg | vgpr+agpr | lds B |",
              "|---|---|---:|---:|---:|---:|---:|---|---|---:|"]
     for r in sorted(rows, key=lambda r: STAGE_ORDER.index(stage_of(r["name"]))):
@@ -146,12 +148,13 @@ def cmd_stats(a):
         tl, inf = last.get(r["name"], (float("nan"), ("", "", "", "", "", "")))
         lines.append(f"| `{short_name(r['name'])}` | {st} | {r['calls']} | {r['avg_us']:.2f} | {tl:.2f} | "
                      f"{r['min_us']:.2f} | {r['max_us']:.2f} | {inf[0]} x {inf[1]} | {inf[2]}+{inf[3]} | {inf[4]} |")
-        if st != "other":
+        if st not in ("other", "forward"):
             stage[st] += r["avg_us"]
             stage_last[st] += tl
     bench = bench_stages(a.bench_log) if a.bench_log else None
-    lines += ["", "Per-stage sums (each kernel is called once per step). `bench events` is what bench.py "
-              "measured for the stage with HIP events on the launch stream in the same run.", "",
+    lines += ["", "Per-stage sums of the per-stage entry points' kernels (stage `forward`: kernels that only "
+              "moe_forward launches, not summed). `bench events` is what bench.py measured for the stage with "
+              "HIP events on the launch stream in the same run.", "",
               "| stage | avg us | timed avg us | bench events us |", "|---|---:|---:|---:|"]
     for st in STAGE_ORDER:
         if st in stage:
