@@ -27,6 +27,8 @@
 //    XCD's L2. The last partial round is split along K; a fix-up kernel sums the pieces in
 //    a fixed order. With at most 64 rows per expert (decode), 64-row tiles and stream-K
 //    spread the weight stream evenly over all compute units.
+//  * The only m-tile of an expert with fewer than BM rows runs a copy of the K loop in
+//    which waves whose rows all lie past the expert's count skip their copies and MFMAs.
 #include <type_traits>
 
 #include "gemm_common.h"
