@@ -33,12 +33,19 @@ CSRC = os.path.join(PKG, "csrc")
 STAGE_ORDER = ["route", "dispatch", "expert_up", "expert_down", "expert_ffn", "combine", "stats", "forward", "other"]
 
 
+def _code_only(text: str) -> str:
+    """Source text without comments and blank space (a comment edit changes no kernel)."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def source_hash() -> str:
-    """Hash of every file of the kernel sources (names + contents)."""
+    """Hash of the kernel sources' code (file names + text without comments)."""
     h = hashlib.sha256()
     for name in sorted(os.listdir(CSRC)):
-        with open(os.path.join(CSRC, name), "rb") as f:
-            h.update(name.encode() + f.read())
+        with open(os.path.join(CSRC, name), encoding="utf-8") as f:
+            h.update(name.encode() + _code_only(f.read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -80,3 +80,11 @@ def test_configs_scaled_names_and_fields():
         g = configs.get_config(name)
         assert g["D"] % 64 == 0 and g["F"] % 64 == 0 and 1 <= g["k"] <= g["E"]
     assert np.isclose(configs.get_config("gshard_capacity")["capacity_factor"], 1.25)
+
+
+def test_source_hash_ignores_comments_only():
+    a = "int f(int x) { return x + 1; }  // add one\n/* block\n comment */"
+    b = "int f(int x) {\n  return x + 1;\n}"
+    c = "int f(int x) { return x + 2; }"
+    assert profiling._code_only(a) == profiling._code_only(b)
+    assert profiling._code_only(a) != profiling._code_only(c)
