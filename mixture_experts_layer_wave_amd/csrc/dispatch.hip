@@ -471,7 +471,7 @@ __global__ __launch_bounds__(256) void k_route_dispatch_small(const RouterArgs r
       p[x] = 0.f;
     }
     if (valid) {
-      route_token(ra, t, l, p, e, gt);
+      route_token(ra, t, ra.noise != nullptr ? ra.noise + t * E : nullptr, l, p, e, gt);
       if (blockIdx.x == 0) store_topk(ra, t, e, gt);
     }
 #pragma unroll

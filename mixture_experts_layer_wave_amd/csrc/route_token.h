@@ -21,15 +21,16 @@ __device__ __forceinline__ float pick(const float (&v)[EP], int i) {
 
 // Epilogue of one token t < N from its logits l (bias included): noisy top-k gating,
 // softmax into p, optional logits/probs outputs, the k selected experts (sel, slot 0
-// first) and their gates (gt).
+// first) and their gates (gt). nz: the token's E noise values (a.noise row t, or a copy
+// of it), unused without noise.
 template <int EP>
-__device__ __forceinline__ void route_token(const RouterArgs& a, int64_t t, float (&l)[EP], float (&p)[EP],
-                                            int (&sel)[kMaxK], float (&gt)[kMaxK]) {
+__device__ __forceinline__ void route_token(const RouterArgs& a, int64_t t, const float* nz, float (&l)[EP],
+                                            float (&p)[EP], int (&sel)[kMaxK], float (&gt)[kMaxK]) {
   const int E = a.E;
   if (a.noisy == 2) {
 #pragma unroll
     for (int e = 0; e < EP; ++e)
-      if (e < E) l[e] += a.noise[t * E + e];  // logit' = fl32(logit + noise)
+      if (e < E) l[e] += nz[e];  // logit' = fl32(logit + noise)
   }
   float mx = l[0];
 #pragma unroll
@@ -52,7 +53,7 @@ __device__ __forceinline__ void route_token(const RouterArgs& a, int64_t t, floa
   for (int e = 0; e < EP; ++e) z[e] = l[e];
   if (a.noisy == 1) {
 #pragma unroll
-    for (int e = 0; e < EP; ++e) z[e] = (e < E) ? l[e] + a.noise[t * E + e] : 0.f;
+    for (int e = 0; e < EP; ++e) z[e] = (e < E) ? l[e] + nz[e] : 0.f;
   }
 
   uint64_t chosen = 0;

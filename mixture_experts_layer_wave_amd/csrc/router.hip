@@ -163,7 +163,7 @@ __global__ __launch_bounds__(512) void k_router(const RouterArgs a) {
     if (valid) {
       int sel[kMaxK];
       float gt[kMaxK];
-      route_token(a, t, l, p, sel, gt);
+      route_token(a, t, a.noise != nullptr ? a.noise + t * E : nullptr, l, p, sel, gt);
       store_topk(a, t, sel, gt);
     }
     if (a.psum) {
@@ -318,6 +318,7 @@ template <int EP>
 __global__ __launch_bounds__(256) void k_router_epi(const RouterArgs a, RouterSplit rs) {
   __shared__ float l_s[64][EP + 1];
   __shared__ float ps_s[EP][64];
+  __shared__ float nz_s[64][EP];  // the 64 tokens' noise rows (coalesced copy)
   const int tid = threadIdx.x;
   const int E = a.E;
   const int64_t t0 = (int64_t)blockIdx.x * 64;
@@ -348,6 +349,8 @@ __global__ __launch_bounds__(256) void k_router_epi(const RouterArgs a, RouterSp
     const int i = tid + 256 * j;
     if (i < nitem) l_s[i / E][i % E] = v[j];
   }
+  if (a.noise != nullptr)
+    for (int i = tid; i < nitem; i += 256) nz_s[i / E][i % E] = a.noise[t0 * E + i];
   __syncthreads();
   if (tid < 64) {  // wave 0: one token per lane
     const int64_t t = t0 + tid;
@@ -361,7 +364,7 @@ __global__ __launch_bounds__(256) void k_router_epi(const RouterArgs a, RouterSp
     if (valid) {
       int sel[kMaxK];
       float gt[kMaxK];
-      route_token(a, t, l, p, sel, gt);
+      route_token(a, t, nz_s[tid], l, p, sel, gt);
       store_topk(a, t, sel, gt);
     }
 #pragma unroll
