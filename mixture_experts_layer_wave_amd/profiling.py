@@ -6,6 +6,10 @@ Two commands, both reading the CSV files that ``rocprofv3 --output-format csv`` 
             kernel's calls and average duration, plus per-stage sums (a stage is one call
             of the C ABI, e.g. the gated up-projection = its GEMM kernel + its split-K or
             stream-K fix-up kernel).
+``mfma``    one counter run of the derived metrics MfmaUtil (SQ_VALU_MFMA_BUSY_CYCLES over
+            GRBM_GUI_ACTIVE x SIMDs) and MfmaFlopsBF16 (SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512):
+            per kernel with matrix-core work, the busy percentage and the bf16 flops it
+            executed per dispatch, next to the useful flops of the stage when given.
 ``traffic`` two counter runs (``FETCH_SIZE`` and ``WRITE_SIZE``, KiB per dispatch) of the
             bench, and the same two counters for a plain device copy of known size. The
             copy gives the factor that turns counter KiB into bytes actually moved
@@ -187,6 +191,32 @@ def counter_avgs(counter_csv: str, counter: str):
     return {k: tot[k] / len(disp[k]) for k in tot}
 
 
+def cmd_mfma(a):
+    csv_path = _one(os.path.join(a.dir, "**", "*counter_collection.csv"))
+    util = counter_avgs(csv_path, "MfmaUtil")
+    flops = counter_avgs(csv_path, "MfmaFlopsBF16")
+    useful = dict(kv.split("=") for kv in a.useful) if a.useful else {}
+    lines = [f"# Matrix-core counters: {a.title}", "", "Command:", "", "```", a.cmd, "```", "",
+             f"Kernel sources hash: `{source_hash()}`", "",
+             "Averages per dispatch over every call of the run. `MfmaUtil` = SQ_VALU_MFMA_BUSY_CYCLES / "
+             "(GRBM_GUI_ACTIVE x SIMDs) x 100; `bf16 flops` = SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512 (all MFMAs "
+             "issued, padding rows of partial tiles included); `useful` = the stage's algorithmic flops.", "",
+             "| kernel | stage | MfmaUtil % | bf16 flops / dispatch | useful flops | executed / useful |",
+             "|---|---|---:|---:|---:|---:|"]
+    for k in sorted(util, key=lambda k: STAGE_ORDER.index(stage_of(k))):
+        if flops.get(k, 0.0) <= 0.0:
+            continue
+        st = stage_of(k)
+        u = float(useful[st]) if st in useful else float("nan")
+        lines.append(f"| `{short_name(k)}` | {st} | {util[k]:.1f} | {flops[k]:.4g} | {u:.4g} | {flops[k] / u:.3f} |")
+    lines.append("")
+    text = "\n".join(lines)
+    if a.out:
+        with open(a.out, "w") as f:
+            f.write(text)
+    print(text)
+
+
 def cmd_traffic(a):
     fetch = counter_avgs(_one(os.path.join(a.fetch, "**", "*counter_collection.csv")), "FETCH_SIZE")
     write = counter_avgs(_one(os.path.join(a.write, "**", "*counter_collection.csv")), "WRITE_SIZE")
@@ -236,8 +266,14 @@ def main():
     t.add_argument("--workload", required=True)
     t.add_argument("--cmd", required=True)
     t.add_argument("--out")
+    m = sub.add_parser("mfma")
+    m.add_argument("dir", help="rocprofv3 --pmc MfmaUtil MfmaFlopsBF16 output directory")
+    m.add_argument("--title", required=True)
+    m.add_argument("--cmd", required=True)
+    m.add_argument("--useful", nargs="*", help="stage=flops pairs (useful flops per launch)")
+    m.add_argument("--out")
     a = p.parse_args()
-    cmd_stats(a) if a.cmd_name == "stats" else cmd_traffic(a)
+    {"stats": cmd_stats, "traffic": cmd_traffic, "mfma": cmd_mfma}[a.cmd_name](a)
 
 
 if __name__ == "__main__":
