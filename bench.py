@@ -267,6 +267,23 @@ def main():
         "expert_down": dict(flops=2.0 * A * F * D,
                             bytes=ws * 1.0 * active * D * F + (4.0 * active * D if q8 else 0.0) + es * (A * F + A * D)),
     }
+    # Algorithmic HBM bytes of the small stages: router reads x (+ W_r, noise) and writes
+    # the selection; dispatch reads the selection and the token rows and writes the expert
+    # buffers (padding rows included) and the per-record metadata; combine reads the
+    # accepted expert rows and the per-record gates and writes y.
+    noisy = cfg["second_choice"] != "topk"
+    small_bytes = {
+        "route": es * N * D + 4.0 * D * E + (4.0 * N * E if noisy else 0.0) + 8.0 * N * k,
+        "dispatch": 8.0 * N * k + es * N * D + es * rows * D + 9.0 * N * k + 4.0 * rows + 12.0 * E,
+        "combine": es * A * D + 8.0 * N * k + es * N * D,
+    }
+    small = {}
+    for st_name, b in small_bytes.items():
+        warm = b / (stage_ms[st_name] * 1e-3) / 1e9
+        small[st_name] = {"bytes": b, "warm_gbs": warm, "warm_frac": warm / PEAK_HBM_GBS}
+        if st_name in cold_ms:
+            cold = b / (cold_ms[st_name] * 1e-3) / 1e9
+            small[st_name].update({"cold_gbs": cold, "cold_frac": cold / PEAK_HBM_GBS})
     gemm_ms = stage_ms["expert_up"] + stage_ms["expert_down"]
     gemm_tflops = (work["expert_up"]["flops"] + work["expert_down"]["flops"]) / (gemm_ms * 1e-3) / 1e12
     dom = max(("expert_up", "expert_down"), key=lambda s: stage_ms[s])
@@ -307,6 +324,7 @@ def main():
         "stages_ms": stage_ms,
         "stages_ms_pct": stage_pct,
         "stages_ms_cold": cold_ms,
+        "small_stages_hbm": small,
         "roofline": roof,
         "cpu_baseline": None,
     }
