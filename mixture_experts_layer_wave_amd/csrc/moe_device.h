@@ -42,7 +42,8 @@ enum { ACT_SILU = 0, ACT_GELU_ERF = 1, ACT_GELU_TANH = 2 };
 template <int ACT>
 __device__ __forceinline__ float activate(float z) {
   if constexpr (ACT == ACT_SILU) {
-    return z / (1.0f + expf(-z));
+    // hardware exponential and reciprocal: a few fp32 ulp, far below the bf16 rounding of h
+    return z * __builtin_amdgcn_rcpf(1.0f + __expf(-z));
   } else if constexpr (ACT == ACT_GELU_ERF) {
     return 0.5f * z * (1.0f + erff(z * 0.70710678118654752f));
   } else {
