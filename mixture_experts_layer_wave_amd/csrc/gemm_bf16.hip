@@ -240,6 +240,9 @@ __device__ __forceinline__ void fixup_item(const GemmParams& p, const Tile& tl, 
   using FR = Frag<BM, BNF, NB, Q8>;
   const int w = it / (FR::G4 * 64), rem = it % (FR::G4 * 64);
   const int g = rem / 64, lane = rem % 64;
+  const int q = g % 4, ij = g / 4, i = ij / FR::TN, j = ij % FR::TN;
+  const int row = (w / FR::WGN) * FR::WM + 32 * i + (lane & 31);
+  if (row >= tl.mcount) return;  // past the expert's count: no partials stored
   f32x4 acc[NB];
 #pragma unroll
   for (int m = 0; m < NB; ++m) acc[m] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -249,9 +252,6 @@ __device__ __forceinline__ void fixup_item(const GemmParams& p, const Tile& tl, 
 #pragma unroll
     for (int m = 0; m < NB; ++m) acc[m] += P[(m * FR::G4 + g) * 64];
   }
-  const int q = g % 4, ij = g / 4, i = ij / FR::TN, j = ij % FR::TN;
-  const int row = (w / FR::WGN) * FR::WM + 32 * i + (lane & 31);
-  if (row >= tl.mcount) return;
   const int col = (w % FR::WGN) * FR::WN + 32 * j + 8 * q + 4 * (lane >> 5);
   bf16* C = reinterpret_cast<bf16*>(p.C) + (tl.row_base + row) * p.N + tl.n0 + col;
   *reinterpret_cast<bf16x4*>(C) = epilogue4<NB, ACT, Q8>(p, tl, col, acc[0], acc[NB - 1]);
@@ -484,7 +484,8 @@ __global__ __launch_bounds__(512, 1) void k_gemm_bf16(const GemmParams p) {
     __syncthreads();  // every wave done reading the ring before the next tile refills it
 
     if (pslot >= 0) {
-      // A K piece of a tile: keep the raw fp32 accumulators for the fix-up.
+      // A K piece of a tile: keep the raw fp32 accumulators of the rows below the expert's
+      // count for the fix-up (the fix-up reads no others).
       f32x4* P = slot_base<BM, BNF, NB, Q8>(p, pslot, wid) + lane;
 #pragma unroll
       for (int m = 0; m < NB; ++m)
@@ -492,6 +493,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm_bf16(const GemmParams p) {
         for (int i = 0; i < TM; ++i)
 #pragma unroll
           for (int j = 0; j < TN; ++j)
+            if (wm * WM + 32 * i + (lane & 31) < tl.mcount)
 #pragma unroll
             for (int q = 0; q < 4; ++q)
               P[(((m * TM + i) * TN + j) * 4 + q) * 64] =
