@@ -69,17 +69,19 @@ __device__ __forceinline__ i32x2 tr_read_b8x8(const void* q) {
 }
 
 // Eight int8 values (little-endian in two dwords) -> eight bf16, exactly: each byte is
-// biased to unsigned (xor 0x80), converted to fp32 and unbiased; |v| <= 128 is exact in bf16.
+// sign-extended and converted to fp32 in one instruction (a byte-select operand), and a
+// byte permute takes the upper halves of two results as a bf16 pair (|v| <= 128 has at most
+// 8 significant bits, so dropping the low 16 bits of the fp32 value is exact): 1.5
+// instructions per weight.
 __device__ __forceinline__ bf16x8 i8x8_to_bf16(i32x2 r) {
   u32x4 o;
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
-    const uint32_t u = (uint32_t)r[h] ^ 0x80808080u;
 #pragma unroll
     for (int pr = 0; pr < 2; ++pr) {
-      const float f0 = (float)((u >> (16 * pr)) & 0xffu) - 128.f;
-      const float f1 = (float)((u >> (16 * pr + 8)) & 0xffu) - 128.f;
-      o[2 * h + pr] = (__float_as_uint(f0) >> 16) | (__float_as_uint(f1) & 0xffff0000u);
+      const float f0 = (float)(int32_t)(int8_t)(r[h] >> (16 * pr));
+      const float f1 = (float)(int32_t)(int8_t)(r[h] >> (16 * pr + 8));
+      o[2 * h + pr] = __builtin_amdgcn_perm(__float_as_uint(f1), __float_as_uint(f0), 0x07060302u);
     }
   }
   return __builtin_bit_cast(bf16x8, o);
