@@ -195,17 +195,36 @@ __device__ __forceinline__ void store_tile(const f32x16 (&acc)[NB][TM][TN], cons
 __device__ __forceinline__ int64_t sk_begin(int64_t w, int64_t W, int64_t G) { return w * W / G; }
 __device__ __forceinline__ int64_t sk_owner(int64_t s, int64_t W, int64_t G) { return ((s + 1) * G - 1) / W; }
 
-// Stream-K schedule over G workgroups: the first dp = (T / G) G tiles run whole, one per
-// workgroup per round; the remaining T - dp tiles are cut into G equal (tile, K slice)
-// ranges, so every workgroup streams the same number of K slices.
+// Stream-K schedule over G workgroups. All T tiles run whole (tile L on workgroup L % Gd,
+// the other workgroups idle) when they fit in one round on Gd = T >= 5/8 G workgroups, or
+// in r = ceil(T / G) rounds on Gd = ceil(T / r) >= 7/8 G: that many compute units already
+// saturate HBM with the weight stream, and no partial tiles or fix-up work arise (measured
+// on the decode shapes: one round on 168 workgroups beats stream-K on 256, two rounds on
+// 168 do not, since a workgroup then has to stream ~40% faster). Otherwise the first
+// dp = (T / G) G tiles run whole, one per workgroup per round, and the remaining T - dp
+// tiles are cut into G equal (tile, K slice) ranges, so every workgroup streams the same
+// number of K slices.
+#ifndef MOE_SK_WHOLE
+#define MOE_SK_WHOLE 1
+#endif
 struct SkPlan {
-  int dp;     // data-parallel tiles
-  int64_t W;  // stream-K work items: (T - dp) * nk
+  int dp;      // tiles run whole
+  int64_t W;   // stream-K work items: (T - dp) * nk
+  int stride;  // workgroups running the whole tiles
 };
 __device__ __forceinline__ SkPlan sk_plan(int T, int G, int nk) {
   SkPlan s;
+  const int r = (T + G - 1) / G;
+  const int gd = r > 0 ? (T + r - 1) / r : 0;
+  if (MOE_SK_WHOLE && ((r == 1 && 8 * T >= 5 * G) || 8 * gd >= 7 * G)) {
+    s.dp = T;
+    s.W = 0;
+    s.stride = gd;
+    return s;
+  }
   s.dp = T / G * G;
   s.W = (int64_t)(T - s.dp) * nk;
+  s.stride = G;
   return s;
 }
 
@@ -336,10 +355,11 @@ __global__ __launch_bounds__(512, 1) void k_gemm_bf16(const GemmParams p) {
   // any) one K piece of a tail tile. Stream-K: every tile its range touches.
   int units, sk_t0 = 0, dp_rounds = 0;
   int64_t sk_s0 = 0, sk_s1 = 0;
-  SkPlan sk{0, 0};
+  SkPlan sk{0, 0, 1};
   if constexpr (STREAMK) {
     sk = sk_plan(ts.total, gridDim.x, nk);
-    dp_rounds = sk.dp / gridDim.x;
+    const int b = blockIdx.x;
+    dp_rounds = b < min(sk.dp, sk.stride) ? (sk.dp - b + sk.stride - 1) / sk.stride : 0;
     sk_s0 = sk_begin(blockIdx.x, sk.W, gridDim.x);
     sk_s1 = sk_begin(blockIdx.x + 1, sk.W, gridDim.x);
     sk_t0 = (int)(sk_s0 / nk);
@@ -351,7 +371,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm_bf16(const GemmParams p) {
     int L, kb = 0, ke = nk, pslot = -1;
     if constexpr (STREAMK) {
       if (u < dp_rounds) {
-        L = blockIdx.x + u * gridDim.x;
+        L = blockIdx.x + u * sk.stride;
       } else {
         const int ls = sk_t0 + (u - dp_rounds);  // tile index within the stream-K tiles
         const int64_t base = (int64_t)ls * nk;

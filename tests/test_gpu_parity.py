@@ -195,6 +195,13 @@ FFN_CASES = [
     ("bf16", "gelu_erf", 512, 256, 8, [1, 2, 3, 4, 5, 6, 7, 8]),
     ("bf16", "silu", 4096, 512, 3, [64, 0, 0]),
     ("bf16", "gelu_tanh", 384, 256, 3, [17, 64, 0]),        # stream-K, D not a multiple of 256
+    # <= 64 rows per expert and enough up-projection tiles to run them whole, no stream-K
+    # split: bf16 160 tiles in one round (int8: 80 tiles, stream-K)
+    ("bf16", "silu", 512, 2560, 8, [64, 5, 33, 1, 64, 17, 40, 9]),
+    # bf16 320 tiles (stream-K); int8 160 tiles in one round
+    ("bf16", "gelu_erf", 256, 5120, 8, [3, 64, 0, 22, 64, 64, 1, 50]),
+    # bf16 448 tiles in two rounds on 224 workgroups; int8 224 tiles in one round
+    ("bf16", "silu", 256, 7168, 8, [10, 20, 30, 40, 50, 60, 64, 2]),
     ("f32", "silu", 128, 256, 4, [30, 33, 0, 65]),
     ("f32", "gelu_erf", 256, 128, 3, [64, 1, 100]),
 ]
