@@ -300,8 +300,19 @@ __device__ __forceinline__ void gather_row(const GatherArgs& a, int64_t r, int64
   const int nvec = (int)(row_bytes / VB);
   u32x4* dst = reinterpret_cast<u32x4*>(reinterpret_cast<char*>(a.x_perm) + r * row_bytes);
   if (t >= 0 && t < a.N) {
+    // up to kU vectors per lane in flight before the first store, so a row costs about one
+    // memory latency instead of one per vector
+    constexpr int kU = 8;
     const u32x4* src = reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(a.x) + t * row_bytes);
-    for (int i = lane; i < nvec; i += 64) dst[i] = src[i];
+    for (int i0 = lane; i0 < nvec; i0 += 64 * kU) {
+      u32x4 v[kU];
+#pragma unroll
+      for (int u = 0; u < kU; ++u)
+        if (i0 + 64 * u < nvec) v[u] = src[i0 + 64 * u];
+#pragma unroll
+      for (int u = 0; u < kU; ++u)
+        if (i0 + 64 * u < nvec) dst[i0 + 64 * u] = v[u];
+    }
   } else {
     const u32x4 z = {0u, 0u, 0u, 0u};
     for (int i = lane; i < nvec; i += 64) dst[i] = z;
@@ -439,6 +450,8 @@ __global__ __launch_bounds__(256) void k_route_dispatch_small(const RouterArgs r
                                                               const GatherArgs g) {
   __shared__ float l_s[kDispatchTokens][EP + 1];
   __shared__ float ps_s[EP][kDispatchTokens];
+  __shared__ float nz_s[kDispatchTokens][EP];  // the tokens' noise rows (coalesced copy)
+  __shared__ float b_s[EP];                    // logit bias (0 without one)
   const int tid = threadIdx.x;
   const int E = ra.E;
   const int64_t items = ra.N * E;
@@ -456,6 +469,9 @@ __global__ __launch_bounds__(256) void k_route_dispatch_small(const RouterArgs r
     }
     l_s[it / E][it % E] = v;
   }
+  if (ra.noise != nullptr)
+    for (int64_t i = tid; i < items; i += 256) nz_s[i / E][i % E] = ra.noise[i];
+  if (tid < EP) b_s[tid] = (ra.bias != nullptr && tid < E) ? ra.bias[tid] : 0.f;
   __syncthreads();
   const int64_t t = tid;
   const bool valid = t < ra.N;
@@ -467,11 +483,11 @@ __global__ __launch_bounds__(256) void k_route_dispatch_small(const RouterArgs r
     float l[EP], p[EP];
 #pragma unroll
     for (int x = 0; x < EP; ++x) {
-      l[x] = (valid && x < E) ? l_s[tid][x] + (ra.bias != nullptr ? ra.bias[x] : 0.f) : 0.f;
+      l[x] = (valid && x < E) ? l_s[tid][x] + b_s[x] : 0.f;
       p[x] = 0.f;
     }
     if (valid) {
-      route_token(ra, t, ra.noise != nullptr ? ra.noise + t * E : nullptr, l, p, e, gt);
+      route_token(ra, t, ra.noise != nullptr ? nz_s[tid] : nullptr, l, p, e, gt);
       if (blockIdx.x == 0) store_topk(ra, t, e, gt);
     }
 #pragma unroll

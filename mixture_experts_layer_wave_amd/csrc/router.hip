@@ -319,6 +319,7 @@ __global__ __launch_bounds__(256) void k_router_epi(const RouterArgs a, RouterSp
   __shared__ float l_s[64][EP + 1];
   __shared__ float ps_s[EP][64];
   __shared__ float nz_s[64][EP];  // the 64 tokens' noise rows (coalesced copy)
+  __shared__ float b_s[EP];       // logit bias (0 without one)
   const int tid = threadIdx.x;
   const int E = a.E;
   const int64_t t0 = (int64_t)blockIdx.x * 64;
@@ -351,6 +352,7 @@ __global__ __launch_bounds__(256) void k_router_epi(const RouterArgs a, RouterSp
   }
   if (a.noise != nullptr)
     for (int i = tid; i < nitem; i += 256) nz_s[i / E][i % E] = a.noise[t0 * E + i];
+  if (tid < EP) b_s[tid] = (a.bias != nullptr && tid < E) ? a.bias[tid] : 0.f;
   __syncthreads();
   if (tid < 64) {  // wave 0: one token per lane
     const int64_t t = t0 + tid;
@@ -358,7 +360,7 @@ __global__ __launch_bounds__(256) void k_router_epi(const RouterArgs a, RouterSp
     float l[EP], p[EP];
 #pragma unroll
     for (int e = 0; e < EP; ++e) {
-      l[e] = (valid && e < E) ? l_s[tid][e] + (a.bias != nullptr ? a.bias[e] : 0.f) : 0.f;
+      l[e] = (valid && e < E) ? l_s[tid][e] + b_s[e] : 0.f;
       p[e] = 0.f;
     }
     if (valid) {
