@@ -21,6 +21,9 @@
 //    natural layout and is turned into MFMA operands by the gfx950 transposing read
 //    ds_read_b64_tr_b16 (ds_read_b64_tr_b8 plus an exact widening for int8 weights).
 //    Both LDS tiles are unpadded and XOR-swizzled so these reads are bank-conflict free.
+//    The bf16 256-row tiles split the 160 KB of LDS into two A slices and three B slices:
+//    the A copies of slice kt + 1 go out after the barrier, those of B slice kt + 2 one
+//    share after each 16-deep MFMA group of slice kt, so copy issue overlaps the MFMAs.
 //  * Persistent, XCD-aware schedule: the grid is a multiple of 8 workgroups; workgroup b
 //    runs on XCD b mod 8 and walks a contiguous eighth of the tile list, so the tiles
 //    sharing one expert's activations and weight columns run concurrently inside one
@@ -48,6 +51,9 @@ constexpr int kSplitMax = 8;  // most K pieces of one tail tile
 #endif
 #ifndef MOE_GEMM_STAGES
 #define MOE_GEMM_STAGES 2
+#endif
+#ifndef MOE_GEMM_B3
+#define MOE_GEMM_B3 1
 #endif
 
 __device__ __forceinline__ bf16x8 tr_read_b16x8(const bf16* q, int row_stride) {
@@ -305,8 +311,15 @@ __global__ __launch_bounds__(512, 1) void k_gemm_bf16(const GemmParams p) {
   static_assert(!Q8 || BK == 64, "int8 tiles: 64-deep slices");
   static_assert(STAGES >= 2 && STAGES <= 8 && STAGES * STAGE * 2 <= 160 * 1024, "LDS ring");
   static_assert(A_CP >= 1 && B_CP >= 1 && TM >= 1 && TN >= 1 && (NB * B_CPM) % 8 == 0, "tile shape");
+  // Split ring (persistent bf16 tiles with 2 stages): A slices double-buffered, B slices
+  // triple-buffered, and the copies of B slice kt + 2 spread between the MFMA groups of
+  // slice kt instead of issued in one burst after the barrier.
+  constexpr bool B3 = MOE_GEMM_B3 && !STREAMK && !Q8 && STAGES == 2;
+  constexpr int B_EL = NB * B_BYTES / 2;  // bf16 elements of one B slice (all matrices)
+  constexpr int RING_EL = B3 ? 2 * A_EL + 3 * B_EL : STAGES * STAGE;
+  static_assert(RING_EL * 2 <= 160 * 1024, "LDS ring");
 
-  __shared__ __attribute__((aligned(1024))) bf16 ring[STAGES * STAGE];
+  __shared__ __attribute__((aligned(1024))) bf16 ring[RING_EL];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -430,6 +443,22 @@ __global__ __launch_bounds__(512, 1) void k_gemm_bf16(const GemmParams p) {
       for (int q = 0; q < B_CP; ++q)
         load_lds16(b_src[q] + (int64_t)k0 * N * WB, (uint32_t)uniform(base + A_EL * 2 + (B_CP * wid + q) * 1024));
     };
+    // split ring: A slice kt in A slot kt % 2, B slice kt in B slot kt % 3
+    auto issue_a = [&](int kt) {
+      const int k0 = (kb + kt) * BK;
+      const int base = ring_addr + (kt % 2) * A_EL * 2;
+#pragma unroll
+      for (int q = 0; q < A_CP; ++q) load_lds16(a_src[q] + k0, (uint32_t)uniform(base + (A_CP * wid + q) * 1024));
+    };
+    // copies q of B slice kt with q0 <= q < q1 (q0, q1 compile-time after unrolling)
+    auto issue_b = [&](int kt, int q0, int q1) {
+      const int k0 = (kb + kt) * BK;
+      const int base = ring_addr + 2 * A_EL * 2 + (kt % 3) * B_EL * 2;
+#pragma unroll
+      for (int q = 0; q < B_CP; ++q)
+        if (q >= q0 && q < q1)
+          load_lds16(b_src[q] + (int64_t)k0 * N * WB, (uint32_t)uniform(base + (B_CP * wid + q) * 1024));
+    };
 
     f32x16 acc[NB][TM][TN];
 #pragma unroll
@@ -450,6 +479,61 @@ __global__ __launch_bounds__(512, 1) void k_gemm_bf16(const GemmParams p) {
       constexpr bool LONE = decltype(lone_tile)::value;
       const bool a_live = !LONE || A_RPC * A_CP * wid < tl.mcount;
       const bool c_live = !LONE || wm * WM < tl.mcount;
+    if constexpr (B3) {
+      // Issue order per wave: A0, B0, B1 | A1, B2 | A2, B3 | ... (iteration kt issues A kt+1
+      // after its barrier and B kt+2 between its MFMA groups), so when iteration kt starts
+      // at most the copies of B kt+1 may still be outstanding after A kt and B kt.
+      constexpr int GROUPS = BK / 16;  // MFMA groups (16-deep K steps); B copies split over them
+      if (a_live) issue_a(0);
+      issue_b(0, 0, B_CP);
+      if (nku > 1) issue_b(1, 0, B_CP);
+      for (int kt = 0; kt < nku; ++kt) {
+        if (kt + 1 < nku) wait_vmcnt<B_CP>();
+        else wait_vmcnt<0>();
+        barrier_no_fence();  // A kt and B kt visible to every wave; slice kt-1 fully consumed
+        if (a_live && kt + 1 < nku) issue_a(kt + 1);
+        const bool b2 = kt + 2 < nku;
+        if (!c_live) {
+          if (b2) issue_b(kt + 2, 0, B_CP);
+          continue;
+        }
+        const bf16* As = ring + (kt % 2) * A_EL;
+        const bf16* Bs = ring + 2 * A_EL + (kt % 3) * B_EL;
+        // fragments of one 16-deep group, read one group ahead (two groups live)
+        bf16x8 af[2][TM], bfr[2][NB][TN];
+        auto load_group = [&](int kk, int buf) {
+#pragma unroll
+          for (int i = 0; i < TM; ++i)
+            af[buf][i] = *reinterpret_cast<const bf16x8*>(As + (a_row + 32 * i) * BK + 8 * ((2 * kk + (lane >> 5)) ^ a_swz));
+#pragma unroll
+          for (int m = 0; m < NB; ++m)
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+              bfr[buf][m][j] = tr_read_b16x8(Bs + m * (B_BYTES / 2) + (kk * 16 + b_row) * BNF +
+                                                 16 * ((b_seg + 2 * j) ^ b_swz) + b_in, BNF);
+        };
+        load_group(0, 0);
+#pragma unroll
+        for (int kk = 0; kk < GROUPS; ++kk) {
+          if (kk + 1 < GROUPS) load_group(kk + 1, (kk + 1) & 1);
+#pragma unroll
+          for (int m = 0; m < NB; ++m)
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+#pragma unroll
+              for (int i = 0; i < TM; ++i)
+                acc[m][i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[kk & 1][m][j], af[kk & 1][i], acc[m][i][j], 0, 0, 0);
+          // this group's share of the copies of B slice kt + 2, kept between the MFMA groups
+          const int q0 = kk * B_CP / GROUPS, q1 = (kk + 1) * B_CP / GROUPS;  // unrolled: constants
+          if (q1 > q0 && b2) {
+            __builtin_amdgcn_sched_barrier(0);
+            issue_b(kt + 2, q0, q1);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        }
+      }
+      return;
+    }
 #pragma unroll
     for (int st = 0; st < STAGES - 1; ++st)
       if (st < nku) issue_slice(st, a_live);
