@@ -52,13 +52,14 @@ __device__ __forceinline__ void wave_match(int e, int E, int (*cnt_s)[kMaxE], in
 // Token-major match over all k slots of each lane's token: on return rank[j] = records of
 // expert e[j] in lower lanes (any slot) plus those in earlier slots of the same lane, and
 // cnt_s[w][x] = records of expert x in wave w.
+template <int KM = kMaxK>
 __device__ __forceinline__ void wave_match_tokens(const int (&e)[kMaxK], int k, int E, int (*cnt_s)[kMaxE],
                                                   int (&rank)[kMaxK]) {
   const int w = threadIdx.x >> 6;
   const int lane = lane_id();
   const uint64_t lt = lanemask_lt();
 #pragma unroll
-  for (int j = 0; j < kMaxK; ++j) rank[j] = 0;
+  for (int j = 0; j < KM; ++j) rank[j] = 0;
   for (int x = 0; x < E; ++x) {
     int c = 0, below = 0;
     for (int j = 0; j < k; ++j) {
@@ -68,7 +69,7 @@ __device__ __forceinline__ void wave_match_tokens(const int (&e)[kMaxK], int k, 
     }
     int same = 0;  // earlier slots of this lane with expert x
 #pragma unroll
-    for (int j = 0; j < kMaxK; ++j) {
+    for (int j = 0; j < KM; ++j) {
       if (j < k && e[j] == x) {
         rank[j] = below + same;
         ++same;
@@ -78,9 +79,12 @@ __device__ __forceinline__ void wave_match_tokens(const int (&e)[kMaxK], int k, 
   }
 }
 
+template <int KM = kMaxK>
 __device__ __forceinline__ void load_experts(const DispatchArgs& a, int64_t t, bool valid, int (&e)[kMaxK]) {
 #pragma unroll
-  for (int j = 0; j < kMaxK; ++j) {
+  for (int j = KM; j < kMaxK; ++j) e[j] = -1;
+#pragma unroll
+  for (int j = 0; j < KM; ++j) {
     int v = (valid && j < a.k) ? a.topk_idx[t * a.k + j] : -1;
     if (v >= a.E) v = -1;  // out-of-range ids are ignored (they never index LDS or scratch)
     e[j] = v;
@@ -325,10 +329,11 @@ __device__ __forceinline__ void gather_row(const GatherArgs& a, int64_t r, int64
 // running sum over (segment, wave) gives the first position of each wave's records, as the
 // three-pass path does over (segment, block).
 // e[j] / gt[j]: the experts (-1: none) and gates of this thread's token t = threadIdx.x.
+template <int KM>
 __device__ __forceinline__ void dispatch_small_body(const DispatchArgs& a, const GatherArgs& g, int (&e)[kMaxK],
                                                     const float (&gt)[kMaxK]) {
-  __shared__ int cnt_s[kMaxK][4][kMaxE];
-  __shared__ int base_s[kMaxK][4][kMaxE];
+  __shared__ int cnt_s[KM][4][kMaxE];
+  __shared__ int base_s[KM][4][kMaxE];
   __shared__ int cap_s[kMaxE];
   __shared__ int off_s[kMaxE + 1];
   __shared__ int tor_s[kSmallRows];
@@ -342,10 +347,10 @@ __device__ __forceinline__ void dispatch_small_body(const DispatchArgs& a, const
 
   int rank[kMaxK];
   if (a.token_major) {
-    wave_match_tokens(e, a.k, a.E, cnt_s[0], rank);
+    wave_match_tokens<KM>(e, a.k, a.E, cnt_s[0], rank);
   } else {
 #pragma unroll
-    for (int j = 0; j < kMaxK; ++j)
+    for (int j = 0; j < KM; ++j)
       if (j < a.k) wave_match(e[j], a.E, cnt_s[j], rank[j]);
   }
   for (int r = tid; r < g.rows; r += 256) tor_s[r] = -1;
@@ -378,7 +383,7 @@ __device__ __forceinline__ void dispatch_small_body(const DispatchArgs& a, const
   int row[kMaxK];
   bool kept[kMaxK];
 #pragma unroll
-  for (int j = 0; j < kMaxK; ++j) {
+  for (int j = 0; j < KM; ++j) {
     row[j] = -1;
     kept[j] = false;
     if (j < a.k && e[j] >= 0) {
@@ -396,7 +401,7 @@ __device__ __forceinline__ void dispatch_small_body(const DispatchArgs& a, const
     float all = 0.f, ksum = 0.f;
     int nk = 0;
 #pragma unroll
-    for (int j = 0; j < kMaxK; ++j) {
+    for (int j = 0; j < KM; ++j) {
       if (j < a.k) {
         all += gt[j];
         if (kept[j]) { ksum += gt[j]; nk += 1; }
@@ -405,7 +410,7 @@ __device__ __forceinline__ void dispatch_small_body(const DispatchArgs& a, const
     all_dropped = (nk == 0);
     if (writer) {
 #pragma unroll
-      for (int j = 0; j < kMaxK; ++j) {
+      for (int j = 0; j < KM; ++j) {
         if (j < a.k) {
           float ge;
           if (nk == a.k) ge = gt[j];
@@ -429,15 +434,16 @@ __device__ __forceinline__ void dispatch_small_body(const DispatchArgs& a, const
     gather_row<16>(g, r, tor_s[r], lane);
 }
 
+template <int KM>
 __global__ __launch_bounds__(256) void k_dispatch_small(const DispatchArgs a, const GatherArgs g) {
   const int64_t t = threadIdx.x;
   const bool valid = t < a.N;
   int e[kMaxK];
   float gt[kMaxK];
-  load_experts(a, t, valid, e);
+  load_experts<KM>(a, t, valid, e);
 #pragma unroll
-  for (int j = 0; j < kMaxK; ++j) gt[j] = (valid && j < a.k) ? a.topk_gate[t * a.k + j] : 0.f;
-  dispatch_small_body(a, g, e, gt);
+  for (int j = 0; j < KM; ++j) gt[j] = (valid && j < a.k) ? a.topk_gate[t * a.k + j] : 0.f;
+  dispatch_small_body<KM>(a, g, e, gt);
 }
 
 // Route epilogue and dispatch of at most kDispatchTokens tokens in one launch (the layer's
@@ -445,7 +451,7 @@ __global__ __launch_bounds__(256) void k_dispatch_small(const DispatchArgs a, co
 // in split order and runs the token epilogue, as k_router_epi does, then dispatches as
 // k_dispatch_small. Workgroup 0 also stores the selection, the gates and the probability
 // block sums, so the results equal those of the separate router and dispatch calls.
-template <int EP>
+template <int EP, int KM>
 __global__ __launch_bounds__(256) void k_route_dispatch_small(const RouterArgs ra, int S, const DispatchArgs a,
                                                               const GatherArgs g) {
   __shared__ float l_s[kDispatchTokens][EP + 1];
@@ -456,18 +462,30 @@ __global__ __launch_bounds__(256) void k_route_dispatch_small(const RouterArgs r
   const int E = ra.E;
   const int64_t items = ra.N * E;
   const int64_t stride = ra.N * E;  // floats between consecutive splits
-  constexpr int SB = 32;  // splits whose loads are in flight together
-  for (int64_t it = tid; it < items; it += 256) {
-    float v = 0.f;
+  // two items per thread per pass, 32 splits each: 64 loads in flight together
+  constexpr int SB = 32, IPB = 2;
+  for (int64_t it0 = tid; it0 < items; it0 += 256 * IPB) {
+    float v[IPB];
+#pragma unroll
+    for (int b = 0; b < IPB; ++b) v[b] = 0.f;
     for (int s0 = 0; s0 < S; s0 += SB) {
-      float q[SB];
+      float q[IPB][SB];
 #pragma unroll
-      for (int u = 0; u < SB; ++u) q[u] = s0 + u < S ? ra.rpart[(int64_t)(s0 + u) * stride + it] : 0.f;
+      for (int b = 0; b < IPB; ++b)
 #pragma unroll
-      for (int u = 0; u < SB; ++u)
-        if (s0 + u < S) v += q[u];
+        for (int u = 0; u < SB; ++u)
+          q[b][u] = (s0 + u < S && it0 + 256 * b < items) ? ra.rpart[(int64_t)(s0 + u) * stride + it0 + 256 * b] : 0.f;
+#pragma unroll
+      for (int b = 0; b < IPB; ++b)
+#pragma unroll
+        for (int u = 0; u < SB; ++u)
+          if (s0 + u < S) v[b] += q[b][u];
     }
-    l_s[it / E][it % E] = v;
+#pragma unroll
+    for (int b = 0; b < IPB; ++b) {
+      const int64_t it = it0 + 256 * b;
+      if (it < items) l_s[it / E][it % E] = v[b];
+    }
   }
   if (ra.noise != nullptr)
     for (int64_t i = tid; i < items; i += 256) nz_s[i / E][i % E] = ra.noise[i];
@@ -487,8 +505,8 @@ __global__ __launch_bounds__(256) void k_route_dispatch_small(const RouterArgs r
       p[x] = 0.f;
     }
     if (valid) {
-      route_token(ra, t, ra.noise != nullptr ? nz_s[tid] : nullptr, l, p, e, gt);
-      if (blockIdx.x == 0) store_topk(ra, t, e, gt);
+      route_token<EP, KM>(ra, t, ra.noise != nullptr ? nz_s[tid] : nullptr, l, p, e, gt);
+      if (blockIdx.x == 0) store_topk<KM>(ra, t, e, gt);
     }
 #pragma unroll
     for (int x = 0; x < EP; ++x) ps_s[x][tid] = valid ? p[x] : 0.f;
@@ -508,7 +526,7 @@ __global__ __launch_bounds__(256) void k_route_dispatch_small(const RouterArgs r
     }
     if (blockIdx.x == 0 && tid == 0 && ra.psum_magic) *ra.psum_magic = kPsumMagic;
   }
-  dispatch_small_body(a, g, e, gt);
+  dispatch_small_body<KM>(a, g, e, gt);
 }
 
 // One wave per expert-buffer row: copy the token's row or write zeros for padding.
@@ -582,7 +600,8 @@ hipError_t launch_dispatch_small(const DispatchArgs& a, const GatherArgs& g, hip
   if (a.N > kDispatchTokens || g.rows > kSmallRows) return hipErrorInvalidValue;
   int64_t grid = (g.rows + 3) / 4;
   grid = grid < 1 ? 1 : (grid > 256 ? 256 : grid);
-  hipLaunchKernelGGL(k_dispatch_small, dim3((unsigned)grid), dim3(256), 0, s, a, g);
+  if (a.k <= 2) hipLaunchKernelGGL(k_dispatch_small<2>, dim3((unsigned)grid), dim3(256), 0, s, a, g);
+  else hipLaunchKernelGGL(k_dispatch_small<kMaxK>, dim3((unsigned)grid), dim3(256), 0, s, a, g);
   return hipGetLastError();
 }
 
@@ -594,8 +613,14 @@ hipError_t launch_route_dispatch_small(const RouterArgs& ra, const DispatchArgs&
   const RouterSplit rs = router_split(ra.N, ra.D);
   int64_t grid = (g.rows + 3) / 4;
   grid = grid < 1 ? 1 : (grid > 256 ? 256 : grid);
-  if (ra.E <= 8) hipLaunchKernelGGL((k_route_dispatch_small<8>), dim3((unsigned)grid), dim3(256), 0, s, ra, rs.S, a, g);
-  else hipLaunchKernelGGL((k_route_dispatch_small<16>), dim3((unsigned)grid), dim3(256), 0, s, ra, rs.S, a, g);
+  const dim3 gd((unsigned)grid), wg(256);
+  if (ra.E <= 8) {
+    if (a.k <= 2) hipLaunchKernelGGL((k_route_dispatch_small<8, 2>), gd, wg, 0, s, ra, rs.S, a, g);
+    else hipLaunchKernelGGL((k_route_dispatch_small<8, kMaxK>), gd, wg, 0, s, ra, rs.S, a, g);
+  } else {
+    if (a.k <= 2) hipLaunchKernelGGL((k_route_dispatch_small<16, 2>), gd, wg, 0, s, ra, rs.S, a, g);
+    else hipLaunchKernelGGL((k_route_dispatch_small<16, kMaxK>), gd, wg, 0, s, ra, rs.S, a, g);
+  }
   return hipGetLastError();
 }
 

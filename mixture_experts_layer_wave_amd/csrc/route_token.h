@@ -22,8 +22,9 @@ __device__ __forceinline__ float pick(const float (&v)[EP], int i) {
 // Epilogue of one token t < N from its logits l (bias included): noisy top-k gating,
 // softmax into p, optional logits/probs outputs, the k selected experts (sel, slot 0
 // first) and their gates (gt). nz: the token's E noise values (a.noise row t, or a copy
-// of it), unused without noise.
-template <int EP>
+// of it), unused without noise. KM: compile-time bound on k (a.k <= KM); entries j >= KM
+// of sel and gt are left untouched.
+template <int EP, int KM = kMaxK>
 __device__ __forceinline__ void route_token(const RouterArgs& a, int64_t t, const float* nz, float (&l)[EP],
                                             float (&p)[EP], int (&sel)[kMaxK], float (&gt)[kMaxK]) {
   const int E = a.E;
@@ -56,9 +57,10 @@ __device__ __forceinline__ void route_token(const RouterArgs& a, int64_t t, cons
     for (int e = 0; e < EP; ++e) z[e] = (e < E) ? l[e] + nz[e] : 0.f;
   }
 
+  static_assert(KM >= 1 && KM <= kMaxK, "k bound");
   uint64_t chosen = 0;
 #pragma unroll
-  for (int j = 0; j < kMaxK; ++j) {
+  for (int j = 0; j < KM; ++j) {
     sel[j] = 0;
     if (j < a.k) {
       const bool use_z = (j > 0) && a.noisy == 1;
@@ -77,25 +79,26 @@ __device__ __forceinline__ void route_token(const RouterArgs& a, int64_t t, cons
 
   if (a.mode == 0) {
 #pragma unroll
-    for (int j = 0; j < kMaxK; ++j) gt[j] = (j < a.k) ? pick(p, sel[j]) : 0.f;
+    for (int j = 0; j < KM; ++j) gt[j] = (j < a.k) ? pick(p, sel[j]) : 0.f;
   } else {
     const float ref = pick(l, sel[0]);
     float s2 = 0.f;
 #pragma unroll
-    for (int j = 0; j < kMaxK; ++j) {
+    for (int j = 0; j < KM; ++j) {
       gt[j] = (j < a.k) ? expf(pick(l, sel[j]) - ref) : 0.f;
       s2 += gt[j];
     }
 #pragma unroll
-    for (int j = 0; j < kMaxK; ++j) gt[j] = gt[j] / s2;
+    for (int j = 0; j < KM; ++j) gt[j] = gt[j] / s2;
   }
 }
 
-// Stores the selection and gates of token t.
+// Stores the selection and gates of token t (a.k <= KM).
+template <int KM = kMaxK>
 __device__ __forceinline__ void store_topk(const RouterArgs& a, int64_t t, const int (&sel)[kMaxK],
                                            const float (&gt)[kMaxK]) {
 #pragma unroll
-  for (int j = 0; j < kMaxK; ++j) {
+  for (int j = 0; j < KM; ++j) {
     if (j < a.k) {
       a.topk_idx[t * a.k + j] = sel[j];
       a.topk_gate[t * a.k + j] = gt[j];

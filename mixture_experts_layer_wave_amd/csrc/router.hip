@@ -57,7 +57,7 @@ struct XChunk {
 };
 
 // NT: 32-expert column tiles (E <= 32 * NT); EP: register array width of the epilogue.
-template <int NT, int EP, typename XT, bool FROM_LOGITS>
+template <int NT, int EP, typename XT, bool FROM_LOGITS, int KM>
 __global__ __launch_bounds__(512) void k_router(const RouterArgs a) {
   __shared__ float red_s[FROM_LOGITS ? 1 : kWaves][NT][16][64];  // partial logit blocks, lane-contiguous
   __shared__ float ps_s[EP][kTM];
@@ -163,8 +163,8 @@ __global__ __launch_bounds__(512) void k_router(const RouterArgs a) {
     if (valid) {
       int sel[kMaxK];
       float gt[kMaxK];
-      route_token(a, t, a.noise != nullptr ? a.noise + t * E : nullptr, l, p, sel, gt);
-      store_topk(a, t, sel, gt);
+      route_token<EP, KM>(a, t, a.noise != nullptr ? a.noise + t * E : nullptr, l, p, sel, gt);
+      store_topk<KM>(a, t, sel, gt);
     }
     if (a.psum) {
 #pragma unroll
@@ -314,7 +314,7 @@ __global__ __launch_bounds__(512) void k_router_split(const RouterArgs a, Router
 // 64 x E logits, each in split order (the loads of all items of a thread and of up to
 // 64 / items splits are in flight at once; consecutive threads read consecutive partials). Phase 2: one thread per token adds the
 // bias and runs the token epilogue. Block sums of the probabilities per 32 tokens.
-template <int EP>
+template <int EP, int KM>
 __global__ __launch_bounds__(256) void k_router_epi(const RouterArgs a, RouterSplit rs) {
   __shared__ float l_s[64][EP + 1];
   __shared__ float ps_s[EP][64];
@@ -366,8 +366,8 @@ __global__ __launch_bounds__(256) void k_router_epi(const RouterArgs a, RouterSp
     if (valid) {
       int sel[kMaxK];
       float gt[kMaxK];
-      route_token(a, t, nz_s[tid], l, p, sel, gt);
-      store_topk(a, t, sel, gt);
+      route_token<EP, KM>(a, t, nz_s[tid], l, p, sel, gt);
+      store_topk<KM>(a, t, sel, gt);
     }
 #pragma unroll
     for (int e = 0; e < EP; ++e) ps_s[e][tid] = valid ? p[e] : 0.f;
@@ -387,23 +387,29 @@ __global__ __launch_bounds__(256) void k_router_epi(const RouterArgs a, RouterSp
   if (blockIdx.x == 0 && tid == 0 && a.psum_magic) *a.psum_magic = kPsumMagic;
 }
 
-template <int NT, int EP>
-hipError_t launch_ep(const RouterArgs& a, bool bf16_x, hipStream_t s) {
+// KM: compile-time bound on k for the token epilogue (2 covers the common top-1 / top-2).
+template <int NT, int EP, int KM>
+hipError_t launch_epk(const RouterArgs& a, bool bf16_x, hipStream_t s) {
   if (bf16_x && a.logits_in == nullptr && a.rpart != nullptr && a.D % kRouterChunk == 0) {
     const RouterSplit rs = router_split(a.N, a.D);
     hipLaunchKernelGGL((k_router_split<NT>), dim3((unsigned)(rs.tiles * rs.S)), dim3(512), 0, s, a, rs);
-    hipLaunchKernelGGL((k_router_epi<EP>), dim3((unsigned)((a.N + 63) / 64)), dim3(256), 0, s, a, rs);
+    hipLaunchKernelGGL((k_router_epi<EP, KM>), dim3((unsigned)((a.N + 63) / 64)), dim3(256), 0, s, a, rs);
     return hipGetLastError();
   }
   const dim3 grid((unsigned)((a.N + kTM - 1) / kTM)), block(512);
   if (a.logits_in) {
-    hipLaunchKernelGGL((k_router<NT, EP, float, true>), grid, block, 0, s, a);
+    hipLaunchKernelGGL((k_router<NT, EP, float, true, KM>), grid, block, 0, s, a);
   } else if (bf16_x) {
-    hipLaunchKernelGGL((k_router<NT, EP, bf16, false>), grid, block, 0, s, a);
+    hipLaunchKernelGGL((k_router<NT, EP, bf16, false, KM>), grid, block, 0, s, a);
   } else {
-    hipLaunchKernelGGL((k_router<NT, EP, float, false>), grid, block, 0, s, a);
+    hipLaunchKernelGGL((k_router<NT, EP, float, false, KM>), grid, block, 0, s, a);
   }
   return hipGetLastError();
+}
+
+template <int NT, int EP>
+hipError_t launch_ep(const RouterArgs& a, bool bf16_x, hipStream_t s) {
+  return a.k <= 2 ? launch_epk<NT, EP, 2>(a, bf16_x, s) : launch_epk<NT, EP, kMaxK>(a, bf16_x, s);
 }
 
 }  // namespace
