@@ -462,29 +462,50 @@ __global__ __launch_bounds__(256) void k_route_dispatch_small(const RouterArgs r
   const int E = ra.E;
   const int64_t items = ra.N * E;
   const int64_t stride = ra.N * E;  // floats between consecutive splits
-  // two items per thread per pass, 32 splits each: 64 loads in flight together
+  // Split partials of every token, summed in split order: four consecutive items per
+  // thread with one 16-byte load per split when the layout allows it, else two items per
+  // thread; 32 splits' loads in flight together.
   constexpr int SB = 32, IPB = 2;
-  for (int64_t it0 = tid; it0 < items; it0 += 256 * IPB) {
-    float v[IPB];
-#pragma unroll
-    for (int b = 0; b < IPB; ++b) v[b] = 0.f;
-    for (int s0 = 0; s0 < S; s0 += SB) {
-      float q[IPB][SB];
-#pragma unroll
-      for (int b = 0; b < IPB; ++b)
+  if ((items & 3) == 0 && (stride & 3) == 0) {
+    // four consecutive items per thread, one 16-byte load per split
+    for (int64_t i4 = 4 * (int64_t)tid; i4 < items; i4 += 4 * 256) {
+      f32x4 v = {0.f, 0.f, 0.f, 0.f};
+      for (int s0 = 0; s0 < S; s0 += SB) {
+        f32x4 q[SB];
 #pragma unroll
         for (int u = 0; u < SB; ++u)
-          q[b][u] = (s0 + u < S && it0 + 256 * b < items) ? ra.rpart[(int64_t)(s0 + u) * stride + it0 + 256 * b] : 0.f;
-#pragma unroll
-      for (int b = 0; b < IPB; ++b)
+          q[u] = s0 + u < S ? *reinterpret_cast<const f32x4*>(ra.rpart + (int64_t)(s0 + u) * stride + i4)
+                            : f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int u = 0; u < SB; ++u)
-          if (s0 + u < S) v[b] += q[b][u];
+          if (s0 + u < S) v += q[u];
+      }
+#pragma unroll
+      for (int c = 0; c < 4; ++c) l_s[(i4 + c) / E][(i4 + c) % E] = v[c];
     }
+  } else {
+    for (int64_t it0 = tid; it0 < items; it0 += 256 * IPB) {
+      float v[IPB];
 #pragma unroll
-    for (int b = 0; b < IPB; ++b) {
-      const int64_t it = it0 + 256 * b;
-      if (it < items) l_s[it / E][it % E] = v[b];
+      for (int b = 0; b < IPB; ++b) v[b] = 0.f;
+      for (int s0 = 0; s0 < S; s0 += SB) {
+        float q[IPB][SB];
+#pragma unroll
+        for (int b = 0; b < IPB; ++b)
+#pragma unroll
+          for (int u = 0; u < SB; ++u)
+            q[b][u] = (s0 + u < S && it0 + 256 * b < items) ? ra.rpart[(int64_t)(s0 + u) * stride + it0 + 256 * b] : 0.f;
+#pragma unroll
+        for (int b = 0; b < IPB; ++b)
+#pragma unroll
+          for (int u = 0; u < SB; ++u)
+            if (s0 + u < S) v[b] += q[b][u];
+      }
+#pragma unroll
+      for (int b = 0; b < IPB; ++b) {
+        const int64_t it = it0 + 256 * b;
+        if (it < items) l_s[it / E][it % E] = v[b];
+      }
     }
   }
   if (ra.noise != nullptr)
