@@ -169,7 +169,11 @@ MOE_API int moe_workspace_size(const moe_desc* desc, size_t* bytes);
 
 /* Byte offsets of the intermediates inside a moe_forward workspace, so that a caller
  * can inspect them after moe_forward returns (the workspace keeps the last call's
- * contents). Layout of each is as in the step functions below. */
+ * contents). Layout of each is as in the step functions below. Exception: for bf16
+ * layers with bf16 expert weights, N > 256 (or more than 4096 expert-buffer rows) whose experts can hold more
+ * than 64 rows (N, or C when padded), moe_forward's up-projection reads the token rows of
+ * x directly through token_of_row, so x_perm is not written and the padding entries of
+ * token_of_row (PADDED) are unspecified. */
 typedef struct moe_ws_layout {
   size_t scratch;        /* moe_scratch_size bytes                                      */
   size_t topk_idx;       /* int32 [N,k]                                                 */

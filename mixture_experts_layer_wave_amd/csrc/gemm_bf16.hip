@@ -288,8 +288,10 @@ __device__ __forceinline__ void fixup_item(const GemmParams& p, const Tile& tl, 
 // STREAMK = true : stream-K; the (tile, K slice) list is cut into equal contiguous ranges,
 //                  one per workgroup; a tile cut by a range boundary leaves fp32 partials
 //                  (slot 2w for the workgroup's first tile, 2w + 1 for its last).
-template <int BM, int BNF, int NB, int ACT, int BK, int STAGES, bool STREAMK, bool Q8>
+template <int BM, int BNF, int NB, int ACT, int BK, int STAGES, bool STREAMK, bool Q8, bool GA = false>
 __global__ __launch_bounds__(512, 1) void k_gemm_bf16(const GemmParams p) {
+  // GA: gathered A rows (p.row_token), persistent tiles only.
+  static_assert(!GA || !STREAMK, "gathered rows with persistent tiles");
   // BK: K slice per pipeline stage; STAGES: LDS ring depth (STAGES-1 slices in flight).
   // Q8: B0/B1 are int8 with per-column scales S0/S1 (weight-only 8-bit experts).
   constexpr int WB = Q8 ? 1 : 2;            // bytes per B element
@@ -380,8 +382,11 @@ __global__ __launch_bounds__(512, 1) void k_gemm_bf16(const GemmParams p) {
   } else {
     units = sh.rounds + (slot < sh.tail * sh.S ? 1 : 0);
   }
-  for (int u = 0; u < units; ++u) {
-    int L, kb = 0, ke = nk, pslot = -1;
+  // K range, tile index and partial slot of unit u.
+  auto unit_of = [&](int u, int& L, int& kb, int& ke, int& pslot) {
+    kb = 0;
+    ke = nk;
+    pslot = -1;
     if constexpr (STREAMK) {
       if (u < dp_rounds) {
         L = blockIdx.x + u * sk.stride;
@@ -402,6 +407,22 @@ __global__ __launch_bounds__(512, 1) void k_gemm_bf16(const GemmParams p) {
       ke = (piece + 1) * nk / sh.S;
       if (sh.S > 1) pslot = xcd * nslot + slot;
     }
+  };
+  // Gathered A (p.row_token, persistent tiles only): A row r of the product is row
+  // row_token[r] of p.A. Lane's A copy q covers row A_RPC (A_CP wid + q) + lane / A_CPR of
+  // the tile; its token is read one tile ahead, before the epilogue of the previous tile.
+  auto load_tokens = [&](const Tile& t, int (&tk)[A_CP]) {
+#pragma unroll
+    for (int q = 0; q < A_CP; ++q) {
+      const int row = A_RPC * (A_CP * wid + q) + lane / A_CPR;
+      tk[q] = p.row_token[t.row_base + min(row, t.mcount - 1)];
+    }
+  };
+  int tok_next[A_CP];
+  int tok_unit = -1;  // unit whose tokens tok_next holds
+  for (int u = 0; u < units; ++u) {
+    int L, kb, ke, pslot;
+    unit_of(u, L, kb, ke, pslot);
     Tile tl;
     if (!tile_of<BM, BNF>(p, ts, L, tl)) continue;
 
@@ -410,12 +431,28 @@ __global__ __launch_bounds__(512, 1) void k_gemm_bf16(const GemmParams p) {
     const int mlast = tl.mcount - 1;  // rows past the expert's count re-read a valid row
 
     const bf16* a_src[A_CP];
+    if constexpr (GA) {
+      int tok[A_CP];
+      if (tok_unit == u) {
 #pragma unroll
-    for (int q = 0; q < A_CP; ++q) {
-      const int c = A_CP * wid + q;
-      const int row = A_RPC * c + lane / A_CPR;
-      const int lc = (lane % A_CPR) ^ ((row / A_RPB) % A_CPR);
-      a_src[q] = Ag + (int64_t)min(row, mlast) * K + 8 * lc;
+        for (int q = 0; q < A_CP; ++q) tok[q] = tok_next[q];
+      } else {
+        load_tokens(tl, tok);
+      }
+#pragma unroll
+      for (int q = 0; q < A_CP; ++q) {
+        const int row = A_RPC * (A_CP * wid + q) + lane / A_CPR;
+        const int lc = (lane % A_CPR) ^ ((row / A_RPB) % A_CPR);
+        a_src[q] = reinterpret_cast<const bf16*>(p.A) + (int64_t)tok[q] * K + 8 * lc;
+      }
+    } else {
+#pragma unroll
+      for (int q = 0; q < A_CP; ++q) {
+        const int c = A_CP * wid + q;
+        const int row = A_RPC * c + lane / A_CPR;
+        const int lc = (lane % A_CPR) ^ ((row / A_RPB) % A_CPR);
+        a_src[q] = Ag + (int64_t)min(row, mlast) * K + 8 * lc;
+      }
     }
     const char* b_src[B_CP];  // byte addresses
 #pragma unroll
@@ -588,6 +625,18 @@ __global__ __launch_bounds__(512, 1) void k_gemm_bf16(const GemmParams p) {
     }
     wait_vmcnt<0>();
     __syncthreads();  // every wave done reading the ring before the next tile refills it
+    if constexpr (GA) {
+      // tokens of the next unit that has a tile, requested before this tile's stores
+      for (int un = u + 1; un < units; ++un) {
+        int L2, kb2, ke2, ps2;
+        unit_of(un, L2, kb2, ke2, ps2);
+        Tile t2;
+        if (!tile_of<BM, BNF>(p, ts, L2, t2)) continue;
+        load_tokens(t2, tok_next);
+        tok_unit = un;
+        break;
+      }
+    }
 
     if (pslot >= 0) {
       // A K piece of a tile: keep the raw fp32 accumulators of the rows below the expert's
@@ -716,7 +765,15 @@ hipError_t launch_act(const GemmParams& p, int64_t bound, hipStream_t s) {
                        grid);
   } else {
     const int grid = persistent_grid(bound);
-    hipLaunchKernelGGL((k_gemm_bf16<BM, BNF, NB, ACT, BK, STAGES, false, Q8>), dim3(grid), dim3(512), 0, s, p);
+    bool gathered = false;
+    if constexpr (NB == 2) {
+      if (p.row_token != nullptr) {
+        hipLaunchKernelGGL((k_gemm_bf16<BM, BNF, NB, ACT, BK, STAGES, false, Q8, true>), dim3(grid), dim3(512), 0, s, p);
+        gathered = true;
+      }
+    }
+    if (!gathered)
+      hipLaunchKernelGGL((k_gemm_bf16<BM, BNF, NB, ACT, BK, STAGES, false, Q8>), dim3(grid), dim3(512), 0, s, p);
     if (p.partial != nullptr)
       hipLaunchKernelGGL((k_gemm_tail_reduce<BM, BNF, NB, ACT, BK, Q8>), dim3(fixup_grid(grid)), dim3(256), 0, s, p,
                          grid / kXcds);
@@ -754,7 +811,10 @@ bool skinny(const FfnArgs& a) { return a.partial != nullptr && a.max_rows_per_ex
 
 }  // namespace
 
+bool expert_up_gathers(const FfnArgs& a, bool bf16_io) { return bf16_io && a.s1 == nullptr && !skinny(a); }
+
 hipError_t launch_expert_up(const FfnArgs& a, bool bf16_io, hipStream_t s) {
+  if (a.x_row_token != nullptr && !expert_up_gathers(a, bf16_io)) return hipErrorInvalidValue;
   if (!bf16_io) return launch_gemm_f32(a, true, s);
   if (a.s1 != nullptr) {
     // int8 weights: 128-column tiles; the halved B bytes per slice allow deeper rings.
@@ -782,7 +842,8 @@ hipError_t launch_expert_up(const FfnArgs& a, bool bf16_io, hipStream_t s) {
     return launch_bf16<kSkinnyRows, 128, 2, 64, 4, true>(p, a.act, max_m_tiles(a, kSkinnyRows), s);
   }
   constexpr int BM = 256, BNF = 128;
-  GemmParams p{a.x_perm, a.w1, a.w2, a.h, a.offsets, a.counts, a.E, a.D, a.F, a.F / BNF, a.rows, a.partial, kSplitMax};
+  GemmParams p{a.x_perm, a.w1, a.w2, a.h, a.offsets, a.counts, a.E, a.D, a.F, a.F / BNF, a.rows, a.partial, kSplitMax,
+               nullptr, nullptr, a.x_row_token};
   return launch_bf16<BM, BNF, 2>(p, a.act, max_m_tiles(a, BM), s);
 }
 

@@ -29,6 +29,8 @@ struct GemmParams {
   int split_max;    // most K splits of one tile
   const float* S0;  // [E, N] column scales of int8 B0 (weight-only 8-bit experts; else null)
   const float* S1;  // [E, N] column scales of int8 B1
+  const int32_t* row_token;  // or null: A row r of the product is row row_token[r] of A
+                             // (persistent tiles only; rows past an expert's count unread)
 };
 
 struct Tile {

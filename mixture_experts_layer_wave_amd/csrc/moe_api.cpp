@@ -119,12 +119,12 @@ int do_route(const moe_desc* d, const void* x, const float* w_r, const float* bi
 int do_dispatch(const moe_desc* d, const void* x, const int32_t* idx, const float* gate, int32_t* load,
                 int32_t* counts, int32_t* offsets, int32_t* row_of, uint8_t* dropped, float* gate_eff,
                 int32_t* token_of_row, void* x_perm, void* scratch, hipStream_t st,
-                const RouterArgs* route = nullptr);
+                const RouterArgs* route = nullptr, bool gather = true);
 
 int do_route_dispatch(const moe_desc* d, const void* x, const float* w_r, const float* bias, const float* noise,
                       int32_t* idx, float* gate, int32_t* load, int32_t* counts, int32_t* offsets, int32_t* row_of,
                       uint8_t* dropped, float* gate_eff, int32_t* token_of_row, void* x_perm, void* scratch,
-                      hipStream_t st) {
+                      hipStream_t st, bool gather = true) {
   int64_t rows;
   int rc = rows_of(d, &rows);
   if (rc) return rc;
@@ -135,7 +135,7 @@ int do_route_dispatch(const moe_desc* d, const void* x, const float* w_r, const 
     rc = status_of(launch_router(ra, d->dtype == MOE_DT_BF16, st));
     if (rc) return rc;
     return do_dispatch(d, x, idx, gate, load, counts, offsets, row_of, dropped, gate_eff, token_of_row, x_perm,
-                       scratch, st);
+                       scratch, st, nullptr, gather);
   }
   rc = status_of(launch_router_split(ra, st));
   if (rc) return rc;
@@ -145,7 +145,8 @@ int do_route_dispatch(const moe_desc* d, const void* x, const float* w_r, const 
 
 int do_dispatch(const moe_desc* d, const void* x, const int32_t* idx, const float* gate, int32_t* load,
                 int32_t* counts, int32_t* offsets, int32_t* row_of, uint8_t* dropped, float* gate_eff,
-                int32_t* token_of_row, void* x_perm, void* scratch, hipStream_t st, const RouterArgs* route) {
+                int32_t* token_of_row, void* x_perm, void* scratch, hipStream_t st, const RouterArgs* route,
+                bool gather) {
   int64_t C, rows;
   int rc = capacity_of(d, &C);
   if (rc) return rc;
@@ -173,7 +174,7 @@ int do_dispatch(const moe_desc* d, const void* x, const int32_t* idx, const floa
   if (d->N <= kDispatchTokens && rows <= kSmallRows) return status_of(launch_dispatch_small(a, g, st));
   hipError_t e = launch_dispatch(a, st);
   if (e != hipSuccess) return MOE_E_HIP;
-  return status_of(launch_gather(g, st));
+  return gather ? status_of(launch_gather(g, st)) : MOE_OK;
 }
 
 // Column scales of int8 expert weights (all null: weights in the layer dtype).
@@ -185,8 +186,9 @@ struct Scales {
 
 FfnArgs ffn_args(const moe_desc* d, int64_t C, int64_t rows, const void* x_perm, const int32_t* offsets,
                  const int32_t* counts, const void* w1, const void* w2, const void* w3, void* h, void* y_perm,
-                 void* scratch, Scales sc) {
+                 void* scratch, Scales sc, const int32_t* x_row_token = nullptr) {
   FfnArgs a{};
+  a.x_row_token = x_row_token;
   a.s1 = sc.s1; a.s2 = sc.s2; a.s3 = sc.s3;
   if (d->dtype == MOE_DT_BF16) a.partial = at<float>(scratch, scratch_layout(d->N, d->D, d->E, d->k, true).partial);
   a.x_perm = x_perm; a.offsets = offsets; a.counts = counts; a.w1 = w1; a.w2 = w2; a.w3 = w3;
@@ -197,15 +199,16 @@ FfnArgs ffn_args(const moe_desc* d, int64_t C, int64_t rows, const void* x_perm,
 }
 
 // which: 1 = up only, 2 = down only, 3 = both
+// x_row_token non-null: x_perm is x and the up-projection gathers its rows from it.
 int do_ffn(const moe_desc* d, const void* x_perm, const int32_t* offsets, const int32_t* counts, const void* w1,
            const void* w2, const void* w3, void* h, void* y_perm, void* scratch, int which, hipStream_t st,
-           Scales sc = Scales{nullptr, nullptr, nullptr}) {
+           Scales sc = Scales{nullptr, nullptr, nullptr}, const int32_t* x_row_token = nullptr) {
   int64_t C, rows;
   int rc = capacity_of(d, &C);
   if (rc) return rc;
   rc = rows_of(d, &rows);
   if (rc) return rc;
-  const FfnArgs a = ffn_args(d, C, rows, x_perm, offsets, counts, w1, w2, w3, h, y_perm, scratch, sc);
+  const FfnArgs a = ffn_args(d, C, rows, x_perm, offsets, counts, w1, w2, w3, h, y_perm, scratch, sc, x_row_token);
   const bool bf = d->dtype == MOE_DT_BF16;
   if (which & 1) {
     if (launch_expert_up(a, bf, st) != hipSuccess) return MOE_E_HIP;
@@ -446,13 +449,24 @@ static int forward_impl(const moe_desc* d, const void* x, const float* w_r, cons
   if (workspace_bytes < L.total) return MOE_E_WORKSPACE;
   hipStream_t st = (hipStream_t)stream;
   void* ws = workspace;
+  // Beyond the single-launch dispatch of small batches, the up-projection reads the token
+  // rows of x directly (through token_of_row) when it can, and x_perm is not materialised.
+  int64_t C;
+  rc = capacity_of(d, &C);
+  if (rc) return rc;
+  const bool small = d->N <= kDispatchTokens && rows <= kSmallRows;
+  const bool gathered = !small && expert_up_gathers(ffn_args(d, C, rows, x, nullptr, nullptr, w1, w2, w3, nullptr,
+                                                             nullptr, at<void>(ws, L.scratch), sc),
+                                                    d->dtype == MOE_DT_BF16);
   rc = do_route_dispatch(d, x, w_r, logit_bias, noise, at<int32_t>(ws, L.topk_idx), at<float>(ws, L.topk_gate),
                          at<int32_t>(ws, L.load), at<int32_t>(ws, L.counts), at<int32_t>(ws, L.offsets),
                          at<int32_t>(ws, L.row_of), at<uint8_t>(ws, L.dropped), at<float>(ws, L.gate_eff),
-                         at<int32_t>(ws, L.token_of_row), at<void>(ws, L.x_perm), at<void>(ws, L.scratch), st);
+                         at<int32_t>(ws, L.token_of_row), at<void>(ws, L.x_perm), at<void>(ws, L.scratch), st,
+                         !gathered);
   if (rc) return rc;
-  rc = do_ffn(d, at<void>(ws, L.x_perm), at<int32_t>(ws, L.offsets), at<int32_t>(ws, L.counts), w1, w2, w3,
-              at<void>(ws, L.h), at<void>(ws, L.y_perm), at<void>(ws, L.scratch), 3, st, sc);
+  rc = do_ffn(d, gathered ? x : at<void>(ws, L.x_perm), at<int32_t>(ws, L.offsets), at<int32_t>(ws, L.counts), w1,
+              w2, w3, at<void>(ws, L.h), at<void>(ws, L.y_perm), at<void>(ws, L.scratch), 3, st, sc,
+              gathered ? at<int32_t>(ws, L.token_of_row) : nullptr);
   if (rc) return rc;
   return do_combine(d, at<void>(ws, L.y_perm), at<int32_t>(ws, L.row_of), at<float>(ws, L.gate_eff), y, st);
 }

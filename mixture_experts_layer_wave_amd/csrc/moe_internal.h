@@ -167,9 +167,14 @@ struct FfnArgs {
   int64_t max_rows_per_expert;  // host bound on counts[e] (N, or C when padded)
   int D, F, E, act;
   float* partial;           // scratch for split-K partial tiles (kGemmPartialBytes)
+  const int32_t* x_row_token;  // or null: x_perm is then x [N,D] and expert-buffer row r of
+                               // the up-projection is x row x_row_token[r] (gathered rows)
 };
 // Gated up-projection (h) and down-projection (y_perm) of every expert's rows.
 hipError_t launch_expert_up(const FfnArgs& a, bool bf16, hipStream_t s);
+// True if the up-projection for these arguments can read its rows gathered from x
+// (bf16 activations and weights, tiles of more than 64 rows).
+bool expert_up_gathers(const FfnArgs& a, bool bf16);
 hipError_t launch_expert_down(const FfnArgs& a, bool bf16, hipStream_t s);
 
 // ---- combine --------------------------------------------------------------------------

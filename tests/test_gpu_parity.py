@@ -410,6 +410,9 @@ def test_layer_mid_size(orc, cfg):
 def test_layer_bitwise_reproducible_and_equal_to_steps(orc, cfg):
     inp = inputs.make_inputs(cfg)
     layer = B.MoELayer(cfg, inp)
+    sentinel = 0x7F7F if cfg["dtype"] == "bf16" else 0x7F7F7F7F
+    xp_bits = layer.views()["x_perm"].view(torch.int16 if cfg["dtype"] == "bf16" else torch.int32)
+    xp_bits.fill_(sentinel)
     y1 = layer.forward().clone()
     y2 = layer.forward().clone()
     assert torch.equal(y1, y2)
@@ -432,8 +435,21 @@ def test_layer_bitwise_reproducible_and_equal_to_steps(orc, cfg):
     # the forward's routing and dispatch intermediates equal the separate calls' bit for bit
     v = layer.views()
     assert torch.equal(v["topk_idx"], idx) and torch.equal(v["topk_gate"], gate)
-    for name in ("load", "counts", "offsets", "row_of", "dropped", "gate_eff", "token_of_row", "x_perm"):
+    for name in ("load", "counts", "offsets", "row_of", "dropped", "gate_eff"):
         assert torch.equal(v[name], out[name]), name
+    # Past the single-launch dispatch of small batches (N <= 256), bf16 layers with bf16
+    # weights whose up-projection runs 256-row tiles read the token rows of x through
+    # token_of_row and leave x_perm unwritten (padding entries of token_of_row unspecified).
+    small = N <= 256 and rows <= 4096
+    gathered = cfg["dtype"] == "bf16" and cfg.get("weight_dtype", "same") != "int8" and not small and \
+        (min(rows // E, N) if cfg["capacity_mode"] == "padded" else N) > 64
+    valid = out["token_of_row"] >= 0
+    assert torch.equal(v["token_of_row"][valid], out["token_of_row"][valid])
+    if gathered:
+        assert torch.all(xp_bits == sentinel), "x_perm written by a gathered forward"
+    else:
+        assert torch.equal(v["token_of_row"], out["token_of_row"])
+        assert torch.equal(v["x_perm"], out["x_perm"])
     # and so do the statistics (probability block sums from the router, counts from dispatch)
     B.moe_dispatch(d, layer.x, idx, gate, out["load"], out["counts"], out["offsets"], out["row_of"], out["dropped"],
                    out["gate_eff"], out["token_of_row"], out["x_perm"], sc)
