@@ -83,6 +83,8 @@ def stage_of(name: str) -> str:
         return "dispatch"
     if base == "k_route_dispatch_small":  # launched by moe_forward only (route epilogue + dispatch)
         return "forward"
+    if base == "k_gemm_bf16" and len(args) >= 9 and args[8] == 1:  # gathered rows: moe_forward only
+        return "forward"
     if base in ("k_gemm_bf16", "k_gemm_tail_reduce", "k_gemm_streamk_reduce") and len(args) >= 3:
         return "expert_up" if args[2] == 2 else "expert_down"
     if base == "k_gemm_f32":
