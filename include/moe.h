@@ -170,10 +170,10 @@ MOE_API int moe_workspace_size(const moe_desc* desc, size_t* bytes);
 /* Byte offsets of the intermediates inside a moe_forward workspace, so that a caller
  * can inspect them after moe_forward returns (the workspace keeps the last call's
  * contents). Layout of each is as in the step functions below. Exception: for bf16
- * layers with bf16 expert weights, N > 256 (or more than 4096 expert-buffer rows) whose experts can hold more
- * than 64 rows (N, or C when padded), moe_forward's up-projection reads the token rows of
- * x directly through token_of_row, so x_perm is not written and the padding entries of
- * token_of_row (PADDED) are unspecified. */
+ * layers with bf16 expert weights, N > 256 (or more than 4096 expert-buffer rows) and
+ * experts that can hold more than 64 rows (N, or C when padded), moe_forward's
+ * up-projection reads the token rows of x directly through token_of_row, so x_perm is
+ * not written and the padding entries of token_of_row (PADDED) are unspecified. */
 typedef struct moe_ws_layout {
   size_t scratch;        /* moe_scratch_size bytes                                      */
   size_t topk_idx;       /* int32 [N,k]                                                 */
@@ -276,7 +276,9 @@ MOE_API int moe_combine(const moe_desc* desc, const void* y_perm, const int32_t*
 
 /* The whole layer: moe_route -> moe_dispatch -> moe_expert_ffn -> moe_combine with every
  * intermediate in `workspace` (moe_workspace_size bytes, laid out as
- * moe_workspace_layout reports). Arguments as in the step functions; y [N,D] dtype. */
+ * moe_workspace_layout reports; see there for when x_perm is not materialised).
+ * Arguments as in the step functions; y [N,D] dtype, equal bit for bit to the step
+ * functions' result. */
 MOE_API int moe_forward(const moe_desc* desc, const void* x, const float* w_r, const float* logit_bias,
                 const float* noise, const void* w1, const void* w2, const void* w3, void* y,
                 void* workspace, size_t workspace_bytes, void* stream);
