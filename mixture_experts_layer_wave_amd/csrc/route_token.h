@@ -93,6 +93,105 @@ __device__ __forceinline__ void route_token(const RouterArgs& a, int64_t t, cons
   }
 }
 
+// route_token for E <= 64 on four lanes: the quad (lanes 4i .. 4i + 3 of a wave, part =
+// lane % 4) holds one token, each lane the logits l of experts 16 part .. 16 part + 15.
+// Same steps and selection rule as route_token; the maximum and the selection reduce over
+// the quad, and the probability sum adds the lanes' partial sums as (s0 + s1) + (s2 + s3),
+// so every lane of the quad ends with the same sel and gt. p: this lane's probabilities.
+// nz: this lane's 16 noise values (unused without noise). Outputs are written only when
+// `valid`. All four lanes must call it together.
+template <int KM = kMaxK>
+__device__ __forceinline__ void route_token_quad(const RouterArgs& a, int64_t t, int part, bool valid,
+                                                 const float* nz, float (&l)[16], float (&p)[16],
+                                                 int (&sel)[kMaxK], float (&gt)[kMaxK]) {
+  static_assert(KM >= 1 && KM <= kMaxK, "k bound");
+  const int E = a.E;
+  const int e0 = 16 * part;
+  const int lane = lane_id();
+  const int qbase = lane & ~3;
+  if (a.noisy == 2) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      if (e0 + i < E) l[i] += nz[i];  // logit' = fl32(logit + noise)
+  }
+  float mx = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) mx = (e0 + i < E) ? fmaxf(mx, l[i]) : mx;
+  mx = fmaxf(mx, __shfl_xor(mx, 1));
+  mx = fmaxf(mx, __shfl_xor(mx, 2));
+  float sum = 0.f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    p[i] = (e0 + i < E) ? expf(l[i] - mx) : 0.f;
+    sum += p[i];
+  }
+  sum += __shfl_xor(sum, 1);  // lanes 0, 1: s0 + s1; lanes 2, 3: s2 + s3
+  sum += __shfl_xor(sum, 2);  // (s0 + s1) + (s2 + s3) on every lane (fp32 add commutes)
+#pragma unroll
+  for (int i = 0; i < 16; ++i) p[i] = p[i] / sum;
+
+  if (valid && a.logits_out)
+    for (int i = 0; i < 16 && e0 + i < E; ++i) a.logits_out[t * E + e0 + i] = pick(l, i);
+  if (valid && a.probs_out)
+    for (int i = 0; i < 16 && e0 + i < E; ++i) a.probs_out[t * E + e0 + i] = pick(p, i);
+
+  float z[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) z[i] = l[i];
+  if (a.noisy == 1) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) z[i] = (e0 + i < E) ? l[i] + nz[i] : 0.f;
+  }
+
+  uint64_t chosen = 0;
+#pragma unroll
+  for (int j = 0; j < KM; ++j) {
+    sel[j] = 0;
+    if (j < a.k) {
+      const bool use_z = (j > 0) && a.noisy == 1;
+      int best = -1;
+      float bv = 0.f;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int e = e0 + i;
+        const float v = use_z ? z[i] : l[i];
+        const bool cand = (e < E) && !((chosen >> e) & 1ull);
+        if (cand && (best < 0 || v > bv)) { best = e; bv = v; }
+      }
+      // quad reduction: larger value wins, equal values go to the lower expert index
+#pragma unroll
+      for (int off = 1; off <= 2; off <<= 1) {
+        const int ob = __shfl_xor(best, off);
+        const float ov = __shfl_xor(bv, off);
+        if (ob >= 0 && (best < 0 || ov > bv || (ov == bv && ob < best))) { best = ob; bv = ov; }
+      }
+      sel[j] = best;
+      chosen |= 1ull << best;
+    }
+  }
+
+  // value of expert sel (held by quad lane sel / 16) on every lane of the quad
+  auto fetch = [&](const float (&v)[16], int e) { return __shfl(pick(v, e & 15), qbase + (e >> 4)); };
+  if (a.mode == 0) {
+#pragma unroll
+    for (int j = 0; j < KM; ++j) {
+      const float g = fetch(p, sel[j]);
+      gt[j] = (j < a.k) ? g : 0.f;
+    }
+  } else {
+    const float ref = fetch(l, sel[0]);
+    float s2 = 0.f;
+#pragma unroll
+    for (int j = 0; j < KM; ++j) {
+      const float lj = fetch(l, sel[j]);
+      gt[j] = (j < a.k) ? expf(lj - ref) : 0.f;
+      s2 += gt[j];
+    }
+#pragma unroll
+    for (int j = 0; j < KM; ++j) gt[j] = gt[j] / s2;
+  }
+}
+
 // Stores the selection and gates of token t (a.k <= KM).
 template <int KM = kMaxK>
 __device__ __forceinline__ void store_topk(const RouterArgs& a, int64_t t, const int (&sel)[kMaxK],

@@ -354,7 +354,24 @@ __global__ __launch_bounds__(256) void k_router_epi(const RouterArgs a, RouterSp
     for (int i = tid; i < nitem; i += 256) nz_s[i / E][i % E] = a.noise[t0 * E + i];
   if (tid < EP) b_s[tid] = (a.bias != nullptr && tid < E) ? a.bias[tid] : 0.f;
   __syncthreads();
-  if (tid < 64) {  // wave 0: one token per lane
+  if constexpr (EP == 64) {
+    // four lanes per token (16 experts each): all four waves, a quarter of the chain
+    const int tok = tid >> 2, part = tid & 3;
+    const int64_t t = t0 + tok;
+    const bool valid = tok < ntok;
+    float l[16], p[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int e = 16 * part + i;
+      l[i] = (valid && e < E) ? l_s[tok][e] + b_s[e] : 0.f;
+    }
+    int sel[kMaxK];
+    float gt[kMaxK];
+    route_token_quad<KM>(a, t, part, valid, &nz_s[tok][16 * part], l, p, sel, gt);
+    if (valid && part == 0) store_topk<KM>(a, t, sel, gt);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) ps_s[16 * part + i][tok] = valid ? p[i] : 0.f;
+  } else if (tid < 64) {  // wave 0: one token per lane
     const int64_t t = t0 + tid;
     const bool valid = tid < ntok;
     float l[EP], p[EP];

@@ -78,6 +78,36 @@ def test_route_from_identical_logits(orc, N, E, k, dist, mode, noisy):
     np.testing.assert_allclose(host(probs), r.probs, rtol=2e-6, atol=1e-7)
 
 
+@pytest.mark.parametrize("N,E,k", [(300, 64, 2), (300, 40, 8), (97, 64, 1), (300, 33, 3), (1000, 16, 2)])
+@pytest.mark.parametrize("mode", ["softmax_topk", "topk_softmax"])
+@pytest.mark.parametrize("noisy", [False, "second", "all"])
+def test_route_split_epilogue(orc, N, E, k, mode, noisy):
+    """The split-K router's own epilogue (bf16 x with scratch; four lanes per token when
+    E > 32) against the oracle routing the logits that router produced: identical
+    selection, gates and probabilities within fp32 rounding."""
+    if noisy == "second" and k < 2:
+        pytest.skip("noisy second choice needs k >= 2")
+    cfg = _routing_cfg(N, E, k, mode, noisy, D=256)
+    d = B.make_desc(cfg)
+    seed = 7 * N + E + k
+    x = inputs.make_rows(N, 256, seed, "bf16")
+    w_r = inputs.make_logits(256, E, seed + 2, std=1.0 / 16)  # N(0, 1/D) router weights
+    noise = inputs.make_logits(N, E, seed + 1) if noisy else None
+    idx = torch.empty((N, k), dtype=torch.int32, device=DEV)
+    gate = torch.empty((N, k), dtype=torch.float32, device=DEV)
+    probs = torch.empty((N, E), dtype=torch.float32, device=DEV)
+    lout = torch.empty((N, E), dtype=torch.float32, device=DEV)
+    sc = torch.empty(B.moe_scratch_size(d), dtype=torch.uint8, device=DEV)
+    B.moe_route(d, _dev(x), _dev(w_r), None, _dev(noise), None, lout, probs, idx, gate, sc)
+    torch.cuda.synchronize()
+    # logits_out holds the logits the selection used: fl32(logit + noise) under noisy_all
+    used = host(lout)
+    r = orc.route(used, k, mode, noise=noise if noisy == "second" else None)
+    assert np.array_equal(host(idx), r.idx), "selection differs from the oracle on the router's own logits"
+    np.testing.assert_allclose(host(gate), r.gate, rtol=2e-6, atol=1e-7)
+    np.testing.assert_allclose(host(probs), r.probs, rtol=2e-6, atol=1e-7)
+
+
 # ---------------------------------------------------------------------------------------
 # Router GEMM: fp32 logits against the exact (fp64) logits
 # ---------------------------------------------------------------------------------------
