@@ -512,29 +512,46 @@ __global__ __launch_bounds__(256) void k_route_dispatch_small(const RouterArgs r
     for (int64_t i = tid; i < items; i += 256) nz_s[i / E][i % E] = ra.noise[i];
   if (tid < EP) b_s[tid] = (ra.bias != nullptr && tid < E) ? ra.bias[tid] : 0.f;
   __syncthreads();
+  // Token epilogue on four lanes per token (EP / 4 experts each), 64 tokens per pass, as
+  // k_router_epi does; each token's selection and gates go through LDS to its dispatch
+  // thread (thread t holds token t below).
+  __shared__ int e_s[kDispatchTokens][KM];
+  __shared__ float g_s[kDispatchTokens][KM];
+  constexpr int EPL = EP / 4;
+  for (int64_t t0 = 0; t0 < ra.N; t0 += 64) {
+    const int tok = (int)t0 + (tid >> 2), part = tid & 3;
+    const bool tv = tok < ra.N;
+    float l[EPL], p[EPL];
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) {
+      const int x = EPL * part + i;
+      l[i] = (tv && x < E) ? l_s[tok][x] + b_s[x] : 0.f;
+    }
+    int sel[kMaxK];
+    float gq[kMaxK];
+    route_token_quad<EPL, KM>(ra, tok, part, tv, &nz_s[tok][EPL * part], l, p, sel, gq);
+    if (tv && part == 0) {
+#pragma unroll
+      for (int j = 0; j < KM; ++j) {
+        e_s[tok][j] = sel[j];
+        g_s[tok][j] = gq[j];
+      }
+      if (blockIdx.x == 0) store_topk<KM>(ra, tok, sel, gq);
+    }
+#pragma unroll
+    for (int i = 0; i < EPL; ++i)
+      if (tok < kDispatchTokens) ps_s[EPL * part + i][tok] = tv ? p[i] : 0.f;
+  }
+  __syncthreads();
   const int64_t t = tid;
   const bool valid = t < ra.N;
   int e[kMaxK];
   float gt[kMaxK];
 #pragma unroll
-  for (int j = 0; j < kMaxK; ++j) { e[j] = -1; gt[j] = 0.f; }
-  {
-    float l[EP], p[EP];
-#pragma unroll
-    for (int x = 0; x < EP; ++x) {
-      l[x] = (valid && x < E) ? l_s[tid][x] + b_s[x] : 0.f;
-      p[x] = 0.f;
-    }
-    if (valid) {
-      route_token<EP, KM>(ra, t, ra.noise != nullptr ? nz_s[tid] : nullptr, l, p, e, gt);
-      if (blockIdx.x == 0) store_topk<KM>(ra, t, e, gt);
-    }
-#pragma unroll
-    for (int x = 0; x < EP; ++x) ps_s[x][tid] = valid ? p[x] : 0.f;
+  for (int j = 0; j < kMaxK; ++j) {
+    e[j] = (valid && j < KM && j < a.k) ? e_s[t][j < KM ? j : 0] : -1;
+    gt[j] = (valid && j < KM && j < a.k) ? g_s[t][j < KM ? j : 0] : 0.f;
   }
-#pragma unroll
-  for (int j = 0; j < kMaxK; ++j)
-    if (j >= a.k) e[j] = -1;
   if (ra.psum != nullptr) {
     __syncthreads();
     // block sums of the probabilities per kRouterTokens tokens, in token order

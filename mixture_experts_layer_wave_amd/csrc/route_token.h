@@ -93,54 +93,54 @@ __device__ __forceinline__ void route_token(const RouterArgs& a, int64_t t, cons
   }
 }
 
-// route_token for E <= 64 on four lanes: the quad (lanes 4i .. 4i + 3 of a wave, part =
-// lane % 4) holds one token, each lane the logits l of experts 16 part .. 16 part + 15.
-// Same steps and selection rule as route_token; the maximum and the selection reduce over
-// the quad, and the probability sum adds the lanes' partial sums as (s0 + s1) + (s2 + s3),
-// so every lane of the quad ends with the same sel and gt. p: this lane's probabilities.
-// nz: this lane's 16 noise values (unused without noise). Outputs are written only when
-// `valid`. All four lanes must call it together.
-template <int KM = kMaxK>
+// route_token on four lanes: the quad (lanes 4i .. 4i + 3 of a wave, part = lane % 4)
+// holds one token, each lane the logits l of experts EPL part .. EPL part + EPL - 1 (E <=
+// 4 EPL). Same steps and selection rule as route_token; the maximum and the selection
+// reduce over the quad, and the probability sum adds the lanes' partial sums as
+// (s0 + s1) + (s2 + s3), so every lane of the quad ends with the same sel and gt.
+// p: this lane's probabilities. nz: this lane's EPL noise values (unused without noise).
+// Outputs are written only when `valid`. All four lanes must call it together.
+template <int EPL, int KM = kMaxK>
 __device__ __forceinline__ void route_token_quad(const RouterArgs& a, int64_t t, int part, bool valid,
-                                                 const float* nz, float (&l)[16], float (&p)[16],
+                                                 const float* nz, float (&l)[EPL], float (&p)[EPL],
                                                  int (&sel)[kMaxK], float (&gt)[kMaxK]) {
   static_assert(KM >= 1 && KM <= kMaxK, "k bound");
   const int E = a.E;
-  const int e0 = 16 * part;
+  const int e0 = EPL * part;
   const int lane = lane_id();
   const int qbase = lane & ~3;
   if (a.noisy == 2) {
 #pragma unroll
-    for (int i = 0; i < 16; ++i)
+    for (int i = 0; i < EPL; ++i)
       if (e0 + i < E) l[i] += nz[i];  // logit' = fl32(logit + noise)
   }
   float mx = -INFINITY;
 #pragma unroll
-  for (int i = 0; i < 16; ++i) mx = (e0 + i < E) ? fmaxf(mx, l[i]) : mx;
+  for (int i = 0; i < EPL; ++i) mx = (e0 + i < E) ? fmaxf(mx, l[i]) : mx;
   mx = fmaxf(mx, __shfl_xor(mx, 1));
   mx = fmaxf(mx, __shfl_xor(mx, 2));
   float sum = 0.f;
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
+  for (int i = 0; i < EPL; ++i) {
     p[i] = (e0 + i < E) ? expf(l[i] - mx) : 0.f;
     sum += p[i];
   }
   sum += __shfl_xor(sum, 1);  // lanes 0, 1: s0 + s1; lanes 2, 3: s2 + s3
   sum += __shfl_xor(sum, 2);  // (s0 + s1) + (s2 + s3) on every lane (fp32 add commutes)
 #pragma unroll
-  for (int i = 0; i < 16; ++i) p[i] = p[i] / sum;
+  for (int i = 0; i < EPL; ++i) p[i] = p[i] / sum;
 
   if (valid && a.logits_out)
-    for (int i = 0; i < 16 && e0 + i < E; ++i) a.logits_out[t * E + e0 + i] = pick(l, i);
+    for (int i = 0; i < EPL && e0 + i < E; ++i) a.logits_out[t * E + e0 + i] = pick(l, i);
   if (valid && a.probs_out)
-    for (int i = 0; i < 16 && e0 + i < E; ++i) a.probs_out[t * E + e0 + i] = pick(p, i);
+    for (int i = 0; i < EPL && e0 + i < E; ++i) a.probs_out[t * E + e0 + i] = pick(p, i);
 
-  float z[16];
+  float z[EPL];
 #pragma unroll
-  for (int i = 0; i < 16; ++i) z[i] = l[i];
+  for (int i = 0; i < EPL; ++i) z[i] = l[i];
   if (a.noisy == 1) {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) z[i] = (e0 + i < E) ? l[i] + nz[i] : 0.f;
+    for (int i = 0; i < EPL; ++i) z[i] = (e0 + i < E) ? l[i] + nz[i] : 0.f;
   }
 
   uint64_t chosen = 0;
@@ -152,7 +152,7 @@ __device__ __forceinline__ void route_token_quad(const RouterArgs& a, int64_t t,
       int best = -1;
       float bv = 0.f;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
+      for (int i = 0; i < EPL; ++i) {
         const int e = e0 + i;
         const float v = use_z ? z[i] : l[i];
         const bool cand = (e < E) && !((chosen >> e) & 1ull);
@@ -170,8 +170,8 @@ __device__ __forceinline__ void route_token_quad(const RouterArgs& a, int64_t t,
     }
   }
 
-  // value of expert sel (held by quad lane sel / 16) on every lane of the quad
-  auto fetch = [&](const float (&v)[16], int e) { return __shfl(pick(v, e & 15), qbase + (e >> 4)); };
+  // value of expert e (held by quad lane e / EPL) on every lane of the quad
+  auto fetch = [&](const float (&v)[EPL], int e) { return __shfl(pick(v, e % EPL), qbase + e / EPL); };
   if (a.mode == 0) {
 #pragma unroll
     for (int j = 0; j < KM; ++j) {

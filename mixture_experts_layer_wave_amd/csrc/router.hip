@@ -354,40 +354,24 @@ __global__ __launch_bounds__(256) void k_router_epi(const RouterArgs a, RouterSp
     for (int i = tid; i < nitem; i += 256) nz_s[i / E][i % E] = a.noise[t0 * E + i];
   if (tid < EP) b_s[tid] = (a.bias != nullptr && tid < E) ? a.bias[tid] : 0.f;
   __syncthreads();
-  if constexpr (EP == 64) {
-    // four lanes per token (16 experts each): all four waves, a quarter of the chain
+  {
+    // four lanes per token (EP / 4 experts each): all four waves, a quarter of the chain
+    constexpr int EPL = EP / 4;
     const int tok = tid >> 2, part = tid & 3;
     const int64_t t = t0 + tok;
     const bool valid = tok < ntok;
-    float l[16], p[16];
+    float l[EPL], p[EPL];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int e = 16 * part + i;
+    for (int i = 0; i < EPL; ++i) {
+      const int e = EPL * part + i;
       l[i] = (valid && e < E) ? l_s[tok][e] + b_s[e] : 0.f;
     }
     int sel[kMaxK];
     float gt[kMaxK];
-    route_token_quad<KM>(a, t, part, valid, &nz_s[tok][16 * part], l, p, sel, gt);
+    route_token_quad<EPL, KM>(a, t, part, valid, &nz_s[tok][EPL * part], l, p, sel, gt);
     if (valid && part == 0) store_topk<KM>(a, t, sel, gt);
 #pragma unroll
-    for (int i = 0; i < 16; ++i) ps_s[16 * part + i][tok] = valid ? p[i] : 0.f;
-  } else if (tid < 64) {  // wave 0: one token per lane
-    const int64_t t = t0 + tid;
-    const bool valid = tid < ntok;
-    float l[EP], p[EP];
-#pragma unroll
-    for (int e = 0; e < EP; ++e) {
-      l[e] = (valid && e < E) ? l_s[tid][e] + b_s[e] : 0.f;
-      p[e] = 0.f;
-    }
-    if (valid) {
-      int sel[kMaxK];
-      float gt[kMaxK];
-      route_token<EP, KM>(a, t, nz_s[tid], l, p, sel, gt);
-      store_topk<KM>(a, t, sel, gt);
-    }
-#pragma unroll
-    for (int e = 0; e < EP; ++e) ps_s[e][tid] = valid ? p[e] : 0.f;
+    for (int i = 0; i < EPL; ++i) ps_s[EPL * part + i][tok] = valid ? p[i] : 0.f;
   }
   if (a.psum == nullptr) return;  // uniform
   __syncthreads();

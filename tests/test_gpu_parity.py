@@ -78,13 +78,14 @@ def test_route_from_identical_logits(orc, N, E, k, dist, mode, noisy):
     np.testing.assert_allclose(host(probs), r.probs, rtol=2e-6, atol=1e-7)
 
 
-@pytest.mark.parametrize("N,E,k", [(300, 64, 2), (300, 40, 8), (97, 64, 1), (300, 33, 3), (1000, 16, 2)])
+@pytest.mark.parametrize("N,E,k", [(300, 64, 2), (300, 40, 8), (97, 64, 1), (300, 33, 3), (1000, 16, 2),
+                                   (300, 8, 2), (65, 4, 3), (200, 5, 2), (129, 24, 4)])
 @pytest.mark.parametrize("mode", ["softmax_topk", "topk_softmax"])
 @pytest.mark.parametrize("noisy", [False, "second", "all"])
 def test_route_split_epilogue(orc, N, E, k, mode, noisy):
-    """The split-K router's own epilogue (bf16 x with scratch; four lanes per token when
-    E > 32) against the oracle routing the logits that router produced: identical
-    selection, gates and probabilities within fp32 rounding."""
+    """The split-K router's own epilogue (bf16 x with scratch; four lanes per token, each
+    with E / 4 experts) against the oracle routing the logits that router produced:
+    identical selection, gates and probabilities within fp32 rounding."""
     if noisy == "second" and k < 2:
         pytest.skip("noisy second choice needs k >= 2")
     cfg = _routing_cfg(N, E, k, mode, noisy, D=256)
