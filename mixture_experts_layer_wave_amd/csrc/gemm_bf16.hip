@@ -32,6 +32,7 @@
 //    spread the weight stream evenly over all compute units.
 //  * The only m-tile of an expert with fewer than BM rows runs a copy of the K loop in
 //    which waves whose rows all lie past the expert's count skip their copies and MFMAs.
+#include <atomic>
 #include <type_traits>
 
 #include "gemm_common.h"
@@ -728,17 +729,22 @@ __global__ __launch_bounds__(256) void k_gemm_streamk_reduce(const GemmParams p,
   }
 }
 
-int g_num_cus = 0;
+// Compute units of the first device asked (a launch size only: every kernel is correct for
+// any grid, so a device with another count runs correctly, just less well balanced).
+// Atomic: host threads may launch concurrently.
+std::atomic<int> g_num_cus{0};
 
 int persistent_grid(int64_t tiles_bound) {
-  if (g_num_cus <= 0) {
+  int cus = g_num_cus.load(std::memory_order_relaxed);
+  if (cus <= 0) {
     int dev = 0, n = 0;
     if (hipGetDevice(&dev) != hipSuccess ||
         hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
       n = 256;
-    g_num_cus = n;
+    g_num_cus.store(n, std::memory_order_relaxed);
+    cus = n;
   }
-  int64_t g = tiles_bound < g_num_cus ? tiles_bound : g_num_cus;
+  int64_t g = tiles_bound < cus ? tiles_bound : cus;
   if (g > (int64_t)kGemmPartialUnits) g = kGemmPartialUnits;
   g = (g + kXcds - 1) / kXcds * kXcds;
   return (int)g;
