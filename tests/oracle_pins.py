@@ -174,6 +174,53 @@ def pin_tie_rule(orc):
     assert r.margin[1] == 0.0 and r.margin[3] == 0.0
 
 
+def pin_margin(orc):
+    """Near-tie margin of a token: the smallest gap, over its k selection steps, between
+    the probability of the expert a step chooses and that of the best expert still
+    unchosen, the probabilities being the softmax over all E of the values that step
+    ranks (clean logits; fl32(logit + noise) for the noisy steps). Each token is built
+    from probability vectors that sum to 1 (logits ln p, noise ln q - ln p), so every
+    step's probabilities are the printed vectors and each expected margin is a
+    difference of two printed entries (up to the fp32 rounding of the logits). The
+    smallest gap is placed at a later step, so a margin taken at step 0 only, on
+    logits instead of probabilities, on the clean values of a noisy step, or against
+    an already chosen runner-up, all fail."""
+    def lg(p):
+        return np.log(np.array([p], np.float64))
+
+    # plain top-k: step gaps 0.5-0.2 and 0.2-0.19 (experts shuffled so the gaps are
+    # between non-adjacent indices)
+    r = orc.route(lg([0.19, 0.5, 0.11, 0.2]), 2, "topk_softmax")
+    assert r.idx.tolist() == [[1, 3]], r.idx
+    _close(r.margin, [0.01], rtol=0, atol=1e-6)
+    r = orc.route(lg([0.19, 0.5, 0.11, 0.2]), 1, "softmax_topk")
+    _close(r.margin, [0.3], rtol=0, atol=1e-6)
+    # k = 3: gaps 0.15, 0.10, 0.01 (the smallest at the last step)
+    r = orc.route(lg([0.06, 0.4, 0.14, 0.25, 0.15]), 3, "softmax_topk")
+    assert r.idx.tolist() == [[1, 3, 4]], r.idx
+    _close(r.margin, [0.01], rtol=0, atol=1e-6)
+    # k = E: the last step has no unchosen expert left; gaps 0.2 and 0.1
+    r = orc.route(lg([0.3, 0.5, 0.2]), 3, "topk_softmax")
+    _close(r.margin, [0.1], rtol=0, atol=1e-6)
+    r = orc.route(lg([1.0]), 1, "topk_softmax")
+    assert np.isinf(r.margin[0]) and r.margin[0] > 0
+    # GShard noisy second choice: step 0 ranks the clean p = (0.4, 0.3, 0.2, 0.1) (gap
+    # 0.1), step 1 the noisy q = (0.1, 0.35, 0.33, 0.22) with expert 0 chosen (gap 0.02);
+    # on the clean values step 1 would give 0.1
+    p = np.array([0.4, 0.3, 0.2, 0.1])
+    q = np.array([0.1, 0.35, 0.33, 0.22])
+    noise = (np.log(q) - np.log(p)).astype(np.float32)[None, :]
+    r = orc.route(lg(p), 2, "topk_softmax", noise=noise)
+    assert r.idx.tolist() == [[0, 1]], r.idx
+    _close(r.margin, [0.02], rtol=0, atol=1e-6)
+    # noisy top-k gating: every step ranks fl32(logit + noise) = ln q; gaps 0.22, 0.01
+    q = np.array([0.1, 0.45, 0.23, 0.22])
+    noise = (np.log(q) - np.log(p)).astype(np.float32)[None, :]
+    r = orc.route(lg(p), 2, "softmax_topk", noise=noise, noise_all=True)
+    assert r.idx.tolist() == [[1, 2]], r.idx
+    _close(r.margin, [0.01], rtol=0, atol=1e-6)
+
+
 def pin_uniform_routing(orc):
     """W_r = 0: p = 1/E, slots (0..k-1) by the tie rule, gates 1/E (mode A) or 1/k (mode
     B), and the balance loss equals 1 ([F2C] §2.2; [SERIES] §7.3)."""

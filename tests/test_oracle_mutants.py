@@ -53,6 +53,11 @@ MUTANTS = {
     "drop_case_b_keeps_gates": ("if (nk == k) gate_eff[t * k + j] = g;",
                                 "if (nk == k || nk == 0) gate_eff[t * k + j] = g;"),
     "bf16_truncated_shift": ("uint32_t u = (uint32_t)bits << 16;", "uint32_t u = (uint32_t)bits << 15;"),
+    "margin_step0_only": ("if (gap < tok_margin) tok_margin = gap;", "if (j == 0 && gap < tok_margin) tok_margin = gap;"),
+    "margin_on_logits": ("double gap = (q[best] - q[second]) / vz;", "double gap = (double)val[best] - (double)val[second];"),
+    "margin_on_clean_values": ("q[e] = exp((double)val[e] - vm); vz += q[e];", "q[e] = exp((double)l32[e] - vm); vz += q[e];"),
+    "margin_runner_up_already_chosen": ("if (!chosen[e] && e != best && (second < 0 || val[e] > val[second])) second = e;",
+                                        "if (e != best && (second < 0 || val[e] > val[second])) second = e;"),
 }
 
 
