@@ -14,7 +14,7 @@ import torch
 
 from mixture_experts_layer_wave_amd import binding as B
 from mixture_experts_layer_wave_amd import configs, inputs
-from parity_util import (MARGIN, TOL_Y, affected_experts, ambiguous_tokens, assert_rows_close, host)
+from parity_util import MARGIN, TOL_Y, ambiguous_tokens, assert_rows_close, host
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -156,6 +156,11 @@ DISPATCH_CASES = [
     # at most 256 tokens: one fused launch while the buffer has at most 4096 rows, else
     # the three-pass path
     (64, 8, 2, 4.0, "none", 0.0, 0), (256, 64, 8, 1.0, "padded", 2.0, 0), (200, 64, 8, 1.0, "padded", 30.0, 0),
+    # more than 512 (segment, 256-token block) entries per expert: the scan's long-sequence
+    # loop (slot-major: k segments; token-major: one segment)
+    (70000, 64, 2, 1.2, "padded", 1.25, 4),   # slot-major 548 entries; token-major 274
+    (20000, 16, 8, 1.0, "padded", 1.0, 0),    # slot-major 632 entries; token-major 79
+    (140000, 8, 2, 0.5, "none", 0.0, 0),      # slot-major 1094 entries; token-major 547
 ]
 
 
@@ -210,6 +215,65 @@ def test_dispatch_from_identical_records(orc, N, E, k, skew, cap, cf, minc, prio
     filled[o.row_of[kept]] = True
     assert np.all(tor[~filled] == -1)
     assert torch.all(xp[torch.from_numpy(~filled)] == 0)
+
+
+def test_route_dispatch_random_tiny(orc):
+    """Seeded random sweep of routing and dispatch on tiny shapes: N <= 300, E 2-64, k 1 to
+    min(E, 8), both gate modes, clean / GShard-noisy second / noisy top-k, no capacity or
+    CF 0.5 / 1 / 1.25 with a minimum capacity, slot- or token-major priority, k or Switch
+    capacity formula, fp32 or bf16 rows, logits with frequent exact ties, Zipf skew or a
+    hot expert. Selection from identical logits and dispatch from identical records must
+    equal the oracle's bit for bit; the first mismatch stops the sweep and names its case."""
+    rng = np.random.default_rng(20261203)
+    n_cases = 400
+    for case in range(n_cases):
+        N = int(rng.integers(1, 301))
+        E = int(rng.integers(2, 65))
+        k = int(rng.integers(1, min(E, 8) + 1))
+        mode = ["softmax_topk", "topk_softmax"][int(rng.integers(2))]
+        noisy = [False, "second", "all"][int(rng.integers(3))]
+        if noisy == "second" and k < 2:
+            noisy = False
+        cf = [None, 0.5, 1.0, 1.25][int(rng.integers(4))]
+        minc = int(rng.choice([0, 1, 4]))
+        prio = ["slot_major", "token_major"][int(rng.integers(2))]
+        formula = ["tokens_k", "tokens"][int(rng.integers(2))]
+        dt = ["bf16", "f32"][int(rng.integers(2))]
+        dist = ["ties", "normal", "zipf", "hot"][int(rng.integers(4))]
+        desc = (f"case {case}: N={N} E={E} k={k} {mode} noisy={noisy} cf={cf} min_cap={minc} {prio} {formula} "
+                f"{dt} {dist}")
+        seed = 1000 + case
+        kw = {"ties": dict(quantum=0.25), "normal": {}, "zipf": dict(zipf_s=1.2, zipf_beta=1.0),
+              "hot": dict(hot_expert=int(rng.integers(E)))}[dist]
+        logits = inputs.make_logits(N, E, seed, **kw)
+        noise = inputs.make_logits(N, E, seed + 1, quantum=0.25 if dist == "ties" else None) if noisy else None
+        padded = cf is not None
+        cfg = _routing_cfg(N, E, k, mode, noisy, dtype=dt, D=128, capacity_mode="padded" if padded else "none",
+                           capacity_factor=cf if padded else 0.0, min_capacity=minc if padded else 0,
+                           capacity_priority=prio, capacity_formula=formula)
+        d = B.make_desc(cfg)
+        idx = torch.empty((N, k), dtype=torch.int32, device=DEV)
+        gate = torch.empty((N, k), dtype=torch.float32, device=DEV)
+        B.moe_route(d, None, None, None, _dev(noise), _dev(logits), None, None, idx, gate)
+        x = inputs.make_rows(N, 128, seed, dt)
+        out, _ = _run_dispatch(d, x.to(DEV), idx, gate)
+        r = orc.route(logits, k, mode, noise=noise, noise_all=noisy == "all")
+        g_idx = host(idx)
+        assert np.array_equal(g_idx, r.idx), f"selection differs: {desc}"
+        assert np.allclose(host(gate), r.gate, rtol=2e-6, atol=1e-7), f"gates differ: {desc}"
+        C = orc.capacity(N, E, k, cf, minc, formula) if padded else None
+        if padded:
+            assert B.moe_capacity(d) == C, desc
+        o = orc.dispatch(g_idx, host(gate).astype(np.float64), E, C, padded, token_major=prio == "token_major")
+        for name in ("load", "counts", "offsets", "row_of", "dropped"):
+            assert np.array_equal(host(out[name]), getattr(o, name)), f"{name} differs: {desc}"
+        assert np.allclose(host(out["gate_eff"]), o.gate_eff, rtol=1e-6, atol=1e-7), f"gate_eff differs: {desc}"
+        kept = o.row_of >= 0
+        tok = np.broadcast_to(np.arange(N)[:, None], o.row_of.shape)
+        assert np.array_equal(host(out["token_of_row"])[o.row_of[kept]], tok[kept]), f"token_of_row differs: {desc}"
+        assert torch.equal(out["x_perm"].cpu()[torch.from_numpy(o.row_of[kept])],
+                           x[torch.from_numpy(tok[kept].copy())]), f"x_perm differs: {desc}"
+    print(f"{n_cases} random tiny routing + dispatch cases bit-exact", flush=True)
 
 
 # ---------------------------------------------------------------------------------------
@@ -334,22 +398,93 @@ def _workload(cfg):
     return _CACHE[key]
 
 
-def _oracle_routing(orc, cfg, inp):
-    """The oracle's routing and dispatch of a workload (all N tokens)."""
+def _oracle_routing(orc, cfg, inp, logits=None):
+    """The oracle's routing and dispatch of a workload (all N tokens), from its own exact
+    logits, or from the given fp32 logits (the logits the selection used: under noisy
+    top-k gating these already hold logit + noise)."""
     N, E, k = cfg["N"], cfg["E"], cfg["k"]
     padded = cfg["capacity_mode"] == "padded"
     sc = cfg["second_choice"]
-    logits = orc.router_logits(inp["x"], inp["w_r"], inp["logit_bias"])
-    r = orc.route(logits, k, cfg["routing_mode"], noise=inp["noise"] if sc != "topk" else None,
-                  noise_all=sc == "noisy_all")
+    if logits is None:
+        logits = orc.router_logits(inp["x"], inp["w_r"], inp["logit_bias"])
+        r = orc.route(logits, k, cfg["routing_mode"], noise=inp["noise"] if sc != "topk" else None,
+                      noise_all=sc == "noisy_all")
+    else:
+        r = orc.route(logits, k, cfg["routing_mode"], noise=inp["noise"] if sc == "noisy" else None)
     C = (orc.capacity(N, E, k, cfg["capacity_factor"], cfg["min_capacity"], cfg.get("capacity_formula", "tokens_k"))
          if padded else None)
     o = orc.dispatch(r.idx, r.gate, E, C, padded, token_major=cfg.get("capacity_priority") == "token_major")
     return r, o
 
 
-def _check_layer(orc, cfg, sample=None, max_amb=16):
-    """Runs moe_forward and checks routing, dispatch and outputs against the oracle."""
+def _gpu_router_logits(orc, cfg, inp, layer):
+    """The fp32 logits the forward routed from: moe_route on the same device inputs,
+    whose selection and gates must equal the forward's bit for bit. They are checked
+    against the exact logits (|dl| <= 4e-6 sum_d |x_d w_de| + 1e-6, plus one fp32 rounding
+    of logit + noise under noisy top-k gating) and returned as a host array."""
+    d = layer.desc
+    N, E, k = cfg["N"], cfg["E"], cfg["k"]
+    sc = torch.empty(B.moe_scratch_size(d), dtype=torch.uint8, device=DEV)
+    lout = torch.empty((N, E), dtype=torch.float32, device=DEV)
+    idx = torch.empty((N, k), dtype=torch.int32, device=DEV)
+    gate = torch.empty((N, k), dtype=torch.float32, device=DEV)
+    B.moe_route(d, layer.x, layer.w_r, layer.bias, layer.noise, None, lout, None, idx, gate, sc)
+    torch.cuda.synchronize()
+    v = layer.views()
+    assert torch.equal(idx, v["topk_idx"]) and torch.equal(gate, v["topk_gate"]), \
+        "moe_route and moe_forward route differently from the same inputs"
+    g = host(lout).astype(np.float64)
+    exact = orc.router_logits(inp["x"], inp["w_r"], inp["logit_bias"])
+    mag = np.abs(inp["x"].double().numpy()) @ np.abs(inp["w_r"].double().numpy())
+    tol = 4e-6 * mag + 1e-6
+    if cfg["second_choice"] == "noisy_all":
+        exact = exact + inp["noise"].double().numpy()
+        tol = tol + np.abs(g) * 2.0 ** -23
+    err = np.abs(g - exact)
+    assert np.all(err <= tol), f"router logits: max |dl| {err.max():.3e}, worst ratio {(err / tol).max():.2f}"
+    return host(lout)
+
+
+def _step_values(r, noise, second_noisy):
+    """Per selection step, the probabilities that step ranks ([N,k,E]): the softmax of
+    the fp32 logits, and for the noisy steps of the GShard second choice the softmax of
+    fl32(logit + noise). Used only to check that a near-tie token's GPU selection is a
+    valid one."""
+    N, k = r.idx.shape
+    out = np.repeat(r.probs[:, None, :], k, axis=1)
+    if second_noisy and k > 1:
+        v = (r.logits.astype(np.float32) + noise.numpy()).astype(np.float64)
+        v = np.exp(v - v.max(axis=1, keepdims=True))
+        out[:, 1:, :] = (v / v.sum(axis=1, keepdims=True))[:, None, :]
+    return out
+
+
+def _drop_cases(dropped, per_case):
+    """Up to per_case tokens of every pattern of kept / dropped slots, evenly spread, and
+    the patterns present (k = 1: kept, dropped; k = 2: kk, kd, dk, dd)."""
+    k = dropped.shape[1]
+    toks, present = [], []
+    for pat in np.ndindex(*(2,) * k):
+        m = np.nonzero(np.all(dropped == np.array(pat, np.uint8), axis=1))[0]
+        if len(m):
+            present.append("".join("kd"[b] for b in pat))
+            toks += m[:: max(1, len(m) // per_case)][:per_case].tolist()
+    return toks, present
+
+
+def _check_layer(orc, cfg, sample=None, max_amb=16, drop_sample=0, min_frac=0.9):
+    """Runs moe_forward and checks routing, dispatch and outputs against the oracle.
+
+    Without capacity the oracle routes from its own exact logits: selections must be
+    equal on every token except the near ties (margin < 1e-5), whose GPU selection must
+    be a valid one; dispatch, which a flipped near tie shifts, is compared bit for bit
+    over all tokens and experts against the oracle's dispatch of the GPU's own selection
+    (no other token's output depends on a near tie). With capacity a flipped record moves
+    other tokens' slots, so the oracle routes from the GPU's own fp32 logits (checked
+    against the exact ones): selection, loads, counts, offsets, slots and the drop mask
+    must then be equal over all tokens. Outputs are compared on the sampled tokens (all
+    tokens when sample is None), near ties excluded in the first case only; at least
+    min_frac of the sample must be compared."""
     inp = _workload(cfg)
     layer = B.MoELayer(cfg, inp)
     layer.forward()
@@ -357,44 +492,78 @@ def _check_layer(orc, cfg, sample=None, max_amb=16):
     v = layer.views()
     N, E, k = cfg["N"], cfg["E"], cfg["k"]
     padded = cfg["capacity_mode"] == "padded"
+    noise = inp["noise"]
+    g_idx, g_gate = host(v["topk_idx"]), host(v["topk_gate"])
+    g_logits = _gpu_router_logits(orc, cfg, inp, layer)
+    r_own, o_own = _oracle_routing(orc, cfg, inp)
+    amb_own = ambiguous_tokens(r_own)
+    assert len(amb_own) <= max_amb, f"{len(amb_own)} near-tie tokens"
 
-    r, o = _oracle_routing(orc, cfg, inp)
-
-    g_idx = host(v["topk_idx"])
-    amb = ambiguous_tokens(r)
-    assert len(amb) <= max_amb, f"{len(amb)} near-tie tokens"
-    clear = np.ones(N, bool)
-    clear[amb] = False
-    assert np.array_equal(g_idx[clear], r.idx[clear]), "routing differs on tokens with a clear margin"
-    np.testing.assert_allclose(host(v["topk_gate"])[clear], r.gate[clear], rtol=2e-5, atol=1e-6)
-
-    moved = affected_experts(r.idx, g_idx, amb)
-    stable = np.array([e not in moved for e in range(E)])
-    g_load, g_cnt = host(v["load"]), host(v["counts"])
-    g_off = host(v["offsets"]).astype(np.int64)
-    assert np.array_equal(g_load[stable], o.load[stable])
-    assert np.array_equal(g_cnt[stable], o.counts[stable])
-    assert g_load.sum() == N * k
-    g_row = host(v["row_of"]).astype(np.int64)
-    g_drop = host(v["dropped"])
-    rec_stable = stable[r.idx] & clear[:, None]
-    assert np.array_equal(g_drop[rec_stable], o.dropped[rec_stable])
-    gp = np.where(g_row >= 0, g_row - g_off[np.clip(g_idx, 0, E - 1)], -1)
-    op = np.where(o.row_of >= 0, o.row_of - o.offsets[r.idx], -1)
-    assert np.array_equal(gp[rec_stable], op[rec_stable]), "capacity slot positions differ"
-
-    tok_ok = clear & np.all(stable[r.idx], axis=1)
-    if sample is None:
-        toks = np.nonzero(tok_ok)[0]
+    if padded:
+        r, o = _oracle_routing(orc, cfg, inp, logits=g_logits)
+        assert np.array_equal(g_idx, r.idx), "routing differs from the oracle's on the GPU's logits"
+        np.testing.assert_allclose(g_gate, r.gate, rtol=2e-6, atol=1e-7)
+        amb = np.zeros(0, np.int64)
     else:
-        toks = np.array([t for t in sample if tok_ok[t]], np.int64)
-    y_ref = orc.layer_tokens(toks, inp["x"], inp["w1"], inp["w2"], inp["w3"], r.idx, o.dropped, o.gate_eff,
+        r, o_r = r_own, o_own
+        amb = amb_own
+        clear = np.ones(N, bool)
+        clear[amb] = False
+        assert np.array_equal(g_idx[clear], r.idx[clear]), "routing differs on tokens with a clear margin"
+        np.testing.assert_allclose(g_gate[clear], r.gate[clear], rtol=2e-5, atol=1e-6)
+        # a near-tie token's GPU selection must be a valid one: distinct experts, each
+        # step's choice within the margin of the best expert the GPU had not yet chosen,
+        # in the values that step ranks
+        sv = _step_values(r, noise, cfg["second_choice"] == "noisy")
+        for t in amb:
+            assert len(set(g_idx[t].tolist())) == k and g_idx[t].min() >= 0 and g_idx[t].max() < E
+            left = np.ones(E, bool)
+            for j in range(k):
+                best = sv[t, j, left].max()
+                assert sv[t, j, g_idx[t, j]] >= best - MARGIN, \
+                    f"token {t}: GPU selection {g_idx[t]} is not a near tie of {r.idx[t]} (step {j})"
+                left[g_idx[t, j]] = False
+        o = orc.dispatch(g_idx, g_gate.astype(np.float64), E, None, False,
+                         token_major=cfg.get("capacity_priority") == "token_major")
+        # loads of the oracle's own routing differ only by the records of near-tie tokens
+        assert np.abs(host(v["load"]).astype(np.int64) - o_own.load).sum() <= 2 * k * len(amb)
+
+    # dispatch: bit-exact over all tokens and experts
+    assert np.array_equal(host(v["load"]), o.load)
+    assert np.array_equal(host(v["counts"]), o.counts)
+    assert np.array_equal(host(v["offsets"]), o.offsets)
+    assert np.array_equal(host(v["row_of"]), o.row_of), "capacity slots differ"
+    assert np.array_equal(host(v["dropped"]), o.dropped), "drop mask differs"
+    np.testing.assert_allclose(host(v["gate_eff"]), o.gate_eff, rtol=2e-5, atol=1e-6)
+    assert int(host(v["load"]).sum()) == N * k
+
+    # outputs
+    present = []
+    if sample is None:
+        sample = np.arange(N)
+    sample = np.asarray(sample, np.int64)
+    if drop_sample:
+        extra, present = _drop_cases(o.dropped, drop_sample)
+        sample = np.union1d(sample, np.array(extra, np.int64))
+    excl = np.zeros(N, bool)
+    excl[amb] = True
+    toks = sample[~excl[sample]]
+    assert len(toks) >= min_frac * len(sample), f"only {len(toks)} of {len(sample)} sampled tokens compared"
+    o_y = o if padded else o_r
+    y_ref = orc.layer_tokens(toks, inp["x"], inp["w1"], inp["w2"], inp["w3"], r.idx, o_y.dropped, o_y.gate_eff,
                              cfg["activation"], scales=(inp["s1"], inp["s2"], inp["s3"]) if "s1" in inp else None)
     y = host(layer.y)[toks]
     err = assert_rows_close(y, y_ref, TOL_Y[cfg["dtype"]], "layer output")
-    zero = np.all(o.dropped[toks] == 1, axis=1)
+    zero = np.all(o_y.dropped[toks] == 1, axis=1)
     assert np.all(y[zero] == 0.0), "fully dropped tokens must have increment exactly 0"
-    return dict(layer=layer, routing=r, dispatch=o, amb=amb, err=err, toks=toks, inp=inp)
+    print(f"[{cfg['name']}] N={N} E={E} k={k}: "
+          + ("routing from the GPU's logits, " if padded else "")
+          + f"selection equal on {N - len(amb)}/{N} tokens ({len(amb_own)} near ties vs the oracle's own logits), "
+          f"dispatch bit-exact on {N} tokens and {E}/{E} experts ({int(o.dropped.sum())} dropped records), "
+          f"outputs compared on {len(toks)}/{len(sample)} sampled tokens"
+          + (f" (drop cases {present})" if present else "") + f", max normwise error {err:.2e}", flush=True)
+    return dict(layer=layer, routing=r, dispatch=o, amb=amb, amb_own=amb_own, err=err, toks=toks, inp=inp,
+                present=present, sample=sample)
 
 
 MID = [
@@ -507,13 +676,14 @@ def test_stats(orc, cfg):
     assert st["dropped_slots"] == int(g_drop.sum())
     assert st["dropped_tokens"] == int(np.all(g_drop == 1, axis=1).sum())
     assert st["drop_rate"] == pytest.approx(g_drop.mean(), rel=1e-12)
-    # and the oracle's up to the near-tie tokens (each can move k records)
-    n_amb = len(res["amb"])
-    assert abs(st["dropped_slots"] - int(o.dropped.sum())) <= n_amb * k
+    # and the oracle's statistics of the same records (its dispatch of the GPU's selection,
+    # or under capacity its routing of the GPU's logits): drops exactly, the balance loss
+    # to the rounding of the fp32 probability sums
+    assert st["dropped_slots"] == int(o.dropped.sum())
+    assert st["dropped_tokens"] == int(np.all(o.dropped == 1, axis=1).sum())
     P, bal, bal_n = orc.balance(r.probs, o.load, k)
-    slack = n_amb * 2 * k * E * P.max() / (N * k)
-    assert abs(st["balance_loss"] - bal) <= 1e-5 * bal + slack
-    assert abs(st["balance_loss_div_n"] - bal_n) <= 1e-5 * bal_n + k * slack
+    assert abs(st["balance_loss"] - bal) <= 1e-5 * bal
+    assert abs(st["balance_loss_div_n"] - bal_n) <= 1e-5 * bal_n
 
 
 # ---- the five workloads at their full sizes ---------------------------------------------
@@ -543,37 +713,28 @@ def test_workload_mixtral_decode(orc):
 
 @pytest.mark.slow
 def test_workload_gshard_capacity(orc):
+    """Capacity slots and drop mask of all 16384 tokens bit-exact (the oracle routes from
+    the GPU's fp32 logits); outputs of evenly spread tokens plus 8 of every drop case."""
     cfg = configs.get_config("gshard_capacity")
-    inp = _workload(cfg)
-    # choose sampled tokens that cover every drop case, from the oracle's own dispatch
-    logits = orc.router_logits(inp["x"], inp["w_r"], inp["logit_bias"])
-    r = orc.route(logits, cfg["k"], cfg["routing_mode"], noise=inp["noise"])
-    o = orc.dispatch(r.idx, r.gate, cfg["E"], 640, True)
-    cases = {"kk": (0, 0), "kd": (0, 1), "dk": (1, 0), "dd": (1, 1)}
-    extra = []
-    for name, pat in cases.items():
-        m = np.nonzero((o.dropped[:, 0] == pat[0]) & (o.dropped[:, 1] == pat[1]))[0]
-        assert len(m) > 0, f"drop case {name} absent from the workload"
-        extra += m[:: max(1, len(m) // 8)][:8].tolist()
+    res = _check_layer(orc, cfg, sample=_spread(cfg["N"], 16), drop_sample=8)
+    assert sorted(res["present"]) == ["dd", "dk", "kd", "kk"], res["present"]
+    assert len(res["toks"]) >= 40
+    o = res["dispatch"]
     assert (o.load > 640).sum() >= 1
-    res = _check_layer(orc, cfg, sample=_spread(cfg["N"], 16, extra=extra))
     st = res["layer"].stats()
     assert st["capacity"] == 640
-    if len(res["amb"]) == 0:
-        assert st["dropped_slots"] == int(o.dropped.sum())
+    assert st["dropped_slots"] == int(o.dropped.sum())
+    assert st["dropped_tokens"] == int(np.all(o.dropped == 1, axis=1).sum())
 
 
 @pytest.mark.slow
 def test_workload_switch_top1(orc):
     cfg = configs.get_config("switch_top1")
-    inp = _workload(cfg)
-    r, o = _oracle_routing(orc, cfg, inp)
+    res = _check_layer(orc, cfg, sample=_spread(cfg["N"], 16), drop_sample=8)
+    o = res["dispatch"]
     C = orc.capacity(cfg["N"], cfg["E"], cfg["k"], cfg["capacity_factor"], cfg["min_capacity"], "tokens")
     assert C == 512 and (o.load > C).sum() >= 1, "the workload must overflow an expert"
-    gone = np.nonzero(o.dropped[:, 0] == 1)[0]
-    kept = np.nonzero(o.dropped[:, 0] == 0)[0]
-    extra = gone[:: max(1, len(gone) // 8)][:8].tolist() + kept[:: max(1, len(kept) // 8)][:8].tolist()
-    res = _check_layer(orc, cfg, sample=_spread(cfg["N"], 16, extra=extra))
+    assert sorted(res["present"]) == ["d", "k"], res["present"]
     assert res["layer"].stats()["capacity"] == C
 
 
