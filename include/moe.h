@@ -283,6 +283,23 @@ MOE_API int moe_forward(const moe_desc* desc, const void* x, const float* w_r, c
                 const float* noise, const void* w1, const void* w2, const void* w3, void* y,
                 void* workspace, size_t workspace_bytes, void* stream);
 
+/* The layer forward for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): moe_forward with its
+ * workspace in a static device array of MOE_NOALLOC_WORKSPACE_BYTES that the library
+ * holds on each GPU it runs on until the process ends. Calls no allocating routine.
+ * Arguments, results and errors as for moe_forward (y equal to its result bit for bit),
+ * except: no workspace argument; MOE_E_WORKSPACE if moe_workspace_size(desc) exceeds
+ * MOE_NOALLOC_WORKSPACE_BYTES (e.g. Mixtral-shaped decode batches fit, prefill batches do
+ * not); MOE_E_INVAL if `stream` belongs to another device than the current one.
+ * Every call on one GPU uses that GPU's array: calls that overlap on one GPU (on
+ * different streams, or from different host threads) race and must be serialised by the
+ * caller. The array keeps the previous call's intermediates; nothing in the forward
+ * depends on their initial contents. */
+#define MOE_NOALLOC_WORKSPACE_BYTES (128u << 20)
+MOE_API int moe_forward_noalloc(const moe_desc* desc, const void* x, const float* w_r, const float* logit_bias,
+                        const float* noise, const void* w1, const void* w2, const void* w3, void* y,
+                        void* stream);
+
 /* ---- weight-only 8-bit experts ------------------------------------------------------
  * Grok-1 keeps its expert weights 8-bit and dequantises them right before the expert
  * matmul, weight = weight * scales ([GROK5] §5.3.3 moe_slow_matmul1 and §5.3.4 moe_slow_matmul2). Here:

@@ -29,7 +29,7 @@ EXPORTED = ["moe_status_string", "moe_capacity", "moe_rows", "moe_scratch_size",
             "moe_workspace_layout", "moe_route", "moe_dispatch", "moe_expert_ffn", "moe_expert_up",
             "moe_expert_down", "moe_combine",
             "moe_forward", "moe_read_stats", "moe_expert_up_q8", "moe_expert_down_q8", "moe_expert_ffn_q8",
-            "moe_forward_q8"]
+            "moe_forward_q8", "moe_forward_noalloc"]
 
 
 class MoeError(RuntimeError):
@@ -90,6 +90,7 @@ def lib():
         L.moe_expert_down.argtypes = [_dp] + [_vp] * 5 + [_vp, ctypes.c_size_t, _vp]
         L.moe_combine.argtypes = [_dp] + [_vp] * 4 + [_vp]
         L.moe_forward.argtypes = [_dp] + [_vp] * 8 + [_vp, ctypes.c_size_t, _vp]
+        L.moe_forward_noalloc.argtypes = [_dp] + [_vp] * 8 + [_vp]
         L.moe_read_stats.argtypes = [_dp, _vp, ctypes.c_size_t, ctypes.POINTER(moe_stats), _vp]
         L.moe_expert_up_q8.argtypes = [_dp] + [_vp] * 8 + [_vp, ctypes.c_size_t, _vp]
         L.moe_expert_down_q8.argtypes = [_dp] + [_vp] * 6 + [_vp, ctypes.c_size_t, _vp]
@@ -282,6 +283,18 @@ def moe_forward(d, x, w_r, logit_bias, noise, w1, w2, w3, y, workspace, stream=N
                              _ptr(w1, (E, D, F), dt, "w1"), _ptr(w2, (E, D, F), dt, "w2"),
                              _ptr(w3, (E, F, D), dt, "w3"), _ptr(y, (N, D), dt, "y"), pw, wb, _stream(stream)),
            "moe_forward")
+
+
+def moe_forward_noalloc(d, x, w_r, logit_bias, noise, w1, w2, w3, y, stream=None):
+    """moe_forward with the library's static per-GPU workspace (no workspace argument)."""
+    N, D, F, E = d.N, d.D, d.F, d.E
+    dt = _tdtype(d)
+    _check(lib().moe_forward_noalloc(ctypes.byref(d), _ptr(x, (N, D), dt, "x"), _ptr(w_r, (D, E), torch.float32, "w_r"),
+                                     _ptr(logit_bias, (E,), torch.float32, "logit_bias", optional=True),
+                                     _ptr(noise, (N, E), torch.float32, "noise", optional=(d.second_choice == 0)),
+                                     _ptr(w1, (E, D, F), dt, "w1"), _ptr(w2, (E, D, F), dt, "w2"),
+                                     _ptr(w3, (E, F, D), dt, "w3"), _ptr(y, (N, D), dt, "y"), _stream(stream)),
+           "moe_forward_noalloc")
 
 
 # ---- weight-only 8-bit experts: int8 W [E, K, N] with fp32 column scales s [E, N] --------

@@ -7,6 +7,8 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "moe_internal.h"
 
 using namespace moe;
@@ -390,6 +392,60 @@ int moe_forward_q8(const moe_desc* d, const void* x, const float* w_r, const flo
   if ((rc = check_q8(d, s1, s2)) != MOE_OK || (rc = check_q8(d, s3, nullptr)) != MOE_OK) return rc;
   return forward_impl(d, x, w_r, logit_bias, noise, w1, w2, w3, y, workspace, workspace_bytes, stream,
                       Scales{s1, s2, s3});
+}
+
+}  // extern "C"
+
+// ---- the forward without a caller workspace ---------------------------------------------
+// moe_forward_noalloc runs moe_forward with its workspace in one file-scope device array
+// per GPU (allocated with the library's code object on that GPU, held until the process
+// ends). Its host-side name is not a device address: the address is taken once per
+// device, with that device current, by hipGetSymbolAddress and kept in g_noalloc_ws;
+// kernels only ever receive that address.
+namespace noalloc {
+static __device__ __align__(256) unsigned char scratch[MOE_NOALLOC_WORKSPACE_BYTES];
+}  // namespace noalloc
+
+namespace {
+constexpr int kNoallocDevices = 64;
+std::mutex g_noalloc_mu;
+void* g_noalloc_ws[kNoallocDevices];  // per device; guarded by g_noalloc_mu
+
+// Device address of the static workspace on device `dev` (the current device), or null
+// if the runtime call fails.
+void* noalloc_workspace(int dev) {
+  std::lock_guard<std::mutex> lock(g_noalloc_mu);
+  if (g_noalloc_ws[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(noalloc::scratch)) != hipSuccess || p == nullptr) return nullptr;
+    g_noalloc_ws[dev] = p;
+  }
+  return g_noalloc_ws[dev];
+}
+}  // namespace
+
+extern "C" {
+
+int moe_forward_noalloc(const moe_desc* d, const void* x, const float* w_r, const float* logit_bias,
+                        const float* noise, const void* w1, const void* w2, const void* w3, void* y, void* stream) {
+  int rc = check_desc(d);
+  if (rc) return rc;
+  int64_t rows;
+  rc = rows_of(d, &rows);
+  if (rc) return rc;
+  if (layout_of(d, rows).total > (size_t)MOE_NOALLOC_WORKSPACE_BYTES) return MOE_E_WORKSPACE;
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return MOE_E_HIP;
+  if (dev < 0 || dev >= kNoallocDevices) return MOE_E_UNSUPPORTED;
+  if (stream != nullptr) {
+    hipDevice_t sd = -1;
+    if (hipStreamGetDevice((hipStream_t)stream, &sd) != hipSuccess) return MOE_E_HIP;
+    if (sd != dev) return MOE_E_INVAL;  // the stream must belong to the current device
+  }
+  void* ws = noalloc_workspace(dev);
+  if (ws == nullptr) return MOE_E_HIP;
+  return forward_impl(d, x, w_r, logit_bias, noise, w1, w2, w3, y, ws, (size_t)MOE_NOALLOC_WORKSPACE_BYTES, stream,
+                      Scales{nullptr, nullptr, nullptr});
 }
 
 int moe_expert_up_q8(const moe_desc* d, const void* x_perm, const int32_t* offsets, const int32_t* counts,
