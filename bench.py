@@ -8,8 +8,11 @@ then exactly K timed steps between two device synchronisations give the throughp
 K more steps through the per-stage entry points (the same kernels), with HIP events
 recorded on the launch stream between the stages, give each stage's duration.
 
-Prints one JSON line: tokens/s, the roofline of the dominant kernel, and the fp64 CPU
-oracle timed on a bounded sample of the same workload on the host cores.
+Prints one JSON line: tokens/s, the roofline of the dominant kernel, the routing
+statistics of the last forward (balance loss, drop rates) beside the oracle's, the
+weight-streaming decode regime of the same expert shapes (the mixtral_decode workload,
+`decode` key), and the fp64 CPU oracle timed on a bounded sample of the same workload on
+the host cores.
 """
 from __future__ import annotations
 
@@ -41,6 +44,8 @@ def parse():
     p.add_argument("--cpu-sample", type=int, default=2048, help="tokens in the oracle's timed FFN sample")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-graph", action="store_true", help="skip the HIP-graph replay measurement")
+    p.add_argument("--no-decode", dest="decode", action="store_false",
+                   help="skip the decode-regime measurement (the mixtral_decode workload, same run)")
     p.add_argument("--cold-reps", type=int, default=5,
                    help="cold-cache runs of each small stage before the warm-up (0: none)")
     p.add_argument("--copy-mib", type=int, default=0,
@@ -109,38 +114,28 @@ def cpu_baseline(cfg, inp, sample: int, sample_1t: int = 64):
     t4 = time.perf_counter()
     orc.set_threads(threads)
     per_tok_1 = (t1 - t0) * threads / N + (t4 - t3) / len(toks1)
+    # the oracle's routing statistics of the same workload (its own exact logits)
+    _, bal, bal_n = orc.balance(r.probs, o.load, cfg["k"])
+    drops = int(o.dropped.sum())
+    gone = int(np.all(o.dropped == 1, axis=1).sum())
+    stats = {"balance_loss": bal, "balance_loss_div_n": bal_n, "drop_rate": drops / (N * cfg["k"]),
+             "token_drop_rate": gone / N, "dropped_slots": drops, "dropped_tokens": gone}
     return {"value": 1.0 / per_tok, "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "cpu": _cpu_model(), "nproc": os.cpu_count(),
-            "value_1thread": 1.0 / per_tok_1,
+            "value_1thread": 1.0 / per_tok_1, "routing_stats": stats,
             "sample": f"router+softmax+top-k+dispatch of all {N} tokens ({t1 - t0:.2f} s), expert FFN + combine "
                       f"of {n} evenly spaced tokens ({t2 - t1:.2f} s); rate = 1 / (route time per token + "
                       f"FFN time per token). value_1thread: FFN of the first {len(toks1)} of those tokens on one "
                       f"thread ({t4 - t3:.2f} s), routing time scaled by the thread count"}
 
 
-def main():
-    args = parse()
-    if args.gpus != 1:
-        print(f"bench.py measures one GPU only (the layer has no multi-GPU path); got --gpus {args.gpus}",
-              file=sys.stderr)
-        sys.exit(2)
+def measure_layer(B, cfg, inp, args, dev, cold_reps: int, graph: bool) -> dict:
+    """Times one workload on the GPU: K moe_forward calls between two synchronisations (the
+    throughput), then K passes through the per-stage entry points running the same kernels
+    as the forward (the up-projection through moe_expert_up_gathered wherever the forward
+    reads its rows from x), with HIP events recorded on the launch stream between stages."""
     import numpy as np
     import torch
-    if args.copy_mib > 0:
-        src = torch.empty(args.copy_mib * 2 ** 20, dtype=torch.uint8, device="cuda:0")
-        dst = torch.empty_like(src)
-        for _ in range(args.steps):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        print(json.dumps({"copy_mib": args.copy_mib, "copies": args.steps}), flush=True)
-        return
-    from mixture_experts_layer_wave_amd import binding as B
-    from mixture_experts_layer_wave_amd import configs, inputs
-
-    cfg = configs.get_config(args.workload)
-    inp = inputs.make_inputs(cfg)
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
     layer = B.MoELayer(cfg, inp, device=dev)
     d = layer.desc
     N, D, F, E, k = cfg["N"], cfg["D"], cfg["F"], cfg["E"], cfg["k"]
@@ -148,8 +143,16 @@ def main():
     v = layer.views()
     sc = v["scratch"]
     stream = torch.cuda.current_stream()
+    q8 = cfg.get("weight_dtype", "same") == "int8"
 
-    def step(ev=None):
+    def up_gathered():
+        B.moe_expert_up_gathered(d, layer.x, v["token_of_row"], v["offsets"], v["counts"], layer.w1, layer.w2, v["h"],
+                                 sc)
+
+    def up_plain():
+        layer.expert_up(v["x_perm"], v["offsets"], v["counts"], v["h"], sc)
+
+    def step(ev=None, up=up_plain):
         if ev is not None:
             ev[0].record(stream)
         B.moe_route(d, layer.x, layer.w_r, layer.bias, layer.noise, None, None, None, v["topk_idx"], v["topk_gate"],
@@ -160,7 +163,7 @@ def main():
                        v["dropped"], v["gate_eff"], v["token_of_row"], v["x_perm"], sc)
         if ev is not None:
             ev[2].record(stream)
-        layer.expert_up(v["x_perm"], v["offsets"], v["counts"], v["h"], sc)
+        up()
         if ev is not None:
             ev[3].record(stream)
         layer.expert_down(v["h"], v["offsets"], v["counts"], v["y_perm"], sc)
@@ -171,34 +174,45 @@ def main():
             ev[5].record(stream)
 
     step()  # every stage's inputs exist from here on
+    # The instance of the up-projection the forward runs: rows read from x through
+    # token_of_row (bf16 weights, experts that may exceed 64 rows), else x_perm.
+    up = up_plain
+    if not q8:
+        try:
+            up_gathered()
+            up = up_gathered
+        except B.MoeError as err:
+            if err.status != B.MOE_E_UNSUPPORTED:
+                raise
     # Small stages alone, each after writing a 512 MB buffer so the last-level cache holds
     # none of their inputs (the timed steps below give the warm numbers). Run before the
     # warm-up so the timed steps are the last calls of every kernel.
-    flush = torch.empty(512 * 2 ** 20, dtype=torch.uint8, device=dev)
-    small = {
-        "route": lambda: B.moe_route(d, layer.x, layer.w_r, layer.bias, layer.noise, None, None, None, v["topk_idx"],
-                                     v["topk_gate"], sc),
-        "dispatch": lambda: B.moe_dispatch(d, layer.x, v["topk_idx"], v["topk_gate"], v["load"], v["counts"],
-                                           v["offsets"], v["row_of"], v["dropped"], v["gate_eff"], v["token_of_row"],
-                                           v["x_perm"], sc),
-        "combine": lambda: B.moe_combine(d, v["y_perm"], v["row_of"], v["gate_eff"], layer.y),
-    }
     cold_ms = {}
-    for name, fn in (small.items() if args.cold_reps > 0 else ()):
-        ts = []
-        for _ in range(args.cold_reps):
-            flush.fill_(1)
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-            fn()
-            e1.record(stream)
-            torch.cuda.synchronize()
-            ts.append(e0.elapsed_time(e1))
-        cold_ms[name] = float(np.median(ts))
-    del flush
+    if cold_reps > 0:
+        flush = torch.empty(512 * 2 ** 20, dtype=torch.uint8, device=dev)
+        small_fn = {
+            "route": lambda: B.moe_route(d, layer.x, layer.w_r, layer.bias, layer.noise, None, None, None,
+                                         v["topk_idx"], v["topk_gate"], sc),
+            "dispatch": lambda: B.moe_dispatch(d, layer.x, v["topk_idx"], v["topk_gate"], v["load"], v["counts"],
+                                               v["offsets"], v["row_of"], v["dropped"], v["gate_eff"],
+                                               v["token_of_row"], v["x_perm"], sc),
+            "combine": lambda: B.moe_combine(d, v["y_perm"], v["row_of"], v["gate_eff"], layer.y),
+        }
+        for name, fn in small_fn.items():
+            ts = []
+            for _ in range(cold_reps):
+                flush.fill_(1)
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                fn()
+                e1.record(stream)
+                torch.cuda.synchronize()
+                ts.append(e0.elapsed_time(e1))
+            cold_ms[name] = float(np.median(ts))
+        del flush
     for _ in range(args.warmup):
         layer.forward()
-        step()
+        step(up=up)
     # Timed: exactly K passes of the layer, one moe_forward call each, between two device
     # synchronisations; an event pair around each call gives its spread.
     fev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
@@ -209,11 +223,11 @@ def main():
         layer.forward()
         fev[i][1].record(stream)
     torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    elapsed = t1 - t0
+    elapsed = time.perf_counter() - t0
     fwd_t = np.array([a.elapsed_time(b) for a, b in fev])
     forward_ms = {"mean": float(np.mean(fwd_t)), "p10": float(np.percentile(fwd_t, 10)),
                   "median": float(np.median(fwd_t)), "p90": float(np.percentile(fwd_t, 90))}
+    stats = layer.stats()  # routing statistics of the last forward (synchronises)
 
     # Stage breakdown: K more passes through the per-stage entry points (the same kernels),
     # with events between the stages.
@@ -221,14 +235,14 @@ def main():
     torch.cuda.synchronize()
     ts0 = time.perf_counter()
     for i in range(args.steps):
-        step(events[i])
+        step(events[i], up=up)
     torch.cuda.synchronize()
     staged_ms_per_step = (time.perf_counter() - ts0) / args.steps * 1e3
 
     # The same forward captured once in a HIP graph and replayed K times (launch overhead
     # of the individual kernels removed); reported beside the eager throughput.
-    graph = None
-    if not args.no_graph:
+    graph_res = None
+    if graph:
         side = torch.cuda.Stream()
         side.wait_stream(stream)
         with torch.cuda.stream(side):
@@ -246,7 +260,7 @@ def main():
             g.replay()
         torch.cuda.synchronize()
         gms = (time.perf_counter() - tg0) / args.steps * 1e3
-        graph = {"ms_per_step": gms, "tokens_per_s": N / (gms * 1e-3)}
+        graph_res = {"ms_per_step": gms, "tokens_per_s": N / (gms * 1e-3)}
         del g
 
     stage_t = {s: np.array([events[i][j].elapsed_time(events[i][j + 1]) for i in range(args.steps)])
@@ -259,7 +273,6 @@ def main():
     A = int(counts.sum())
     active = int((counts > 0).sum())
     es = 2 if cfg["dtype"] == "bf16" else 4
-    q8 = cfg.get("weight_dtype", "same") == "int8"
     ws = 1 if q8 else es  # bytes per weight element (int8 weights also read 4-byte column scales)
     work = {
         "expert_up": dict(flops=4.0 * A * D * F,
@@ -284,9 +297,7 @@ def main():
         if st_name in cold_ms:
             cold = b / (cold_ms[st_name] * 1e-3) / 1e9
             small[st_name].update({"cold_gbs": cold, "cold_frac": cold / PEAK_HBM_GBS})
-    gemm_ms = stage_ms["expert_up"] + stage_ms["expert_down"]
-    gemm_tflops = (work["expert_up"]["flops"] + work["expert_down"]["flops"]) / (gemm_ms * 1e-3) / 1e12
-    dom = max(("expert_up", "expert_down"), key=lambda s: stage_ms[s])
+    dom = max(("expert_up", "expert_down"), key=lambda s_: stage_ms[s_])
     w = work[dom]
     sec = stage_ms[dom] * 1e-3
     peak_f = PEAK_BF16_TFLOPS if cfg["dtype"] == "bf16" else PEAK_F32_TFLOPS
@@ -295,9 +306,66 @@ def main():
     else:
         roof = {"bound": "hbm", "achieved": w["bytes"] / sec / 1e9, "peak": PEAK_HBM_GBS, "unit": "GB/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = traffic_from_profiles(args.workload, dom)
-    roof["kernel"] = KERNEL_OF_STAGE[dom]
+    kernel = KERNEL_OF_STAGE[dom]
+    if dom == "expert_up" and up is up_gathered:
+        kernel = "k_gemm_bf16, rows gathered from x (gated up-projection, the instance moe_forward runs)"
+    roof["kernel"] = kernel
     roof["per_launch"] = {"flops": w["flops"], "algorithmic_bytes": w["bytes"], "avg_ms": stage_ms[dom]}
+    return dict(elapsed=elapsed, forward_ms=forward_ms, staged_ms_per_step=staged_ms_per_step, graph=graph_res,
+                stage_ms=stage_ms, stage_pct=stage_pct, cold_ms=cold_ms, small=small, work=work, dom=dom, A=A,
+                active=active, q8=q8, roofline=roof, stats=stats)
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (the layer has no multi-GPU path); got --gpus {args.gpus}",
+              file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+    if args.copy_mib > 0:
+        src = torch.empty(args.copy_mib * 2 ** 20, dtype=torch.uint8, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_mib": args.copy_mib, "copies": args.steps}), flush=True)
+        return
+    from mixture_experts_layer_wave_amd import binding as B
+    from mixture_experts_layer_wave_amd import configs, inputs
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    cfg = configs.get_config(args.workload)
+    inp = inputs.make_inputs(cfg)
+    m = measure_layer(B, cfg, inp, args, dev, cold_reps=args.cold_reps, graph=not args.no_graph)
+    N, D, F, E, k = cfg["N"], cfg["D"], cfg["F"], cfg["E"], cfg["k"]
+    elapsed, stage_ms, work, dom = m["elapsed"], m["stage_ms"], m["work"], m["dom"]
+    A, active, q8 = m["A"], m["active"], m["q8"]
+    gemm_ms = stage_ms["expert_up"] + stage_ms["expert_down"]
+    gemm_tflops = (work["expert_up"]["flops"] + work["expert_down"]["flops"]) / (gemm_ms * 1e-3) / 1e12
+    roof = m["roofline"]
+    roof["traffic"] = traffic_from_profiles(args.workload, dom)
+    # The weight-streaming decode regime of the same expert shapes, measured in the same run.
+    decode = None
+    if args.decode and args.workload != "mixtral_decode":
+        dcfg = configs.get_config("mixtral_decode")
+        dinp = inputs.make_inputs(dcfg)
+        dm = measure_layer(B, dcfg, dinp, args, dev, cold_reps=0, graph=False)
+        dw = dm["work"]
+        dg_ms = dm["stage_ms"]["expert_up"] + dm["stage_ms"]["expert_down"]
+        dbytes = dw["expert_up"]["bytes"] + dw["expert_down"]["bytes"]
+        decode = {"workload": dcfg["name"], "N": dcfg["N"], "active_experts": dm["active"],
+                  "accepted_rows": dm["A"], "ms_per_step": dm["elapsed"] / args.steps * 1e3,
+                  "tokens_per_s": dcfg["N"] * args.steps / dm["elapsed"], "forward_ms": dm["forward_ms"],
+                  "stages_ms": dm["stage_ms"], "gemm_ms": dg_ms, "gemm_algorithmic_bytes": dbytes,
+                  "gemm_gbs": dbytes / (dg_ms * 1e-3) / 1e9, "gemm_frac_hbm": dbytes / (dg_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                  "up_gbs": dw["expert_up"]["bytes"] / (dm["stage_ms"]["expert_up"] * 1e-3) / 1e9,
+                  "down_gbs": dw["expert_down"]["bytes"] / (dm["stage_ms"]["expert_down"] * 1e-3) / 1e9,
+                  "bytes": "per active expert its W1, W2 and W3 (6 D F bytes, bf16) plus the activation rows "
+                           "read and written (x_perm, h, y_perm)"}
+        del dm, dinp
 
     out = {
         "metric": METRIC,
@@ -318,18 +386,21 @@ def main():
         "grouped_gemm": {"tflops": gemm_tflops, "frac_bf16_peak": gemm_tflops / PEAK_BF16_TFLOPS,
                          "useful_flops": work["expert_up"]["flops"] + work["expert_down"]["flops"],
                          "accepted_rows": A, "active_experts": active},
-        "forward_ms": forward_ms,
-        "staged_ms_per_step": staged_ms_per_step,
-        "graph_replay": graph,
+        "forward_ms": m["forward_ms"],
+        "staged_ms_per_step": m["staged_ms_per_step"],
+        "graph_replay": m["graph"],
         "stages_ms": stage_ms,
-        "stages_ms_pct": stage_pct,
-        "stages_ms_cold": cold_ms,
-        "small_stages_hbm": small,
+        "stages_ms_pct": m["stage_pct"],
+        "stages_ms_cold": m["cold_ms"],
+        "small_stages_hbm": m["small"],
+        "routing_stats": {"gpu": m["stats"], "oracle": None},
+        "decode": decode,
         "roofline": roof,
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_sample)
+        out["routing_stats"]["oracle"] = out["cpu_baseline"].pop("routing_stats")
     print(json.dumps(out), flush=True)
 
 

@@ -266,6 +266,17 @@ MOE_API int moe_expert_down(const moe_desc* desc, const void* h, const int32_t* 
                     const int32_t* counts, const void* w3, void* y_perm, void* scratch,
                     size_t scratch_bytes, void* stream);
 
+/* The gated up-projection with its rows taken from x instead of x_perm: buffer row r of
+ * expert e reads x[token_of_row[r],:] (token_of_row as written by moe_dispatch), so the
+ * gather of moe_dispatch is not needed. h equals moe_expert_up's result on the gathered
+ * x_perm bit for bit. This is the form moe_forward runs for bf16 layers whose experts may
+ * hold more than 64 rows (the skinny decode regime and fp32 layers keep x_perm); for
+ * other layers it returns MOE_E_UNSUPPORTED. Arguments: x [N,D] and h [rows,F] bf16;
+ * token_of_row [rows] int32; the rest as for moe_expert_up. */
+MOE_API int moe_expert_up_gathered(const moe_desc* desc, const void* x, const int32_t* token_of_row,
+                           const int32_t* offsets, const int32_t* counts, const void* w1, const void* w2,
+                           void* h, void* scratch, size_t scratch_bytes, void* stream);
+
 /* Combine ([GROK5] §5.3.5 gate-weighted sum, §5.8; [BOOK12] §12.2 accumulate, not
  * overwrite): y[t,:] = sum over kept slots j, in slot order, of
  * gate_eff[t,j] * y_perm[row_of[t,j],:], accumulated in fp32 and rounded once to dtype;

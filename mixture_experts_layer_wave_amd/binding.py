@@ -29,7 +29,7 @@ EXPORTED = ["moe_status_string", "moe_capacity", "moe_rows", "moe_scratch_size",
             "moe_workspace_layout", "moe_route", "moe_dispatch", "moe_expert_ffn", "moe_expert_up",
             "moe_expert_down", "moe_combine",
             "moe_forward", "moe_read_stats", "moe_expert_up_q8", "moe_expert_down_q8", "moe_expert_ffn_q8",
-            "moe_forward_q8", "moe_forward_noalloc"]
+            "moe_forward_q8", "moe_forward_noalloc", "moe_expert_up_gathered"]
 
 
 class MoeError(RuntimeError):
@@ -88,6 +88,7 @@ def lib():
         L.moe_expert_ffn.argtypes = [_dp] + [_vp] * 8 + [_vp, ctypes.c_size_t, _vp]
         L.moe_expert_up.argtypes = [_dp] + [_vp] * 6 + [_vp, ctypes.c_size_t, _vp]
         L.moe_expert_down.argtypes = [_dp] + [_vp] * 5 + [_vp, ctypes.c_size_t, _vp]
+        L.moe_expert_up_gathered.argtypes = [_dp] + [_vp] * 7 + [_vp, ctypes.c_size_t, _vp]
         L.moe_combine.argtypes = [_dp] + [_vp] * 4 + [_vp]
         L.moe_forward.argtypes = [_dp] + [_vp] * 8 + [_vp, ctypes.c_size_t, _vp]
         L.moe_forward_noalloc.argtypes = [_dp] + [_vp] * 8 + [_vp]
@@ -249,6 +250,20 @@ def moe_expert_up(d, x_perm, offsets, counts, w1, w2, h, scratch, stream=None):
                                _ptr(counts, (E,), torch.int32, "counts"),
                                _ptr(w1, (E, D, F), dt, "w1"), _ptr(w2, (E, D, F), dt, "w2"),
                                _ptr(h, (rows, F), dt, "h"), ps, sb, _stream(stream)), "moe_expert_up")
+
+
+def moe_expert_up_gathered(d, x, token_of_row, offsets, counts, w1, w2, h, scratch, stream=None):
+    N, D, F, E = d.N, d.D, d.F, d.E
+    rows = moe_rows(d)
+    dt = _tdtype(d)
+    ps, sb = _bytes_ptr(scratch, moe_scratch_size(d), "scratch")
+    _check(lib().moe_expert_up_gathered(ctypes.byref(d), _ptr(x, (N, D), dt, "x"),
+                                        _ptr(token_of_row, (rows,), torch.int32, "token_of_row"),
+                                        _ptr(offsets, (E + 1,), torch.int32, "offsets"),
+                                        _ptr(counts, (E,), torch.int32, "counts"),
+                                        _ptr(w1, (E, D, F), dt, "w1"), _ptr(w2, (E, D, F), dt, "w2"),
+                                        _ptr(h, (rows, F), dt, "h"), ps, sb, _stream(stream)),
+           "moe_expert_up_gathered")
 
 
 def moe_expert_down(d, h, offsets, counts, w3, y_perm, scratch, stream=None):

@@ -347,6 +347,24 @@ int moe_expert_up(const moe_desc* d, const void* x_perm, const int32_t* offsets,
   return do_ffn(d, x_perm, offsets, counts, w1, w2, nullptr, h, nullptr, scratch, 1, (hipStream_t)stream);
 }
 
+int moe_expert_up_gathered(const moe_desc* d, const void* x, const int32_t* token_of_row, const int32_t* offsets,
+                           const int32_t* counts, const void* w1, const void* w2, void* h, void* scratch,
+                           size_t scratch_bytes, void* stream) {
+  int rc = check_desc(d);
+  if (rc) return rc;
+  REQUIRE(x); REQUIRE(token_of_row); REQUIRE(offsets); REQUIRE(counts); REQUIRE(w1); REQUIRE(w2); REQUIRE(h);
+  if (!scratch || !aligned16(scratch)) return MOE_E_WORKSPACE;
+  if (scratch_bytes < scratch_layout(d->N, d->D, d->E, d->k, d->dtype == MOE_DT_BF16).total) return MOE_E_WORKSPACE;
+  int64_t C, rows;
+  if ((rc = capacity_of(d, &C)) != MOE_OK || (rc = rows_of(d, &rows)) != MOE_OK) return rc;
+  const bool bf = d->dtype == MOE_DT_BF16;
+  if (!bf || !expert_up_gathers(ffn_args(d, C, rows, x, offsets, counts, w1, w2, nullptr, h, nullptr, scratch,
+                                         Scales{nullptr, nullptr, nullptr}), bf))
+    return MOE_E_UNSUPPORTED;
+  return do_ffn(d, x, offsets, counts, w1, w2, nullptr, h, nullptr, scratch, 1, (hipStream_t)stream,
+                Scales{nullptr, nullptr, nullptr}, token_of_row);
+}
+
 int moe_expert_down(const moe_desc* d, const void* h, const int32_t* offsets, const int32_t* counts,
                     const void* w3, void* y_perm, void* scratch, size_t scratch_bytes, void* stream) {
   int rc = check_desc(d);

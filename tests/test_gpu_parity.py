@@ -632,6 +632,22 @@ def test_layer_bitwise_reproducible_and_equal_to_steps(orc, cfg):
     B.moe_combine(d, yp, out["row_of"], out["gate_eff"], y3)
     torch.cuda.synchronize()
     assert torch.equal(y1, y3)
+    # the up-projection reading its rows from x through token_of_row equals the one on the
+    # gathered x_perm on every filled row (bf16 weights, experts that may exceed 64 rows)
+    may_gather = cfg["dtype"] == "bf16" and cfg.get("weight_dtype", "same") != "int8" and \
+        (min(rows // E, N) if cfg["capacity_mode"] == "padded" else N) > 64
+    if cfg.get("weight_dtype", "same") != "int8":
+        hg = torch.full_like(h, 5.0)
+        try:
+            B.moe_expert_up_gathered(d, layer.x, out["token_of_row"], out["offsets"], out["counts"], layer.w1,
+                                     layer.w2, hg, sc)
+            torch.cuda.synchronize()
+            assert may_gather, "gathered up-projection accepted for a layer the forward does not gather"
+            off, cnt = host(out["offsets"]), host(out["counts"])
+            filled = torch.from_numpy(np.concatenate([np.arange(off[e], off[e] + cnt[e]) for e in range(E)]))
+            assert torch.equal(hg[filled], h[filled]), "gathered up-projection differs from moe_expert_up"
+        except B.MoeError as err:
+            assert not may_gather and err.status == B.MOE_E_UNSUPPORTED, err
     # the forward's routing and dispatch intermediates equal the separate calls' bit for bit
     v = layer.views()
     assert torch.equal(v["topk_idx"], idx) and torch.equal(v["topk_gate"], gate)
