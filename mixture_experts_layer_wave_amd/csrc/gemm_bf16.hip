@@ -289,8 +289,17 @@ __device__ __forceinline__ void fixup_item(const GemmParams& p, const Tile& tl, 
 // STREAMK = true : stream-K; the (tile, K slice) list is cut into equal contiguous ranges,
 //                  one per workgroup; a tile cut by a range boundary leaves fp32 partials
 //                  (slot 2w for the workgroup's first tile, 2w + 1 for its last).
+// LDS ring of one tile configuration, in bf16 elements.
+template <int BM, int BNF, int NB, int BK, int STAGES, bool STREAMK, bool Q8>
+struct Ring {
+  static constexpr int A_EL = BM * BK, B_BYTES = BK * BNF * (Q8 ? 1 : 2);
+  static constexpr int STAGE = A_EL + NB * B_BYTES / 2;
+  static constexpr bool B3 = MOE_GEMM_B3 && !STREAMK && !Q8 && STAGES == 2;
+  static constexpr int EL = B3 ? 2 * A_EL + 3 * (NB * B_BYTES / 2) : STAGES * STAGE;
+};
+
 template <int BM, int BNF, int NB, int ACT, int BK, int STAGES, bool STREAMK, bool Q8, bool GA = false>
-__global__ __launch_bounds__(512, 1) void k_gemm_bf16(const GemmParams p) {
+__device__ __forceinline__ void gemm_tiles(const GemmParams& p, bf16* ring) {
   // GA: gathered A rows (p.row_token), persistent tiles only.
   static_assert(!GA || !STREAMK, "gathered rows with persistent tiles");
   // BK: K slice per pipeline stage; STAGES: LDS ring depth (STAGES-1 slices in flight).
@@ -301,7 +310,9 @@ __global__ __launch_bounds__(512, 1) void k_gemm_bf16(const GemmParams p) {
   constexpr int TM = WM / 32, TN = WN / 32;
   constexpr int A_EL = BM * BK, B_BYTES = BK * BNF * WB;
   constexpr int STAGE = A_EL + NB * B_BYTES / 2;    // bf16 elements per ring stage
-  constexpr int A_CP = A_EL * 2 / 1024 / 8;         // 1 KB copies per wave per slice
+  constexpr int A_COPIES = A_EL * 2 / 1024;         // 1 KB copies of one A slice
+  constexpr int A_CP = A_COPIES >= 8 ? A_COPIES / 8 : 1;  // 1 KB copies per copying wave per slice
+  constexpr int A_WAVES = A_COPIES / A_CP;           // waves copying A (all 8 but for small slices)
   constexpr int B_CPM = B_BYTES / 1024;             // 1 KB copies per matrix per slice
   constexpr int B_CP = NB * B_CPM / 8;              // B copies per wave per slice
   constexpr int LOADS = A_CP + B_CP;
@@ -313,7 +324,9 @@ __global__ __launch_bounds__(512, 1) void k_gemm_bf16(const GemmParams p) {
   static_assert((BM == 256 || BM == 64) && (BNF == 128 || BNF == 256) && (BK == 32 || BK == 64), "tile shape");
   static_assert(!Q8 || BK == 64, "int8 tiles: 64-deep slices");
   static_assert(STAGES >= 2 && STAGES <= 8 && STAGES * STAGE * 2 <= 160 * 1024, "LDS ring");
-  static_assert(A_CP >= 1 && B_CP >= 1 && TM >= 1 && TN >= 1 && (NB * B_CPM) % 8 == 0, "tile shape");
+  static_assert(A_COPIES >= 1 && A_CP * A_WAVES == A_COPIES && B_CP >= 1 && TM >= 1 && TN >= 1 &&
+                (NB * B_CPM) % 8 == 0, "tile shape");
+  static_assert(A_WAVES == 8 || STREAMK, "small A slices: stream-K tiles only");
   // Split ring (persistent bf16 tiles with 2 stages): A slices double-buffered, B slices
   // triple-buffered, and the copies of B slice kt + 2 spread between the MFMA groups of
   // slice kt instead of issued in one burst after the barrier.
@@ -321,8 +334,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm_bf16(const GemmParams p) {
   constexpr int B_EL = NB * B_BYTES / 2;  // bf16 elements of one B slice (all matrices)
   constexpr int RING_EL = B3 ? 2 * A_EL + 3 * B_EL : STAGES * STAGE;
   static_assert(RING_EL * 2 <= 160 * 1024, "LDS ring");
-
-  __shared__ __attribute__((aligned(1024))) bf16 ring[RING_EL];
+  static_assert(RING_EL == Ring<BM, BNF, NB, BK, STAGES, STREAMK, Q8>::EL, "LDS ring size");
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -515,7 +527,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm_bf16(const GemmParams p) {
     // accumulator rows that are never stored.
     auto k_loop = [&](auto lone_tile) {
       constexpr bool LONE = decltype(lone_tile)::value;
-      const bool a_live = !LONE || A_RPC * A_CP * wid < tl.mcount;
+      const bool a_live = wid < A_WAVES && (!LONE || A_RPC * A_CP * wid < tl.mcount);
       const bool c_live = !LONE || wm * WM < tl.mcount;
     if constexpr (B3) {
       // Issue order per wave: A0, B0, B1 | A1, B2 | A2, B3 | ... (iteration kt issues A kt+1
@@ -660,6 +672,46 @@ __global__ __launch_bounds__(512, 1) void k_gemm_bf16(const GemmParams p) {
   }
 }
 
+template <int BM, int BNF, int NB, int ACT, int BK, int STAGES, bool STREAMK, bool Q8, bool GA = false>
+__global__ __launch_bounds__(512, 1) void k_gemm_bf16(const GemmParams p) {
+  __shared__ __attribute__((aligned(1024))) bf16 ring[Ring<BM, BNF, NB, BK, STAGES, STREAMK, Q8>::EL];
+  gemm_tiles<BM, BNF, NB, ACT, BK, STAGES, STREAMK, Q8, GA>(p, ring);
+}
+
+// Skinny gated up-projection (every expert at most 64 rows) with two tile widths in one
+// launch, chosen on the device from counts[]: 64 x (2 x 256) tiles (32-deep slices, four
+// stages) when they fill one round of whole tiles (or several rounds on >= 7/8 of the
+// workgroups) and 64 x (2 x 128) tiles would not, since their stream-K remainder then
+// needs partials and a fix-up; 64 x (2 x 128) tiles (64-deep slices) otherwise. A whole tile
+// of either width forms each output as one fp32 sum over K in the same order.
+// p describes the narrow tiles (n_tiles = N / 128); N % 256 == 0.
+constexpr int kSkinnyRows64 = 64;
+__device__ __forceinline__ bool skinny_wide(const GemmParams& p, int grid) {
+  const TileScan ts = tile_scan<kSkinnyRows64>(p);  // narrow tiles
+  const SkPlan wide = sk_plan(ts.total / 2, grid, 1), narrow = sk_plan(ts.total, grid, 1);
+  return wide.W == 0 && narrow.W != 0;
+}
+
+#ifndef MOE_DUAL_BK
+#define MOE_DUAL_BK 32
+#endif
+#ifndef MOE_DUAL_STAGES
+#define MOE_DUAL_STAGES 4
+#endif
+template <int ACT>
+__global__ __launch_bounds__(512, 1) void k_gemm_skinny_dual(const GemmParams p) {
+  constexpr int EL_N = Ring<64, 128, 2, 64, 4, true, false>::EL;
+  constexpr int EL_W = Ring<64, 256, 2, MOE_DUAL_BK, MOE_DUAL_STAGES, true, false>::EL;
+  __shared__ __attribute__((aligned(1024))) bf16 ring[EL_N > EL_W ? EL_N : EL_W];
+  if (skinny_wide(p, gridDim.x)) {
+    GemmParams q = p;
+    q.n_tiles = p.N / 256;
+    gemm_tiles<64, 256, 2, ACT, MOE_DUAL_BK, MOE_DUAL_STAGES, true, false>(q, ring);
+  } else {
+    gemm_tiles<64, 128, 2, ACT, 64, 4, true, false>(p, ring);
+  }
+}
+
 // Fix-up of the tail split: sums the K pieces of every split tail tile in piece order and
 // stores the tiles. Grid-stride over (tail tile, fix-up thread); the tail tiles of the XCD
 // shares are numbered in XCD order. Repeats the GEMM's schedule arithmetic from counts[]
@@ -707,6 +759,7 @@ __global__ __launch_bounds__(256) void k_gemm_streamk_reduce(const GemmParams p,
   using FR = Frag<BM, BNF, NB, Q8>;
   const int nk = p.K / BK;
   const TileScan ts = tile_scan<BM>(p);
+  if (p.dual && skinny_wide(p, grid)) return;  // the dual skinny kernel ran whole wide tiles
   const SkPlan sk = sk_plan(ts.total, grid, nk);
   const int64_t items = (int64_t)(ts.total - sk.dp) * FR::ITEMS;
   for (int64_t gi = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; gi < items; gi += (int64_t)gridDim.x * blockDim.x) {
@@ -815,6 +868,25 @@ constexpr int kSkinnyRows = 64;
 #endif
 bool skinny(const FfnArgs& a) { return a.partial != nullptr && a.max_rows_per_expert <= kSkinnyRows; }
 
+// The dual-width skinny up-projection and its stream-K fix-up (narrow tiles only).
+template <int ACT>
+hipError_t launch_dual_act(const GemmParams& p, int64_t bound, hipStream_t s) {
+  using FR = Frag<64, 128, 2, false>;
+  const int grid = persistent_grid(1 << 30);
+  const int64_t threads = (bound < grid ? bound : grid) * (int64_t)FR::ITEMS;
+  const int64_t wg = (threads + 255) / 256;
+  hipLaunchKernelGGL(k_gemm_skinny_dual<ACT>, dim3(grid), dim3(512), 0, s, p);
+  hipLaunchKernelGGL((k_gemm_streamk_reduce<64, 128, 2, ACT, 64, false>), dim3((unsigned)(wg < 2048 ? wg : 2048)),
+                     dim3(256), 0, s, p, grid);
+  return hipGetLastError();
+}
+hipError_t launch_skinny_dual(const GemmParams& p, int act, int64_t bound, hipStream_t s) {
+  if (bound <= 0) return hipSuccess;
+  if (act == ACT_SILU) return launch_dual_act<ACT_SILU>(p, bound, s);
+  if (act == ACT_GELU_ERF) return launch_dual_act<ACT_GELU_ERF>(p, bound, s);
+  return launch_dual_act<ACT_GELU_TANH>(p, bound, s);
+}
+
 }  // namespace
 
 bool expert_up_gathers(const FfnArgs& a, bool bf16_io) { return bf16_io && a.s1 == nullptr && !skinny(a); }
@@ -838,6 +910,11 @@ hipError_t launch_expert_up(const FfnArgs& a, bool bf16_io, hipStream_t s) {
     }
     return launch_bf16<256, 128, 2, 64, 3, false, true>(p, a.act, max_m_tiles(a, 256), s);
   }
+  if (skinny(a) && a.F % 256 == 0) {
+    GemmParams p{a.x_perm, a.w1, a.w2, a.h, a.offsets, a.counts, a.E, a.D, a.F, a.F / 128, a.rows, a.partial, 1};
+    p.dual = 1;
+    return launch_skinny_dual(p, a.act, max_m_tiles(a, kSkinnyRows) * (a.F / 128), s);
+  }
   if (skinny(a)) {
     constexpr int BNF = MOE_SKINNY_BNF;
     GemmParams p{a.x_perm, a.w1, a.w2, a.h, a.offsets, a.counts, a.E, a.D, a.F, a.F / BNF, a.rows, a.partial, 1};
@@ -853,38 +930,32 @@ hipError_t launch_expert_up(const FfnArgs& a, bool bf16_io, hipStream_t s) {
   return launch_bf16<BM, BNF, 2>(p, a.act, max_m_tiles(a, BM), s);
 }
 
-hipError_t launch_expert_down(const FfnArgs& a, bool bf16_io, hipStream_t s) {
-  if (!bf16_io) return launch_gemm_f32(a, false, s);
-  if (a.s3 != nullptr) {
-    GemmParams p{a.h, a.w3, nullptr, a.y_perm, a.offsets, a.counts, a.E, a.F, a.D, a.D / 128, a.rows, a.partial,
-                 kSplitMax, a.s3, nullptr};
-    if (skinny(a)) {
-      p.split_max = 1;
-      if (a.D % 256 == 0) {
-        p.n_tiles = a.D / 256;
-        return launch_bf16<kSkinnyRows, 256, 1, 64, 6, true, true>(p, a.act, max_m_tiles(a, kSkinnyRows), s);
-      }
-      return launch_bf16<kSkinnyRows, 128, 1, 64, 8, true, true>(p, a.act, max_m_tiles(a, kSkinnyRows), s);
-    }
-    return launch_bf16<256, 128, 1, 64, 4, false, true>(p, a.act, max_m_tiles(a, 256), s);
-  }
-  if (skinny(a)) {
-#ifndef MOE_SKINNY_DOWN_BNF
-#define MOE_SKINNY_DOWN_BNF 256
-#endif
-#ifndef MOE_SKINNY_DOWN_BK
-#define MOE_SKINNY_DOWN_BK 64
-#endif
+// Skinny down-projection (stream-K over 64-row tiles, every expert at most 64 rows).
 #ifndef MOE_SKINNY_DOWN_STAGES
 #define MOE_SKINNY_DOWN_STAGES 4
 #endif
-    constexpr int BNF = MOE_SKINNY_DOWN_BNF;
-    GemmParams p{a.h, a.w3, nullptr, a.y_perm, a.offsets, a.counts, a.E, a.F, a.D, a.D / BNF, a.rows, a.partial, 1};
-    if (a.D % BNF == 0)
-      return launch_bf16<kSkinnyRows, BNF, 1, MOE_SKINNY_DOWN_BK, MOE_SKINNY_DOWN_STAGES, true>(
-          p, a.act, max_m_tiles(a, kSkinnyRows), s);
-    p.n_tiles = a.D / 128;
-    return launch_bf16<kSkinnyRows, 128, 1, 64, 4, true>(p, a.act, max_m_tiles(a, kSkinnyRows), s);
+namespace {
+hipError_t launch_down_skinny(const FfnArgs& a, hipStream_t s) {
+  const int bnf = a.D % 256 == 0 ? 256 : 128;
+  const GemmParams p{a.h, a.w3, nullptr, a.y_perm, a.offsets, a.counts, a.E, a.F, a.D, a.D / bnf, a.rows, a.partial,
+                     1, a.s3, nullptr};
+  const int64_t mt = max_m_tiles(a, kSkinnyRows);
+  if (a.s3 != nullptr) {
+    if (bnf == 256) return launch_bf16<kSkinnyRows, 256, 1, 64, 6, true, true>(p, a.act, mt, s);
+    return launch_bf16<kSkinnyRows, 128, 1, 64, 8, true, true>(p, a.act, mt, s);
+  }
+  if (bnf == 256) return launch_bf16<kSkinnyRows, 256, 1, 64, MOE_SKINNY_DOWN_STAGES, true>(p, a.act, mt, s);
+  return launch_bf16<kSkinnyRows, 128, 1, 64, 4, true>(p, a.act, mt, s);
+}
+}  // namespace
+
+hipError_t launch_expert_down(const FfnArgs& a, bool bf16_io, hipStream_t s) {
+  if (!bf16_io) return launch_gemm_f32(a, false, s);
+  if (skinny(a)) return launch_down_skinny(a, s);
+  if (a.s3 != nullptr) {
+    GemmParams p{a.h, a.w3, nullptr, a.y_perm, a.offsets, a.counts, a.E, a.F, a.D, a.D / 128, a.rows, a.partial,
+                 kSplitMax, a.s3, nullptr};
+    return launch_bf16<256, 128, 1, 64, 4, false, true>(p, a.act, max_m_tiles(a, 256), s);
   }
   constexpr int BM = 256;
   if (a.D % 256 == 0) {

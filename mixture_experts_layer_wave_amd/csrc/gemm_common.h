@@ -31,6 +31,7 @@ struct GemmParams {
   const float* S1;  // [E, N] column scales of int8 B1
   const int32_t* row_token;  // or null: A row r of the product is row row_token[r] of A
                              // (persistent tiles only; rows past an expert's count unread)
+  int dual;         // skinny up-projection launched as k_gemm_skinny_dual (its fix-up checks)
 };
 
 struct Tile {

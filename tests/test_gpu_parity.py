@@ -297,6 +297,9 @@ FFN_CASES = [
     ("bf16", "gelu_erf", 256, 5120, 8, [3, 64, 0, 22, 64, 64, 1, 50]),
     # bf16 448 tiles in two rounds on 224 workgroups; int8 224 tiles in one round
     ("bf16", "silu", 256, 7168, 8, [10, 20, 30, 40, 50, 60, 64, 2]),
+    # bf16: 320 tiles of 64 x (2 x 128) would need stream-K, 160 tiles of 64 x (2 x 256) fill
+    # one round whole: the dual-width up-projection takes the wide tiles
+    ("bf16", "silu", 256, 5120, 8, [3, 64, 7, 22, 64, 64, 1, 50]),
     ("f32", "silu", 128, 256, 4, [30, 33, 0, 65]),
     ("f32", "gelu_erf", 256, 128, 3, [64, 1, 100]),
 ]
@@ -587,6 +590,9 @@ MID = [
     configs.scaled_config("mixtral_decode_int8", N=64, D=512, F=384),
     configs.scaled_config("mixtral_prefill_int8", N=700, D=256, F=512),
     configs.scaled_config("gshard_capacity", N=900, D=128, F=256, E=16, weight_dtype="int8", name="gshard_int8"),
+    # at most 64 rows per expert, all 8 experts active: wide up-projection tiles, and most
+    # down-projection tiles cut by stream-K ranges
+    configs.scaled_config("mixtral_prefill", N=64, D=256, F=5120, name="skinny_wide_tiles"),
 ]
 
 
@@ -606,6 +612,8 @@ def test_layer_mid_size(orc, cfg):
     configs.scaled_config("mixtral_prefill", N=256, D=256, F=256, routing_mode="softmax_topk", activation="gelu_erf",
                           name="prefill_256"),
     configs.scaled_config("mixtral_prefill", N=257, D=256, F=256, name="prefill_257"),
+    configs.scaled_config("mixtral_prefill", N=64, D=256, F=5120, name="skinny_wide_tiles"),
+    configs.scaled_config("mixtral_decode_int8", N=64, D=512, F=5120, name="decode_int8_f5120"),
 ], ids=lambda c: c["name"])
 def test_layer_bitwise_reproducible_and_equal_to_steps(orc, cfg):
     inp = inputs.make_inputs(cfg)
