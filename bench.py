@@ -49,14 +49,18 @@ def parse():
     p.add_argument("--cold-reps", type=int, default=5,
                    help="cold-cache runs of each small stage before the warm-up (0: none)")
     p.add_argument("--copy-mib", type=int, default=0,
-                   help="instead of the bench: run a plain device copy of this many MiB `steps` times "
-                        "(calibration of the HBM byte counters)")
+                   help="instead of the bench: run a device copy of this many MiB `steps` times "
+                        "(calibration of the memory-traffic counters)")
+    p.add_argument("--copy-kind", choices=("lds", "blit"), default="lds",
+                   help="calibration copy: reads by direct-to-LDS copies, the GEMMs' read path (lds), or "
+                        "the runtime's blit kernel (blit)")
     return p.parse_args()
 
 
 def traffic_from_profiles(workload: str, kernel_stage: str):
-    """HBM bytes per launch from the committed rocprofv3 counter summary, if it was taken
-    on the current kernel sources; else None."""
+    """Memory-side bytes per launch (L2 misses and write-backs, Infinity Cache or HBM) from
+    the committed rocprofv3 counter summary, if it was taken on the current kernel sources;
+    else None."""
     path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
     if not os.path.exists(path):
         return None
@@ -66,7 +70,7 @@ def traffic_from_profiles(workload: str, kernel_stage: str):
     if t.get("source_hash") != source_hash():
         return None
     st = t.get("stages", {}).get(kernel_stage)
-    return None if st is None else st.get("hbm_bytes_per_launch")
+    return None if st is None else st.get("memory_bytes_per_launch")
 
 
 def _cpu_model() -> str:
@@ -327,10 +331,24 @@ def main():
     if args.copy_mib > 0:
         src = torch.empty(args.copy_mib * 2 ** 20, dtype=torch.uint8, device="cuda:0")
         dst = torch.empty_like(src)
-        for _ in range(args.steps):
-            dst.copy_(src)
+        if args.copy_kind == "lds":
+            import ctypes
+            from mixture_experts_layer_wave_amd.build import CALIB_LIB
+            if not os.path.exists(CALIB_LIB):
+                raise RuntimeError(f"calibration library not built: {CALIB_LIB}")
+            L = ctypes.CDLL(CALIB_LIB)
+            L.moe_calib_copy_lds.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+            stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+            for _ in range(args.steps):
+                rc = L.moe_calib_copy_lds(ctypes.c_void_p(src.data_ptr()), ctypes.c_void_p(dst.data_ptr()),
+                                          src.numel(), stream)
+                if rc != 0:
+                    raise RuntimeError(f"moe_calib_copy_lds failed: {rc}")
+        else:
+            for _ in range(args.steps):
+                dst.copy_(src)
         torch.cuda.synchronize()
-        print(json.dumps({"copy_mib": args.copy_mib, "copies": args.steps}), flush=True)
+        print(json.dumps({"copy_mib": args.copy_mib, "copies": args.steps, "kind": args.copy_kind}), flush=True)
         return
     from mixture_experts_layer_wave_amd import binding as B
     from mixture_experts_layer_wave_amd import configs, inputs
@@ -347,6 +365,8 @@ def main():
     gemm_tflops = (work["expert_up"]["flops"] + work["expert_down"]["flops"]) / (gemm_ms * 1e-3) / 1e12
     roof = m["roofline"]
     roof["traffic"] = traffic_from_profiles(args.workload, dom)
+    roof["traffic_what"] = ("bytes per launch through the L2's memory-side interface (Infinity Cache hits "
+                            "included), rocprofv3 FETCH_SIZE + WRITE_SIZE scaled by a direct-to-LDS copy")
     # The weight-streaming decode regime of the same expert shapes, measured in the same run.
     decode = None
     if args.decode and args.workload != "mixtral_decode":

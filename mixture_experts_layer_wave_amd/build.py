@@ -17,6 +17,9 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmoe_mi355x.so")
 SOURCES = ["router.hip", "dispatch.hip", "combine.hip", "gemm_f32.hip", "gemm_bf16.hip", "moe_api.cpp"]
+# measurement tooling (the memory-counter calibration copy), a library of its own
+CALIB_LIB = os.path.join(PKG, "libmoe_calib.so")
+CALIB_SOURCES = ["calib_copy.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
     "-x", "hip", "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
@@ -37,17 +40,24 @@ def _compile(src: str, extra) -> str:
     return obj
 
 
-def build_library(extra_flags=(), verbose: bool = True) -> str:
-    """Compile every source and link the shared library; returns its path."""
-    os.makedirs(BUILD, exist_ok=True)
-    with ThreadPoolExecutor(len(SOURCES)) as ex:
-        objs = list(ex.map(lambda s: _compile(s, list(extra_flags)), SOURCES))
-    tmp = LIB + ".tmp"
+def _link(objs, lib: str) -> None:
+    tmp = lib + ".tmp"
     cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs]
     subprocess.run(cmd, check=True)
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build_library(extra_flags=(), verbose: bool = True) -> str:
+    """Compile every source and link the shared library (and the calibration library);
+    returns the layer library's path."""
+    os.makedirs(BUILD, exist_ok=True)
+    srcs = SOURCES + CALIB_SOURCES
+    with ThreadPoolExecutor(len(srcs)) as ex:
+        objs = dict(zip(srcs, ex.map(lambda s: _compile(s, list(extra_flags)), srcs)))
+    _link([objs[s] for s in SOURCES], LIB)
+    _link([objs[s] for s in CALIB_SOURCES], CALIB_LIB)
     if verbose:
-        print(f"built {LIB}")
+        print(f"built {LIB} and {CALIB_LIB}")
     return LIB
 
 

@@ -11,11 +11,14 @@ Two commands, both reading the CSV files that ``rocprofv3 --output-format csv`` 
             per kernel with matrix-core work, the busy percentage and the bf16 flops it
             executed per dispatch, next to the useful flops of the stage when given.
 ``traffic`` two counter runs (``FETCH_SIZE`` and ``WRITE_SIZE``, KiB per dispatch) of the
-            bench, and the same two counters for a plain device copy of known size. The
-            copy gives the factor that turns counter KiB into bytes actually moved
-            (bytes copied / counter bytes); the stage averages are scaled by it and written
-            as JSON together with a hash of the kernel sources, so that a later change of
-            the kernels invalidates them.
+            bench, and the same two counters for a device copy of known size whose reads
+            use the GEMMs' direct-to-LDS copies. The copy gives the factor that turns
+            counter KiB into bytes actually moved (bytes copied / counter bytes); the stage
+            averages are scaled by it and written as JSON together with a hash of the
+            kernel sources, so that a later change of the kernels invalidates them. The
+            counters sit at the L2's memory-side interface: the bytes are L2 misses and
+            write-backs, served by the Infinity Cache or by HBM (the counters cannot tell
+            which).
 
 Stage of a kernel: from its name and, for the templated GEMMs, the NB template argument
 (2 = gated up-projection with two weight matrices, 1 = down-projection).
@@ -83,8 +86,8 @@ def stage_of(name: str) -> str:
         return "dispatch"
     if base == "k_route_dispatch_small":  # launched by moe_forward only (route epilogue + dispatch)
         return "forward"
-    if base == "k_gemm_bf16" and len(args) >= 9 and args[8] == 1:  # gathered rows: moe_forward only
-        return "forward"
+    if base == "k_gemm_skinny_dual":  # dual-width skinny up-projection
+        return "expert_up"
     if base in ("k_gemm_bf16", "k_gemm_tail_reduce", "k_gemm_streamk_reduce") and len(args) >= 3:
         return "expert_up" if args[2] == 2 else "expert_down"
     if base == "k_gemm_f32":
@@ -161,12 +164,15 @@ def cmd_stats(a):
         tl, inf = last.get(r["name"], (float("nan"), ("", "", "", "", "", "")))
         lines.append(f"| `{short_name(r['name'])}` | {st} | {r['calls']} | {r['avg_us']:.2f} | {tl:.2f} | "
                      f"{r['min_us']:.2f} | {r['max_us']:.2f} | {inf[0]} x {inf[1]} | {inf[2]}+{inf[3]} | {inf[4]} |")
-        if st not in ("other", "forward"):
+        # a kernel called fewer times than the timed loop (e.g. once while setting up) is
+        # not one of the stage's timed kernels
+        if st not in ("other", "forward", "stats") and (not a.last or r["calls"] >= a.last):
             stage[st] += r["avg_us"]
             stage_last[st] += tl
     bench = bench_stages(a.bench_log) if a.bench_log else None
     lines += ["", "Per-stage sums of the per-stage entry points' kernels (stage `forward`: kernels that only "
-              "moe_forward launches, not summed). `bench events` is what bench.py measured for the stage with "
+              "moe_forward launches, not summed; kernels called fewer times than the timed loop, e.g. once "
+              "while setting up, not summed). `bench events` is what bench.py measured for the stage with "
               "HIP events on the launch stream in the same run.", "",
               "| stage | avg us | timed avg us | bench events us |", "|---|---:|---:|---:|"]
     for st in STAGE_ORDER:
@@ -181,8 +187,8 @@ def cmd_stats(a):
     print(text)
 
 
-def counter_avgs(counter_csv: str, counter: str):
-    """Average value of `counter` per dispatch, per kernel name."""
+def counter_avgs(counter_csv: str, counter: str, with_counts: bool = False):
+    """Average value of `counter` per dispatch, per kernel name (and the dispatch counts)."""
     tot, disp = defaultdict(float), defaultdict(set)
     with open(counter_csv) as f:
         for r in csv.DictReader(f):
@@ -190,7 +196,8 @@ def counter_avgs(counter_csv: str, counter: str):
                 continue
             tot[r["Kernel_Name"]] += float(r["Counter_Value"])
             disp[r["Kernel_Name"]].add(r["Dispatch_Id"])
-    return {k: tot[k] / len(disp[k]) for k in tot}
+    avg = {k: tot[k] / len(disp[k]) for k in tot}
+    return (avg, {k: len(v) for k, v in disp.items()}) if with_counts else avg
 
 
 def cmd_mfma(a):
@@ -219,9 +226,75 @@ def cmd_mfma(a):
     print(text)
 
 
+def all_counter_avgs(counter_csv: str):
+    """{kernel name: {counter: average value per dispatch}} over every counter of a run."""
+    tot, disp = defaultdict(lambda: defaultdict(float)), defaultdict(lambda: defaultdict(set))
+    with open(counter_csv) as f:
+        for r in csv.DictReader(f):
+            tot[r["Kernel_Name"]][r["Counter_Name"]] += float(r["Counter_Value"])
+            disp[r["Kernel_Name"]][r["Counter_Name"]].add(r["Dispatch_Id"])
+    return {k: {c: v / len(disp[k][c]) for c, v in cs.items()} for k, cs in tot.items()}
+
+
+# Ratios reported by `counters` when their operands were collected (each from one run).
+DERIVED = [
+    ("L2 hit %", "TCC_HIT_sum", "TCC_MISS_sum", lambda h, m: 100.0 * h / (h + m)),
+    ("memory-side read latency (L2 cycles)", "TCC_EA0_RDREQ_LEVEL_sum", "TCC_EA0_RDREQ_sum", lambda l, n: l / n),
+    ("TA busy / GUI active (summed over TA instances)", "TA_TA_BUSY_sum", "GRBM_GUI_ACTIVE", lambda a, b: a / b),
+    ("TA address stalled by L1 / TA busy %", "TA_ADDR_STALLED_BY_TC_CYCLES_sum", "TA_TA_BUSY_sum",
+     lambda a, b: 100.0 * a / b),
+    ("LDS data FIFO full / SQ busy %", "SQ_LDS_DATA_FIFO_FULL", "SQ_BUSY_CYCLES", lambda a, b: 100.0 * a / b),
+    ("LDS command FIFO full / SQ busy %", "SQ_LDS_CMD_FIFO_FULL", "SQ_BUSY_CYCLES", lambda a, b: 100.0 * a / b),
+    ("LDS bank conflict / LDS active %", "SQ_LDS_BANK_CONFLICT", "SQ_LDS_IDX_ACTIVE", lambda a, b: 100.0 * a / b),
+]
+
+
+def cmd_counters(a):
+    """Counter averages per dispatch of the stage kernels from one or more --pmc runs (one
+    directory per run), with the ratios of DERIVED whose operands come from one run."""
+    runs = [all_counter_avgs(_one(os.path.join(d, "**", "*counter_collection.csv"))) for d in a.dirs]
+    kernels = sorted({k for r in runs for k in r if stage_of(k) in a.stages},
+                     key=lambda k: (STAGE_ORDER.index(stage_of(k)), k))
+    lines = [f"# Counters: {a.title}", "", "Command:", "", "```", a.cmd, "```", "",
+             f"Kernel sources hash: `{source_hash()}`", "",
+             "Averages per dispatch over every call of each kernel in the run (one `--pmc` run per "
+             "directory, counters from different runs are never combined in a ratio).", ""]
+    for i, r in enumerate(runs):
+        names = sorted({c for k in kernels if k in r for c in r[k]})
+        if not names:
+            continue
+        lines += [f"Run {i + 1}: `{a.dirs[i]}`", "", "| kernel | stage | " + " | ".join(names) + " |",
+                  "|---|---|" + "---:|" * len(names)]
+        for k in kernels:
+            if k not in r:
+                continue
+            lines.append(f"| `{short_name(k)}` | {stage_of(k)} | " +
+                         " | ".join(f"{r[k].get(c, float('nan')):.6g}" for c in names) + " |")
+        lines.append("")
+        rows = []
+        for title, x, y, f in DERIVED:
+            if f is None:
+                continue
+            for k in kernels:
+                if k in r and x in r[k] and y in r[k] and r[k][y] > 0:
+                    rows.append(f"| `{short_name(k)}` | {title} | {f(r[k][x], r[k][y]):.4g} |")
+        if rows:
+            lines += ["| kernel | derived | value |", "|---|---|---:|"] + rows + [""]
+    text = "\n".join(lines)
+    if a.out:
+        with open(a.out, "w") as fo:
+            fo.write(text)
+    print(text)
+
+
 def cmd_traffic(a):
-    fetch = counter_avgs(_one(os.path.join(a.fetch, "**", "*counter_collection.csv")), "FETCH_SIZE")
+    fetch, nf = counter_avgs(_one(os.path.join(a.fetch, "**", "*counter_collection.csv")), "FETCH_SIZE", True)
     write = counter_avgs(_one(os.path.join(a.write, "**", "*counter_collection.csv")), "WRITE_SIZE")
+    # a kernel dispatched far fewer times than the rest of its stage (e.g. once while the
+    # bench sets up) is not one of the stage's kernels per launch
+    most = defaultdict(int)
+    for k, n in nf.items():
+        most[stage_of(k)] = max(most[stage_of(k)], n)
     cf = counter_avgs(_one(os.path.join(a.copy_fetch, "**", "*counter_collection.csv")), "FETCH_SIZE")
     cw = counter_avgs(_one(os.path.join(a.copy_write, "**", "*counter_collection.csv")), "WRITE_SIZE")
     # the copy run launches one kernel kind: the largest per-dispatch figure is the copy
@@ -231,17 +304,20 @@ def cmd_traffic(a):
     stages = defaultdict(lambda: {"fetch_kib": 0.0, "write_kib": 0.0, "kernels": []})
     for k in sorted(set(fetch) | set(write)):
         st = stage_of(k)
-        if st == "other":
+        if st == "other" or 2 * nf.get(k, 0) < most[st]:
             continue
         stages[st]["fetch_kib"] += fetch.get(k, 0.0)
         stages[st]["write_kib"] += write.get(k, 0.0)
         stages[st]["kernels"].append(short_name(k))
     out = {"workload": a.workload, "source_hash": source_hash(), "copy_mib": a.copy_mib,
-           "scale_fetch": f_fetch, "scale_write": f_write, "command": a.cmd, "stages": {}}
+           "copy_kind": a.copy_kind, "scale_fetch": f_fetch, "scale_write": f_write,
+           "what": "bytes through the L2's memory-side interface per launch (L2 misses and write-backs, served "
+                   "by the Infinity Cache or HBM): FETCH_SIZE and WRITE_SIZE scaled by the calibration copy",
+           "command": a.cmd, "stages": {}}
     for st, v in stages.items():
-        hbm = v["fetch_kib"] * 1024.0 * f_fetch + v["write_kib"] * 1024.0 * f_write
+        mem = v["fetch_kib"] * 1024.0 * f_fetch + v["write_kib"] * 1024.0 * f_write
         out["stages"][st] = {"kernels": v["kernels"], "fetch_kib_per_launch": v["fetch_kib"],
-                             "write_kib_per_launch": v["write_kib"], "hbm_bytes_per_launch": hbm}
+                             "write_kib_per_launch": v["write_kib"], "memory_bytes_per_launch": mem}
     text = json.dumps(out, indent=1)
     if a.out:
         with open(a.out, "w") as f:
@@ -259,12 +335,19 @@ def main():
     s.add_argument("--last", type=int, default=0, help="also average the last N calls of each kernel")
     s.add_argument("--bench-log", help="log of the profiled bench.py run (its JSON line)")
     s.add_argument("--out")
+    c = sub.add_parser("counters")
+    c.add_argument("dirs", nargs="+", help="rocprofv3 --pmc output directories, one per run")
+    c.add_argument("--title", required=True)
+    c.add_argument("--cmd", required=True)
+    c.add_argument("--stages", nargs="+", default=["expert_up", "expert_down"])
+    c.add_argument("--out")
     t = sub.add_parser("traffic")
     t.add_argument("--fetch", required=True)
     t.add_argument("--write", required=True)
     t.add_argument("--copy-fetch", required=True)
     t.add_argument("--copy-write", required=True)
     t.add_argument("--copy-mib", type=int, required=True)
+    t.add_argument("--copy-kind", default="lds", help="the calibration copy's read path (bench.py --copy-kind)")
     t.add_argument("--workload", required=True)
     t.add_argument("--cmd", required=True)
     t.add_argument("--out")
@@ -275,7 +358,7 @@ def main():
     m.add_argument("--useful", nargs="*", help="stage=flops pairs (useful flops per launch)")
     m.add_argument("--out")
     a = p.parse_args()
-    {"stats": cmd_stats, "traffic": cmd_traffic, "mfma": cmd_mfma}[a.cmd_name](a)
+    {"stats": cmd_stats, "traffic": cmd_traffic, "mfma": cmd_mfma, "counters": cmd_counters}[a.cmd_name](a)
 
 
 if __name__ == "__main__":

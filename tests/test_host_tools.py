@@ -29,9 +29,11 @@ def test_bench_refuses_more_than_one_gpu():
      "k_gemm_bf16", [64, 256, 1, 0, 64, 4, 1, 0], "expert_down"),
     ("void moe::(anonymous namespace)::k_gemm_bf16<256, 128, 2, 0, 64, 2, false, false, false>(moe::GemmParams)",
      "k_gemm_bf16", [256, 128, 2, 0, 64, 2, 0, 0, 0], "expert_up"),
-    # gathered-row instance: launched by moe_forward only
+    # gathered-row instance: moe_forward and moe_expert_up_gathered
     ("void moe::(anonymous namespace)::k_gemm_bf16<256, 128, 2, 1, 64, 2, false, false, true>(moe::GemmParams)",
-     "k_gemm_bf16", [256, 128, 2, 1, 64, 2, 0, 0, 1], "forward"),
+     "k_gemm_bf16", [256, 128, 2, 1, 64, 2, 0, 0, 1], "expert_up"),
+    ("void moe::(anonymous namespace)::k_gemm_skinny_dual<0>(moe::GemmParams)", "k_gemm_skinny_dual", [0],
+     "expert_up"),
     ("k_gemm_streamk_reduce<64, 128, 2, 0, 64, false>", "k_gemm_streamk_reduce", [64, 128, 2, 0, 64, 0], "expert_up"),
     ("void moe::(anonymous namespace)::k_router_epi<8>(moe::RouterArgs, moe::RouterSplit)", "k_router_epi", [8],
      "route"),
