@@ -595,11 +595,25 @@ __global__ __launch_bounds__(64) void k_stats(const StatsArgs a) {
   const int e = threadIdx.x;
   const bool have_p = *a.psum_magic == kPsumMagic;
   if (e < a.E) {
+    // sum of the block sums in block order; 16 loads in flight ahead of the adds
     double s = 0.0;
-    if (have_p)
-      for (int b = 0; b < a.nblk_r; ++b) s += (double)a.psum[(int64_t)b * a.E + e];
+    if (have_p) {
+      constexpr int U = 16;
+      for (int b0 = 0; b0 < a.nblk_r; b0 += U) {
+        float v[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) v[u] = a.psum[(int64_t)min(b0 + u, a.nblk_r - 1) * a.E + e];  // unconditional
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+          if (b0 + u < a.nblk_r) s += (double)v[u];
+      }
+    }
     P_s[e] = s / (double)a.N;
   }
+  // tokens with every slot dropped: integer sum over the dispatch blocks, spread over the wave
+  int64_t dtok_l = 0;
+  for (int b = e; b < a.nblk_d; b += 64) dtok_l += a.tokdrop[b];
+  for (int off = 32; off > 0; off >>= 1) dtok_l += __shfl_down(dtok_l, off);
   __syncthreads();
   if (e == 0) {
     DevStats st;
@@ -611,8 +625,7 @@ __global__ __launch_bounds__(64) void k_stats(const StatsArgs a) {
       bal += ((double)l / ((double)a.N * (double)a.k)) * P_s[x];
       baln += ((double)l / (double)a.N) * P_s[x];
     }
-    int64_t dtok = 0;
-    for (int b = 0; b < a.nblk_d; ++b) dtok += a.tokdrop[b];
+    const int64_t dtok = dtok_l;
     st.routed_slots = a.N * a.k;
     st.dropped_slots = dslots;
     st.dropped_tokens = dtok;
