@@ -32,7 +32,28 @@ PEAK_F32_TFLOPS = 157.3       # MI355X fp32
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 RIDGE = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
 STAGES = ["route", "dispatch", "expert_up", "expert_down", "combine"]
-KERNEL_OF_STAGE = {"expert_up": "k_gemm_bf16 (gated up-projection)", "expert_down": "k_gemm_bf16 (down-projection)"}
+
+
+def gemm_kernel_of(cfg, stage: str, gathered: bool, capacity) -> str:
+    """Name of the grouped-GEMM kernel the library launches for a stage of this workload
+    (the launch rules of gemm_bf16.hip: fp32 layers, int8 weights, the skinny regime of at
+    most 64 rows per expert, and mixed tile heights when the output width is a multiple of
+    256). capacity: the library's C for padded layers, else None."""
+    what = "gated up-projection" if stage == "expert_up" else "down-projection"
+    if cfg["dtype"] == "f32":
+        return f"k_gemm_f32 ({what})"
+    max_rows = min(cfg["N"], capacity) if capacity is not None else cfg["N"]
+    width = cfg["F"] if stage == "expert_up" else cfg["D"]
+    if max_rows <= 64:
+        if stage == "expert_up" and width % 256 == 0 and cfg.get("weight_dtype", "same") != "int8":
+            return f"k_gemm_skinny_dual ({what}, 64-row tiles of two widths)"
+        return f"k_gemm_bf16 ({what}, 64-row stream-K tiles)"
+    if cfg.get("weight_dtype", "same") == "int8":
+        return f"k_gemm_bf16 ({what}, int8 weights)"
+    if width % 256 == 0:
+        rows = "rows gathered from x, " if gathered else ""
+        return f"k_gemm_mixed ({what}, {rows}256-row tiles, small remainders on 64-row tiles)"
+    return f"k_gemm_bf16 ({what})"
 
 
 def parse():
@@ -310,10 +331,8 @@ def measure_layer(B, cfg, inp, args, dev, cold_reps: int, graph: bool) -> dict:
     else:
         roof = {"bound": "hbm", "achieved": w["bytes"] / sec / 1e9, "peak": PEAK_HBM_GBS, "unit": "GB/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    kernel = KERNEL_OF_STAGE[dom]
-    if dom == "expert_up" and up is up_gathered:
-        kernel = "k_gemm_bf16, rows gathered from x (gated up-projection, the instance moe_forward runs)"
-    roof["kernel"] = kernel
+    cap = B.moe_capacity(d) if cfg["capacity_mode"] == "padded" else None
+    roof["kernel"] = gemm_kernel_of(cfg, dom, dom == "expert_up" and up is up_gathered, cap)
     roof["per_launch"] = {"flops": w["flops"], "algorithmic_bytes": w["bytes"], "avg_ms": stage_ms[dom]}
     return dict(elapsed=elapsed, forward_ms=forward_ms, staged_ms_per_step=staged_ms_per_step, graph=graph_res,
                 stage_ms=stage_ms, stage_pct=stage_pct, cold_ms=cold_ms, small=small, work=work, dom=dom, A=A,

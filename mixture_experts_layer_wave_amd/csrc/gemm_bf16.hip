@@ -299,9 +299,10 @@ struct Ring {
 };
 
 template <int BM, int BNF, int NB, int ACT, int BK, int STAGES, bool STREAMK, bool Q8, bool GA = false>
-__device__ __forceinline__ void gemm_tiles(const GemmParams& p, bf16* ring) {
-  // GA: gathered A rows (p.row_token), persistent tiles only.
-  static_assert(!GA || !STREAMK, "gathered rows with persistent tiles");
+__device__ __forceinline__ void gemm_tiles(const GemmParams& p, bf16* ring, const int bx, const int gd) {
+  // bx, gd: this workgroup's index among the gd workgroups that share the tile list
+  // (blockIdx.x and gridDim.x, or one part of the grid of a mixed-height launch; gd % 8 == 0).
+  // GA: gathered A rows (p.row_token).
   // BK: K slice per pipeline stage; STAGES: LDS ring depth (STAGES-1 slices in flight).
   // Q8: B0/B1 are int8 with per-column scales S0/S1 (weight-only 8-bit experts).
   constexpr int WB = Q8 ? 1 : 2;            // bytes per B element
@@ -344,9 +345,9 @@ __device__ __forceinline__ void gemm_tiles(const GemmParams& p, bf16* ring) {
   const int nk = K / BK;
 
   const TileScan ts = tile_scan<BM>(p);
-  const int xcd = blockIdx.x % kXcds;
-  const int slot = blockIdx.x / kXcds;
-  const int nslot = gridDim.x / kXcds;
+  const int xcd = bx % kXcds;
+  const int slot = bx / kXcds;
+  const int nslot = gd / kXcds;
   const XcdShare sh = xcd_share(ts.total, xcd, kXcds, nslot, nk, p);
 
   // LDS layouts (no padding; 16-byte chunks XOR-swizzled so the MFMA operand reads are
@@ -385,11 +386,11 @@ __device__ __forceinline__ void gemm_tiles(const GemmParams& p, bf16* ring) {
   int64_t sk_s0 = 0, sk_s1 = 0;
   SkPlan sk{0, 0, 1};
   if constexpr (STREAMK) {
-    sk = sk_plan(ts.total, gridDim.x, nk);
-    const int b = blockIdx.x;
+    sk = sk_plan(ts.total, gd, nk);
+    const int b = bx;
     dp_rounds = b < min(sk.dp, sk.stride) ? (sk.dp - b + sk.stride - 1) / sk.stride : 0;
-    sk_s0 = sk_begin(blockIdx.x, sk.W, gridDim.x);
-    sk_s1 = sk_begin(blockIdx.x + 1, sk.W, gridDim.x);
+    sk_s0 = sk_begin(bx, sk.W, gd);
+    sk_s1 = sk_begin(bx + 1, sk.W, gd);
     sk_t0 = (int)(sk_s0 / nk);
     units = dp_rounds + (sk_s1 > sk_s0 ? (int)((sk_s1 - 1) / nk) - sk_t0 + 1 : 0);
   } else {
@@ -402,13 +403,13 @@ __device__ __forceinline__ void gemm_tiles(const GemmParams& p, bf16* ring) {
     pslot = -1;
     if constexpr (STREAMK) {
       if (u < dp_rounds) {
-        L = blockIdx.x + u * sk.stride;
+        L = bx + u * sk.stride;
       } else {
         const int ls = sk_t0 + (u - dp_rounds);  // tile index within the stream-K tiles
         const int64_t base = (int64_t)ls * nk;
         kb = (int)(max(sk_s0, base) - base);
         ke = (int)(min(sk_s1, base + nk) - base);
-        if (kb != 0 || ke != nk) pslot = 2 * blockIdx.x + (u == dp_rounds ? 0 : 1);
+        if (kb != 0 || ke != nk) pslot = 2 * bx + (u == dp_rounds ? 0 : 1);
         L = sk.dp + ls;
       }
     } else if (u < sh.rounds) {
@@ -421,7 +422,7 @@ __device__ __forceinline__ void gemm_tiles(const GemmParams& p, bf16* ring) {
       if (sh.S > 1) pslot = xcd * nslot + slot;
     }
   };
-  // Gathered A (p.row_token, persistent tiles only): A row r of the product is row
+  // Gathered A (p.row_token): A row r of the product is row
   // row_token[r] of p.A. Lane's A copy q covers row A_RPC (A_CP wid + q) + lane / A_CPR of
   // the tile; its token is read one tile ahead, before the epilogue of the previous tile.
   auto load_tokens = [&](const Tile& t, int (&tk)[A_CP]) {
@@ -675,7 +676,7 @@ __device__ __forceinline__ void gemm_tiles(const GemmParams& p, bf16* ring) {
 template <int BM, int BNF, int NB, int ACT, int BK, int STAGES, bool STREAMK, bool Q8, bool GA = false>
 __global__ __launch_bounds__(512, 1) void k_gemm_bf16(const GemmParams p) {
   __shared__ __attribute__((aligned(1024))) bf16 ring[Ring<BM, BNF, NB, BK, STAGES, STREAMK, Q8>::EL];
-  gemm_tiles<BM, BNF, NB, ACT, BK, STAGES, STREAMK, Q8, GA>(p, ring);
+  gemm_tiles<BM, BNF, NB, ACT, BK, STAGES, STREAMK, Q8, GA>(p, ring, blockIdx.x, gridDim.x);
 }
 
 // Skinny gated up-projection (every expert at most 64 rows) with two tile widths in one
@@ -706,9 +707,9 @@ __global__ __launch_bounds__(512, 1) void k_gemm_skinny_dual(const GemmParams p)
   if (skinny_wide(p, gridDim.x)) {
     GemmParams q = p;
     q.n_tiles = p.N / 256;
-    gemm_tiles<64, 256, 2, ACT, MOE_DUAL_BK, MOE_DUAL_STAGES, true, false>(q, ring);
+    gemm_tiles<64, 256, 2, ACT, MOE_DUAL_BK, MOE_DUAL_STAGES, true, false>(q, ring, blockIdx.x, gridDim.x);
   } else {
-    gemm_tiles<64, 128, 2, ACT, 64, 4, true, false>(p, ring);
+    gemm_tiles<64, 128, 2, ACT, 64, 4, true, false>(p, ring, blockIdx.x, gridDim.x);
   }
 }
 
@@ -718,8 +719,9 @@ __global__ __launch_bounds__(512, 1) void k_gemm_skinny_dual(const GemmParams p)
 // so both kernels agree on the split. Every wave handles 64 consecutive threads of one
 // tile (ITEMS is a multiple of 64), so the tile lookup stays wave-uniform.
 template <int BM, int BNF, int NB, int ACT, int BK, bool Q8>
-__global__ __launch_bounds__(256) void k_gemm_tail_reduce(const GemmParams p, int nslot) {
+__device__ __forceinline__ void tail_reduce(const GemmParams& p, const int nslot) {
   using FR = Frag<BM, BNF, NB, Q8>;
+  if (nslot <= 0) return;  // no workgroups ran persistent tiles
   const int nk = p.K / BK;
   const TileScan ts = tile_scan<BM>(p);
   int total = 0;
@@ -750,16 +752,20 @@ __global__ __launch_bounds__(256) void k_gemm_tail_reduce(const GemmParams p, in
     });
   }
 }
+template <int BM, int BNF, int NB, int ACT, int BK, bool Q8>
+__global__ __launch_bounds__(256) void k_gemm_tail_reduce(const GemmParams p, int nslot) {
+  tail_reduce<BM, BNF, NB, ACT, BK, Q8>(p, nslot);
+}
 
 // Stream-K fix-up: for every stream-K tile cut by a range boundary, sums the partials of
 // the workgroups that share it in workgroup order and stores the tile. Grid-stride over
 // (stream-K tile, fix-up thread), wave-uniform tiles as above.
 template <int BM, int BNF, int NB, int ACT, int BK, bool Q8>
-__global__ __launch_bounds__(256) void k_gemm_streamk_reduce(const GemmParams p, int grid) {
+__device__ __forceinline__ void streamk_reduce(const GemmParams& p, const int grid) {
   using FR = Frag<BM, BNF, NB, Q8>;
+  if (grid <= 0) return;  // no workgroups ran stream-K tiles
   const int nk = p.K / BK;
   const TileScan ts = tile_scan<BM>(p);
-  if (p.dual && skinny_wide(p, grid)) return;  // the dual skinny kernel ran whole wide tiles
   const SkPlan sk = sk_plan(ts.total, grid, nk);
   const int64_t items = (int64_t)(ts.total - sk.dp) * FR::ITEMS;
   for (int64_t gi = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; gi < items; gi += (int64_t)gridDim.x * blockDim.x) {
@@ -780,6 +786,132 @@ __global__ __launch_bounds__(256) void k_gemm_streamk_reduce(const GemmParams p,
       return false;
     });
   }
+}
+template <int BM, int BNF, int NB, int ACT, int BK, bool Q8>
+__global__ __launch_bounds__(256) void k_gemm_streamk_reduce(const GemmParams p, int grid) {
+  if (p.dual && skinny_wide(p, grid)) return;  // the dual skinny kernel ran whole wide tiles
+  streamk_reduce<BM, BNF, NB, ACT, BK, Q8>(p, grid);
+}
+
+// ---- mixed tile heights ----------------------------------------------------------------
+// A launch whose experts' rows mostly fill 256-row tiles, but where some experts end in a
+// small remainder (1..64 rows past their last whole 256-row block, or fewer than 65 rows
+// in all): a 256-row tile over such a remainder still streams its whole weight panel
+// through LDS for a few rows. The workgroups of each XCD may instead split into two shares
+// that run concurrently: the big share runs the 256-row tiles of all other rows (persistent
+// XCD schedule, tail split along K), the small share runs 64-row tiles (twice as wide) over
+// the small remainders with stream-K. Each share's work is estimated as its tiles x the
+// elements one tile copies into LDS per row of a K slice, a small tile's weighted by
+// MOE_MIX_SHARED_COST percent when its expert also has 256-row tiles (the same weight
+// panels pass through L2 for those) and by MOE_MIX_LONE_COST percent when not (its panels
+// come from HBM alone); measured: a small share sized too small leaves it the slower one by
+// far, one sized too large costs little. The size of the small share (whole XCD slots, or
+// none: then every row runs on 256-row tiles as in k_gemm_bf16) is the one with the earliest
+// estimated finish of the slower share. Integer arithmetic on counts[] only, so the GEMM and
+// its fix-up agree; every output element is one fp32 sum over K in a fixed order whatever
+// the split.
+#ifndef MOE_MIX_SHARED_COST
+#define MOE_MIX_SHARED_COST 70
+#endif
+#ifndef MOE_MIX_LONE_COST
+#define MOE_MIX_LONE_COST 100
+#endif
+constexpr int kMixRemMax = 64;
+
+// The tile list of one share: part 0 (every row on 256-row tiles), 1 (big share) or 2
+// (small share).
+template <int NB, int BNF_B, int BNF_S>
+__device__ __forceinline__ GemmParams mixed_view(const GemmParams& p, int part) {
+  GemmParams q = p;
+  q.part = part;
+  q.rem_max = kMixRemMax;
+  q.n_tiles = p.N / (part == 2 ? BNF_S : BNF_B);
+  return q;
+}
+
+// Estimated finish time of a split with s of the n slots per XCD in the small share, as a
+// fraction num / den (the slower share's work per slot).
+struct MixTime {
+  int64_t num, den;
+};
+__device__ __forceinline__ bool mix_faster(MixTime a, MixTime b) { return a.num * b.den < b.num * a.den; }
+__device__ __forceinline__ MixTime mix_time(int64_t wb, int64_t ws, int s, int n) {
+  if (s == 0) return MixTime{wb, n};
+  const MixTime big{wb, n - s}, small{ws, s};
+  if (s == n) return small;
+  return mix_faster(big, small) ? small : big;
+}
+
+// Workgroups of the small share (a multiple of kXcds, 0 for none) out of G: the better of
+// no split and the two whole slot counts around the balance point
+// s* = n ws / (wb + ws), where both shares' work per slot is equal.
+template <int NB, int BNF_B, int BNF_S>
+__device__ __forceinline__ int mixed_small_wgs(const GemmParams& p, int G) {
+  // weighted small tiles: one 64-row tile row per expert with a small remainder (lane e =
+  // expert e, E <= 64), summed over the wave in a fixed butterfly order
+  const int lane = lane_id();
+  int c = lane < p.E ? p.counts[lane] : 0;
+  c = c < 0 ? 0 : c;
+  const int rem = c % kMixBlockRows;
+  int64_t wsl = (rem > 0 && rem <= kMixRemMax) ? (c > rem ? MOE_MIX_SHARED_COST : MOE_MIX_LONE_COST) : 0;
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) wsl += __shfl_xor(wsl, off);
+  const int n = G / kXcds;
+  if (wsl == 0 || n < 2) return 0;
+  const int t0 = tile_scan<256>(mixed_view<NB, BNF_B, BNF_S>(p, 0)).total;
+  const int tb = tile_scan<256>(mixed_view<NB, BNF_B, BNF_S>(p, 1)).total;
+  const int64_t cb = (256 + NB * BNF_B) * 100;
+  const int64_t wb = (int64_t)tb * cb, w0 = (int64_t)t0 * cb;
+  const int64_t ws = wsl * (p.N / BNF_S) * (64 + NB * BNF_S);
+  const int smax = tb > 0 ? n - 1 : n;
+  int lo = (int)((int64_t)n * ws / (wb + ws));
+  lo = lo < 1 ? 1 : (lo > smax ? smax : lo);
+  const int hi = lo < smax ? lo + 1 : lo;
+  int best = 0;
+  MixTime bt = mix_time(w0, 0, 0, n);
+  const MixTime tl = mix_time(wb, ws, lo, n), th = mix_time(wb, ws, hi, n);
+  if (mix_faster(tl, bt)) { best = lo; bt = tl; }
+  if (mix_faster(th, bt)) { best = hi; bt = th; }
+  return __builtin_amdgcn_readfirstlane(best * kXcds);  // wave-uniform: the schedule stays scalar
+}
+
+// The fp32 partial slots of the small share follow the big share's.
+template <int NB, int BNF_B>
+__device__ __forceinline__ float* mixed_small_partial(const GemmParams& p, int gb) {
+  return p.partial + (size_t)gb * 8 * Frag<256, BNF_B, NB, false>::NACC * 64;
+}
+
+template <int ACT, int NB, int BNF_B, int BNF_S, int BK_S, int STAGES_S, bool GA>
+__global__ __launch_bounds__(512, 1) void k_gemm_mixed(const GemmParams p) {
+  static_assert(2 * Frag<64, BNF_S, NB, false>::NACC <= Frag<256, BNF_B, NB, false>::NACC,
+                "two small-tile partial slots per big-tile slot");
+  constexpr int EL_B = Ring<256, BNF_B, NB, MOE_GEMM_BK, MOE_GEMM_STAGES, false, false>::EL;
+  constexpr int EL_S = Ring<64, BNF_S, NB, BK_S, STAGES_S, true, false>::EL;
+  __shared__ __attribute__((aligned(1024))) bf16 ring[EL_B > EL_S ? EL_B : EL_S];
+  const int G = gridDim.x;
+  const int gs = mixed_small_wgs<NB, BNF_B, BNF_S>(p, G);
+  const int gb = G - gs;
+  const int b = blockIdx.x;  // b % kXcds is the XCD in both shares (gb % kXcds == 0)
+  if (b < gb) {
+    gemm_tiles<256, BNF_B, NB, ACT, MOE_GEMM_BK, MOE_GEMM_STAGES, false, false, GA>(
+        mixed_view<NB, BNF_B, BNF_S>(p, gs > 0 ? 1 : 0), ring, b, gb);
+  } else {
+    GemmParams q = mixed_view<NB, BNF_B, BNF_S>(p, 2);
+    q.partial = mixed_small_partial<NB, BNF_B>(p, gb);
+    gemm_tiles<64, BNF_S, NB, ACT, BK_S, STAGES_S, true, false, GA>(q, ring, b - gb, gs);
+  }
+}
+
+// Fix-up of a mixed launch of G workgroups: the big share's tail pieces, then the small
+// share's stream-K partials (disjoint rows and partial slots).
+template <int ACT, int NB, int BNF_B, int BNF_S, int BK_S>
+__global__ __launch_bounds__(256) void k_gemm_mixed_reduce(const GemmParams p, int G) {
+  const int gs = mixed_small_wgs<NB, BNF_B, BNF_S>(p, G);
+  const int gb = G - gs;
+  tail_reduce<256, BNF_B, NB, ACT, MOE_GEMM_BK, false>(mixed_view<NB, BNF_B, BNF_S>(p, gs > 0 ? 1 : 0), gb / kXcds);
+  GemmParams q = mixed_view<NB, BNF_B, BNF_S>(p, 2);
+  q.partial = mixed_small_partial<NB, BNF_B>(p, gb);
+  streamk_reduce<64, BNF_S, NB, ACT, BK_S, false>(q, gs);
 }
 
 // Compute units of the first device asked (a launch size only: every kernel is correct for
@@ -887,6 +1019,28 @@ hipError_t launch_skinny_dual(const GemmParams& p, int act, int64_t bound, hipSt
   return launch_dual_act<ACT_GELU_TANH>(p, bound, s);
 }
 
+// Mixed-height launch and its fix-up (one launch each).
+template <int ACT, int NB, int BNF_B, int BNF_S, int BK_S, int STAGES_S, bool GA>
+hipError_t launch_mixed_act(const GemmParams& p, int64_t bound, hipStream_t s) {
+  using FR = Frag<256, BNF_B, NB, false>;
+  const int grid = persistent_grid(1 << 30);
+  const int64_t threads = (bound < grid ? bound : grid) * (int64_t)FR::ITEMS;
+  const int64_t wg = (threads + 255) / 256;
+  hipLaunchKernelGGL((k_gemm_mixed<ACT, NB, BNF_B, BNF_S, BK_S, STAGES_S, GA>), dim3(grid), dim3(512), 0, s, p);
+  hipLaunchKernelGGL((k_gemm_mixed_reduce<ACT, NB, BNF_B, BNF_S, BK_S>), dim3((unsigned)(wg < 2048 ? wg : 2048)),
+                     dim3(256), 0, s, p, grid);
+  return hipGetLastError();
+}
+
+// Gated up-projection: 256 x (2 x 128) tiles beside 64 x (2 x 256) tiles (32-deep slices).
+template <bool GA>
+hipError_t launch_mixed_up(const GemmParams& p, int act, int64_t bound, hipStream_t s) {
+  if (act == ACT_SILU) return launch_mixed_act<ACT_SILU, 2, 128, 256, MOE_DUAL_BK, MOE_DUAL_STAGES, GA>(p, bound, s);
+  if (act == ACT_GELU_ERF)
+    return launch_mixed_act<ACT_GELU_ERF, 2, 128, 256, MOE_DUAL_BK, MOE_DUAL_STAGES, GA>(p, bound, s);
+  return launch_mixed_act<ACT_GELU_TANH, 2, 128, 256, MOE_DUAL_BK, MOE_DUAL_STAGES, GA>(p, bound, s);
+}
+
 }  // namespace
 
 bool expert_up_gathers(const FfnArgs& a, bool bf16_io) { return bf16_io && a.s1 == nullptr && !skinny(a); }
@@ -927,6 +1081,11 @@ hipError_t launch_expert_up(const FfnArgs& a, bool bf16_io, hipStream_t s) {
   constexpr int BM = 256, BNF = 128;
   GemmParams p{a.x_perm, a.w1, a.w2, a.h, a.offsets, a.counts, a.E, a.D, a.F, a.F / BNF, a.rows, a.partial, kSplitMax,
                nullptr, nullptr, a.x_row_token};
+  if (a.F % 256 == 0) {
+    const int64_t bound = max_m_tiles(a, BM) * p.n_tiles;
+    if (bound <= 0) return hipSuccess;
+    return a.x_row_token != nullptr ? launch_mixed_up<true>(p, a.act, bound, s) : launch_mixed_up<false>(p, a.act, bound, s);
+  }
   return launch_bf16<BM, BNF, 2>(p, a.act, max_m_tiles(a, BM), s);
 }
 
@@ -961,7 +1120,10 @@ hipError_t launch_expert_down(const FfnArgs& a, bool bf16_io, hipStream_t s) {
   if (a.D % 256 == 0) {
     GemmParams p{a.h, a.w3, nullptr, a.y_perm, a.offsets, a.counts, a.E, a.F, a.D, a.D / 256, a.rows, a.partial,
                  kSplitMax};
-    return launch_bf16<BM, 256, 1>(p, a.act, max_m_tiles(a, BM), s);
+    // 256 x 256 tiles beside 64 x 256 tiles (64-deep slices, four stages)
+    const int64_t bound = max_m_tiles(a, BM) * p.n_tiles;
+    if (bound <= 0) return hipSuccess;
+    return launch_mixed_act<ACT_SILU, 1, 256, 256, 64, 4, false>(p, bound, s);
   }
   GemmParams p{a.h, a.w3, nullptr, a.y_perm, a.offsets, a.counts, a.E, a.F, a.D, a.D / 128, a.rows, a.partial,
                kSplitMax};

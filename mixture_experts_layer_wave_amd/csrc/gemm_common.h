@@ -30,9 +30,17 @@ struct GemmParams {
   const float* S0;  // [E, N] column scales of int8 B0 (weight-only 8-bit experts; else null)
   const float* S1;  // [E, N] column scales of int8 B1
   const int32_t* row_token;  // or null: A row r of the product is row row_token[r] of A
-                             // (persistent tiles only; rows past an expert's count unread)
+                             // (rows past an expert's count unread)
   int dual;         // skinny up-projection launched as k_gemm_skinny_dual (its fix-up checks)
+  // Row filter of a mixed-height launch (0: every expert's rows). An expert's rows split
+  // into whole 256-row blocks plus a remainder; a remainder of 1..rem_max rows is "small".
+  // part 1: the rows without small remainders; part 2: only the small remainders (an
+  // expert's remainder rows start after its whole blocks).
+  int part;
+  int rem_max;
 };
+
+constexpr int kMixBlockRows = 256;  // row block of the mixed-height filter
 
 struct Tile {
   int e, m0, mcount, n0;
@@ -43,7 +51,8 @@ struct Tile {
 // and the row count of expert e.
 struct TileScan {
   int incl;   // inclusive prefix (lanes >= E hold the total)
-  int cnt;    // counts[lane] (0 for lanes >= E)
+  int cnt;    // rows of expert `lane` this launch covers (0 for lanes >= E)
+  int skip;   // rows of expert `lane` before the first covered row
   int total;  // number of tiles
 };
 
@@ -53,6 +62,17 @@ __device__ __forceinline__ TileScan tile_scan(const GemmParams& p) {
   TileScan s;
   s.cnt = lane < p.E ? p.counts[lane] : 0;
   if (s.cnt < 0) s.cnt = 0;
+  s.skip = 0;
+  if (p.part != 0) {
+    const int rem = s.cnt % kMixBlockRows;
+    const bool small = rem > 0 && rem <= p.rem_max;
+    if (p.part == 1) {
+      if (small) s.cnt -= rem;
+    } else {
+      s.skip = small ? s.cnt - rem : 0;
+      s.cnt = small ? rem : 0;
+    }
+  }
   int incl = ((s.cnt + BM - 1) / BM) * p.n_tiles;
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) {
@@ -80,7 +100,7 @@ __device__ __forceinline__ bool tile_of(const GemmParams& p, const TileScan& s, 
   t.m0 = mt * BM;
   t.mcount = min(BM, cnt - t.m0);
   t.n0 = nt * BN;
-  t.row_base = (int64_t)p.offsets[e] + t.m0;
+  t.row_base = (int64_t)p.offsets[e] + __shfl(s.skip, e) + t.m0;
   if (t.row_base < 0 || t.row_base >= p.rows) return false;
   if (t.row_base + t.mcount > p.rows) t.mcount = (int)(p.rows - t.row_base);
   return true;

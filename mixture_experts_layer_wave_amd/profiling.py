@@ -88,6 +88,8 @@ def stage_of(name: str) -> str:
         return "forward"
     if base == "k_gemm_skinny_dual":  # dual-width skinny up-projection
         return "expert_up"
+    if base in ("k_gemm_mixed", "k_gemm_mixed_reduce") and len(args) >= 2:  # <ACT, NB, ...>
+        return "expert_up" if args[1] == 2 else "expert_down"
     if base in ("k_gemm_bf16", "k_gemm_tail_reduce", "k_gemm_streamk_reduce") and len(args) >= 3:
         return "expert_up" if args[2] == 2 else "expert_down"
     if base == "k_gemm_f32":

@@ -300,6 +300,11 @@ FFN_CASES = [
     # bf16: 320 tiles of 64 x (2 x 128) would need stream-K, 160 tiles of 64 x (2 x 256) fill
     # one round whole: the dual-width up-projection takes the wide tiles
     ("bf16", "silu", 256, 5120, 8, [3, 64, 7, 22, 64, 64, 1, 50]),
+    # mixed tile heights (bf16): small remainders (1..64 rows past the last whole 256-row
+    # block, or all of a small expert) on 64-row tiles beside the 256-row tiles of the rest
+    ("bf16", "silu", 256, 512, 8, [300, 17, 520, 64, 65, 256, 0, 700]),
+    ("bf16", "gelu_erf", 512, 768, 4, [1, 257, 600, 40]),
+    ("bf16", "gelu_tanh", 256, 1024, 3, [320, 512, 129]),
     ("f32", "silu", 128, 256, 4, [30, 33, 0, 65]),
     ("f32", "gelu_erf", 256, 128, 3, [64, 1, 100]),
 ]
@@ -593,6 +598,10 @@ MID = [
     # at most 64 rows per expert, all 8 experts active: wide up-projection tiles, and most
     # down-projection tiles cut by stream-K ranges
     configs.scaled_config("mixtral_prefill", N=64, D=256, F=5120, name="skinny_wide_tiles"),
+    # ~275 rows per expert: most experts end in a small remainder past one 256-row block
+    # (mixed tile heights); capacity layout with experts of 1..157 rows
+    configs.scaled_config("mixtral_prefill", N=1100, D=256, F=512, name="mixed_heights"),
+    configs.scaled_config("gshard_capacity", N=1000, D=256, F=512, E=16, name="gshard_mixed"),
 ]
 
 
@@ -614,6 +623,8 @@ def test_layer_mid_size(orc, cfg):
     configs.scaled_config("mixtral_prefill", N=257, D=256, F=256, name="prefill_257"),
     configs.scaled_config("mixtral_prefill", N=64, D=256, F=5120, name="skinny_wide_tiles"),
     configs.scaled_config("mixtral_decode_int8", N=64, D=512, F=5120, name="decode_int8_f5120"),
+    configs.scaled_config("mixtral_prefill", N=1100, D=256, F=512, name="mixed_heights"),
+    configs.scaled_config("gshard_capacity", N=1000, D=256, F=512, E=16, name="gshard_mixed"),
 ], ids=lambda c: c["name"])
 def test_layer_bitwise_reproducible_and_equal_to_steps(orc, cfg):
     inp = inputs.make_inputs(cfg)

@@ -35,6 +35,13 @@ def test_bench_refuses_more_than_one_gpu():
     ("void moe::(anonymous namespace)::k_gemm_skinny_dual<0>(moe::GemmParams)", "k_gemm_skinny_dual", [0],
      "expert_up"),
     ("k_gemm_streamk_reduce<64, 128, 2, 0, 64, false>", "k_gemm_streamk_reduce", [64, 128, 2, 0, 64, 0], "expert_up"),
+    # mixed-height launches: <ACT, NB, BNF_B, BNF_S, BK_S, STAGES_S, GA> and their fix-up
+    ("void moe::(anonymous namespace)::k_gemm_mixed<0, 2, 128, 256, 32, 4, true>(moe::GemmParams)", "k_gemm_mixed",
+     [0, 2, 128, 256, 32, 4, 1], "expert_up"),
+    ("void moe::(anonymous namespace)::k_gemm_mixed<0, 1, 256, 256, 64, 4, false>(moe::GemmParams)", "k_gemm_mixed",
+     [0, 1, 256, 256, 64, 4, 0], "expert_down"),
+    ("_ZN3moe12_GLOBAL__N_119k_gemm_mixed_reduceILi0ELi1ELi256ELi256ELi64EEEvNS_10GemmParamsEi",
+     "k_gemm_mixed_reduce", [0, 1, 256, 256, 64], "expert_down"),
     ("void moe::(anonymous namespace)::k_router_epi<8>(moe::RouterArgs, moe::RouterSplit)", "k_router_epi", [8],
      "route"),
     ("k_route_dispatch_small<8>", "k_route_dispatch_small", [8], "forward"),
