@@ -1081,7 +1081,7 @@ hipError_t launch_expert_up(const FfnArgs& a, bool bf16_io, hipStream_t s) {
   constexpr int BM = 256, BNF = 128;
   GemmParams p{a.x_perm, a.w1, a.w2, a.h, a.offsets, a.counts, a.E, a.D, a.F, a.F / BNF, a.rows, a.partial, kSplitMax,
                nullptr, nullptr, a.x_row_token};
-  if (a.F % 256 == 0) {
+  if (a.F % 256 == 0 && a.partial != nullptr) {  // the small share's stream-K keeps partials
     const int64_t bound = max_m_tiles(a, BM) * p.n_tiles;
     if (bound <= 0) return hipSuccess;
     return a.x_row_token != nullptr ? launch_mixed_up<true>(p, a.act, bound, s) : launch_mixed_up<false>(p, a.act, bound, s);
@@ -1120,6 +1120,7 @@ hipError_t launch_expert_down(const FfnArgs& a, bool bf16_io, hipStream_t s) {
   if (a.D % 256 == 0) {
     GemmParams p{a.h, a.w3, nullptr, a.y_perm, a.offsets, a.counts, a.E, a.F, a.D, a.D / 256, a.rows, a.partial,
                  kSplitMax};
+    if (a.partial == nullptr) return launch_bf16<BM, 256, 1>(p, a.act, max_m_tiles(a, BM), s);
     // 256 x 256 tiles beside 64 x 256 tiles (64-deep slices, four stages)
     const int64_t bound = max_m_tiles(a, BM) * p.n_tiles;
     if (bound <= 0) return hipSuccess;
