@@ -239,16 +239,20 @@ def measure_layer(B, cfg, inp, args, dev, cold_reps: int, graph: bool) -> dict:
         layer.forward()
         step(up=up)
     # Timed: exactly K passes of the layer, one moe_forward call each, between two device
-    # synchronisations; an event pair around each call gives its spread.
-    fev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    # synchronisations (nothing else enqueued in between).
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    for i in range(args.steps):
+        layer.forward()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    # The spread of one call: K more calls, each between an event pair.
+    fev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
     for i in range(args.steps):
         fev[i][0].record(stream)
         layer.forward()
         fev[i][1].record(stream)
     torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
     fwd_t = np.array([a.elapsed_time(b) for a, b in fev])
     forward_ms = {"mean": float(np.mean(fwd_t)), "p10": float(np.percentile(fwd_t, 10)),
                   "median": float(np.median(fwd_t)), "p90": float(np.percentile(fwd_t, 90))}

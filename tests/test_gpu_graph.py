@@ -19,6 +19,8 @@ pytestmark = pytest.mark.gpu
     configs.scaled_config("mixtral_prefill", N=700, D=256, F=512),
     configs.scaled_config("gshard_capacity", N=900, D=256, F=384, E=16),
     configs.scaled_config("mixtral_decode_int8", N=64, D=512, F=384),
+    # mixed tile heights with both shares (small remainders on 64-row tiles)
+    configs.scaled_config("mixtral_prefill", N=1100, D=256, F=512, name="mixed_heights"),
 ], ids=lambda c: c["name"])
 def test_forward_graph_replays_equal_eager(cfg):
     inp = inputs.make_inputs(cfg)
