@@ -285,6 +285,29 @@ __device__ __forceinline__ void fixup_item(const GemmParams& p, const Tile& tl, 
   *reinterpret_cast<bf16x4*>(C) = epilogue4<NB, ACT, Q8>(p, tl, col, acc[0], acc[NB - 1]);
 }
 
+// Whether a launch leaves partials for its fix-up kernel: a persistent launch of gd
+// workgroups when some XCD share splits its tail round along K, a stream-K launch when its
+// ranges cut tiles at all (conservative: W > 0). Wave-wide (tile_scan).
+template <int BM, int BK>
+__device__ __forceinline__ bool persistent_splits(const GemmParams& p, int gd) {
+  const int nslot = gd / kXcds;
+  if (p.partial == nullptr || nslot <= 0) return false;
+  const TileScan ts = tile_scan<BM>(p);
+  bool any = false;
+  for (int x = 0; x < kXcds; ++x) any = any || xcd_share(ts.total, x, kXcds, nslot, p.K / BK, p).S > 1;
+  return any;
+}
+template <int BM, int BK>
+__device__ __forceinline__ bool streamk_partials(const GemmParams& p, int gd) {
+  return gd > 0 && sk_plan(tile_scan<BM>(p).total, gd, p.K / BK).W > 0;
+}
+// Run by wave 0 of workgroup 0 once its tiles are done: the fix-up word for this launch.
+__device__ __forceinline__ void set_fixup(const GemmParams& p, bool need) {
+  if (p.fixup != nullptr && lane_id() == 0) *p.fixup = need ? 1u : 0u;
+}
+// A fix-up kernel's first step: nothing to do when the GEMM launch left no partials.
+__device__ __forceinline__ bool fixup_idle(const GemmParams& p) { return p.fixup != nullptr && *p.fixup == 0u; }
+
 // STREAMK = false: persistent full tiles per XCD share, tail round split along K.
 // STREAMK = true : stream-K; the (tile, K slice) list is cut into equal contiguous ranges,
 //                  one per workgroup; a tile cut by a range boundary leaves fp32 partials
@@ -677,6 +700,10 @@ template <int BM, int BNF, int NB, int ACT, int BK, int STAGES, bool STREAMK, bo
 __global__ __launch_bounds__(512, 1) void k_gemm_bf16(const GemmParams p) {
   __shared__ __attribute__((aligned(1024))) bf16 ring[Ring<BM, BNF, NB, BK, STAGES, STREAMK, Q8>::EL];
   gemm_tiles<BM, BNF, NB, ACT, BK, STAGES, STREAMK, Q8, GA>(p, ring, blockIdx.x, gridDim.x);
+  if (blockIdx.x == 0 && threadIdx.x < 64) {
+    if constexpr (STREAMK) set_fixup(p, streamk_partials<BM, BK>(p, gridDim.x));
+    else set_fixup(p, persistent_splits<BM, BK>(p, gridDim.x));
+  }
 }
 
 // Skinny gated up-projection (every expert at most 64 rows) with two tile widths in one
@@ -704,13 +731,15 @@ __global__ __launch_bounds__(512, 1) void k_gemm_skinny_dual(const GemmParams p)
   constexpr int EL_N = Ring<64, 128, 2, 64, 4, true, false>::EL;
   constexpr int EL_W = Ring<64, 256, 2, MOE_DUAL_BK, MOE_DUAL_STAGES, true, false>::EL;
   __shared__ __attribute__((aligned(1024))) bf16 ring[EL_N > EL_W ? EL_N : EL_W];
-  if (skinny_wide(p, gridDim.x)) {
+  const bool wide = skinny_wide(p, gridDim.x);
+  if (wide) {
     GemmParams q = p;
     q.n_tiles = p.N / 256;
     gemm_tiles<64, 256, 2, ACT, MOE_DUAL_BK, MOE_DUAL_STAGES, true, false>(q, ring, blockIdx.x, gridDim.x);
   } else {
     gemm_tiles<64, 128, 2, ACT, 64, 4, true, false>(p, ring, blockIdx.x, gridDim.x);
   }
+  if (blockIdx.x == 0 && threadIdx.x < 64) set_fixup(p, !wide && streamk_partials<64, 64>(p, gridDim.x));
 }
 
 // Fix-up of the tail split: sums the K pieces of every split tail tile in piece order and
@@ -754,6 +783,7 @@ __device__ __forceinline__ void tail_reduce(const GemmParams& p, const int nslot
 }
 template <int BM, int BNF, int NB, int ACT, int BK, bool Q8>
 __global__ __launch_bounds__(256) void k_gemm_tail_reduce(const GemmParams p, int nslot) {
+  if (fixup_idle(p)) return;
   tail_reduce<BM, BNF, NB, ACT, BK, Q8>(p, nslot);
 }
 
@@ -789,6 +819,7 @@ __device__ __forceinline__ void streamk_reduce(const GemmParams& p, const int gr
 }
 template <int BM, int BNF, int NB, int ACT, int BK, bool Q8>
 __global__ __launch_bounds__(256) void k_gemm_streamk_reduce(const GemmParams p, int grid) {
+  if (fixup_idle(p)) return;
   if (p.dual && skinny_wide(p, grid)) return;  // the dual skinny kernel ran whole wide tiles
   streamk_reduce<BM, BNF, NB, ACT, BK, Q8>(p, grid);
 }
@@ -900,12 +931,17 @@ __global__ __launch_bounds__(512, 1) void k_gemm_mixed(const GemmParams p) {
     q.partial = mixed_small_partial<NB, BNF_B>(p, gb);
     gemm_tiles<64, BNF_S, NB, ACT, BK_S, STAGES_S, true, false, GA>(q, ring, b - gb, gs);
   }
+  if (b == 0 && threadIdx.x < 64) {
+    const bool big = gb > 0 && persistent_splits<256, MOE_GEMM_BK>(mixed_view<NB, BNF_B, BNF_S>(p, gs > 0 ? 1 : 0), gb);
+    set_fixup(p, big || streamk_partials<64, BK_S>(mixed_view<NB, BNF_B, BNF_S>(p, 2), gs));
+  }
 }
 
 // Fix-up of a mixed launch of G workgroups: the big share's tail pieces, then the small
 // share's stream-K partials (disjoint rows and partial slots).
 template <int ACT, int NB, int BNF_B, int BNF_S, int BK_S>
 __global__ __launch_bounds__(256) void k_gemm_mixed_reduce(const GemmParams p, int G) {
+  if (fixup_idle(p)) return;
   const int gs = mixed_small_wgs<NB, BNF_B, BNF_S>(p, G);
   const int gb = G - gs;
   tail_reduce<256, BNF_B, NB, ACT, MOE_GEMM_BK, false>(mixed_view<NB, BNF_B, BNF_S>(p, gs > 0 ? 1 : 0), gb / kXcds);
@@ -935,8 +971,18 @@ int persistent_grid(int64_t tiles_bound) {
   return (int)g;
 }
 
+// The fix-up word behind the partial tiles (null without a partial buffer).
+GemmParams with_fixup(const GemmParams& p) {
+  GemmParams q = p;
+  q.fixup = p.partial != nullptr
+                ? reinterpret_cast<uint32_t*>(reinterpret_cast<char*>(p.partial) + kGemmPartialBytes)
+                : nullptr;
+  return q;
+}
+
 template <int BM, int BNF, int NB, int ACT, int BK, int STAGES, bool STREAMK, bool Q8>
-hipError_t launch_act(const GemmParams& p, int64_t bound, hipStream_t s) {
+hipError_t launch_act(const GemmParams& p0, int64_t bound, hipStream_t s) {
+  const GemmParams p = with_fixup(p0);
   // fp32 partial tiles: 8 waves x NACC accumulators x 64 lanes per slot; stream-K uses two
   // slots per workgroup, the tail split one.
   using FR = Frag<BM, BNF, NB, Q8>;
@@ -1002,7 +1048,8 @@ bool skinny(const FfnArgs& a) { return a.partial != nullptr && a.max_rows_per_ex
 
 // The dual-width skinny up-projection and its stream-K fix-up (narrow tiles only).
 template <int ACT>
-hipError_t launch_dual_act(const GemmParams& p, int64_t bound, hipStream_t s) {
+hipError_t launch_dual_act(const GemmParams& p0, int64_t bound, hipStream_t s) {
+  const GemmParams p = with_fixup(p0);
   using FR = Frag<64, 128, 2, false>;
   const int grid = persistent_grid(1 << 30);
   const int64_t threads = (bound < grid ? bound : grid) * (int64_t)FR::ITEMS;
@@ -1021,7 +1068,8 @@ hipError_t launch_skinny_dual(const GemmParams& p, int act, int64_t bound, hipSt
 
 // Mixed-height launch and its fix-up (one launch each).
 template <int ACT, int NB, int BNF_B, int BNF_S, int BK_S, int STAGES_S, bool GA>
-hipError_t launch_mixed_act(const GemmParams& p, int64_t bound, hipStream_t s) {
+hipError_t launch_mixed_act(const GemmParams& p0, int64_t bound, hipStream_t s) {
+  const GemmParams p = with_fixup(p0);
   using FR = Frag<256, BNF_B, NB, false>;
   const int grid = persistent_grid(1 << 30);
   const int64_t threads = (bound < grid ? bound : grid) * (int64_t)FR::ITEMS;

@@ -38,6 +38,9 @@ struct GemmParams {
   // expert's remainder rows start after its whole blocks).
   int part;
   int rem_max;
+  // Word the GEMM kernel sets to 1 if its launch left split-K or stream-K partials for the
+  // fix-up kernel, else 0 (the fix-up then returns at once); null: always fix up.
+  uint32_t* fixup;
 };
 
 constexpr int kMixBlockRows = 256;  // row block of the mixed-height filter

@@ -20,6 +20,8 @@ constexpr uint32_t kPsumMagic = 0x5053554du;  // marks valid router partial sums
 // 8 waves x 128 fp32 accumulators x 64 lanes.
 constexpr size_t kGemmPartialUnits = 256;
 constexpr size_t kGemmPartialBytes = kGemmPartialUnits * 8 * 128 * 64 * sizeof(float);
+// After the partial tiles: the word that tells the fix-up kernel whether partials exist.
+constexpr size_t kGemmFixupBytes = 256;
 
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
@@ -70,7 +72,7 @@ inline ScratchLayout scratch_layout(int64_t N, int64_t D, int E, int k, bool bf1
   s.base = o; o = align_up(o + sizeof(int32_t) * (size_t)k * s.nblk_d * E, 256);
   s.tokdrop = o; o = align_up(o + sizeof(int32_t) * (size_t)s.nblk_d, 256);
   s.load = o; o = align_up(o + sizeof(int32_t) * (size_t)E, 256);
-  s.partial = o; o = align_up(o + (bf16 ? kGemmPartialBytes : 0), 256);
+  s.partial = o; o = align_up(o + (bf16 ? kGemmPartialBytes + kGemmFixupBytes : 0), 256);
   s.rpart = o; o = align_up(o + (bf16 ? sizeof(float) * (size_t)router_split(N, D).S * N * E : 0), 256);
   s.total = o;
   return s;
@@ -166,7 +168,8 @@ struct FfnArgs {
   int64_t rows;             // rows of the expert buffers
   int64_t max_rows_per_expert;  // host bound on counts[e] (N, or C when padded)
   int D, F, E, act;
-  float* partial;           // scratch for split-K partial tiles (kGemmPartialBytes)
+  float* partial;           // scratch for split-K partial tiles (kGemmPartialBytes), then
+                            // the fix-up word (kGemmFixupBytes)
   const int32_t* x_row_token;  // or null: x_perm is then x [N,D] and expert-buffer row r of
                                // the up-projection is x row x_row_token[r] (gathered rows)
 };
