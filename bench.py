@@ -49,6 +49,8 @@ def gemm_kernel_of(cfg, stage: str, gathered: bool, capacity) -> str:
             return f"k_gemm_skinny_dual ({what}, 64-row tiles of two widths)"
         return f"k_gemm_bf16 ({what}, 64-row stream-K tiles)"
     if cfg.get("weight_dtype", "same") == "int8":
+        if stage == "expert_up" and width % 256 == 0:
+            return f"k_gemm_mixed ({what}, int8 weights, 256-row tiles, small remainders on 64-row tiles)"
         return f"k_gemm_bf16 ({what}, int8 weights)"
     if width % 256 == 0:
         rows = "rows gathered from x, " if gathered else ""

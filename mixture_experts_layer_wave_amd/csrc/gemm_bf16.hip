@@ -301,7 +301,8 @@ template <int BM, int BK>
 __device__ __forceinline__ bool streamk_partials(const GemmParams& p, int gd) {
   return gd > 0 && sk_plan(tile_scan<BM>(p).total, gd, p.K / BK).W > 0;
 }
-// Run by wave 0 of workgroup 0 once its tiles are done: the fix-up word for this launch.
+// Run by wave 0 of workgroup 0 at the start of a launch: the fix-up word for this launch
+// (the previous launch's fix-up has finished: same stream).
 __device__ __forceinline__ void set_fixup(const GemmParams& p, bool need) {
   if (p.fixup != nullptr && lane_id() == 0) *p.fixup = need ? 1u : 0u;
 }
@@ -699,11 +700,11 @@ __device__ __forceinline__ void gemm_tiles(const GemmParams& p, bf16* ring, cons
 template <int BM, int BNF, int NB, int ACT, int BK, int STAGES, bool STREAMK, bool Q8, bool GA = false>
 __global__ __launch_bounds__(512, 1) void k_gemm_bf16(const GemmParams p) {
   __shared__ __attribute__((aligned(1024))) bf16 ring[Ring<BM, BNF, NB, BK, STAGES, STREAMK, Q8>::EL];
-  gemm_tiles<BM, BNF, NB, ACT, BK, STAGES, STREAMK, Q8, GA>(p, ring, blockIdx.x, gridDim.x);
-  if (blockIdx.x == 0 && threadIdx.x < 64) {
+  if (blockIdx.x == 0 && threadIdx.x < 64) {  // before the tiles, so none of it stays live across them
     if constexpr (STREAMK) set_fixup(p, streamk_partials<BM, BK>(p, gridDim.x));
     else set_fixup(p, persistent_splits<BM, BK>(p, gridDim.x));
   }
+  gemm_tiles<BM, BNF, NB, ACT, BK, STAGES, STREAMK, Q8, GA>(p, ring, blockIdx.x, gridDim.x);
 }
 
 // Skinny gated up-projection (every expert at most 64 rows) with two tile widths in one
@@ -732,6 +733,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm_skinny_dual(const GemmParams p)
   constexpr int EL_W = Ring<64, 256, 2, MOE_DUAL_BK, MOE_DUAL_STAGES, true, false>::EL;
   __shared__ __attribute__((aligned(1024))) bf16 ring[EL_N > EL_W ? EL_N : EL_W];
   const bool wide = skinny_wide(p, gridDim.x);
+  if (blockIdx.x == 0 && threadIdx.x < 64) set_fixup(p, !wide && streamk_partials<64, 64>(p, gridDim.x));
   if (wide) {
     GemmParams q = p;
     q.n_tiles = p.N / 256;
@@ -739,7 +741,6 @@ __global__ __launch_bounds__(512, 1) void k_gemm_skinny_dual(const GemmParams p)
   } else {
     gemm_tiles<64, 128, 2, ACT, 64, 4, true, false>(p, ring, blockIdx.x, gridDim.x);
   }
-  if (blockIdx.x == 0 && threadIdx.x < 64) set_fixup(p, !wide && streamk_partials<64, 64>(p, gridDim.x));
 }
 
 // Fix-up of the tail split: sums the K pieces of every split tail tile in piece order and
@@ -851,6 +852,10 @@ constexpr int kMixRemMax = 64;
 
 // The tile list of one share: part 0 (every row on 256-row tiles), 1 (big share) or 2
 // (small share).
+// Tile shapes of a mixed launch (template arguments of the functions below): the big
+// share's 256 x (NB x BNF_B) tiles with BK_B-deep slices in STAGES_B stages, the small
+// share's 64 x (NB x BNF_S) tiles with BK_S-deep slices in STAGES_S stages; Q8: int8
+// weights with column scales.
 template <int NB, int BNF_B, int BNF_S>
 __device__ __forceinline__ GemmParams mixed_view(const GemmParams& p, int part) {
   GemmParams q = p;
@@ -875,9 +880,11 @@ __device__ __forceinline__ MixTime mix_time(int64_t wb, int64_t ws, int s, int n
 
 // Workgroups of the small share (a multiple of kXcds, 0 for none) out of G: the better of
 // no split and the two whole slot counts around the balance point
-// s* = n ws / (wb + ws), where both shares' work per slot is equal.
-template <int NB, int BNF_B, int BNF_S>
+// s* = n ws / (wb + ws), where both shares' work per slot is equal. A tile's work is the
+// bytes it copies into LDS per row of a K slice (bf16 activation rows, weights of WB bytes).
+template <int NB, int BNF_B, int BNF_S, bool Q8>
 __device__ __forceinline__ int mixed_small_wgs(const GemmParams& p, int G) {
+  constexpr int WB = Q8 ? 1 : 2;
   // weighted small tiles: one 64-row tile row per expert with a small remainder (lane e =
   // expert e, E <= 64), summed over the wave in a fixed butterfly order
   const int lane = lane_id();
@@ -891,9 +898,9 @@ __device__ __forceinline__ int mixed_small_wgs(const GemmParams& p, int G) {
   if (wsl == 0 || n < 2) return 0;
   const int t0 = tile_scan<256>(mixed_view<NB, BNF_B, BNF_S>(p, 0)).total;
   const int tb = tile_scan<256>(mixed_view<NB, BNF_B, BNF_S>(p, 1)).total;
-  const int64_t cb = (256 + NB * BNF_B) * 100;
+  const int64_t cb = (int64_t)(256 * 2 + NB * BNF_B * WB) * 100;
   const int64_t wb = (int64_t)tb * cb, w0 = (int64_t)t0 * cb;
-  const int64_t ws = wsl * (p.N / BNF_S) * (64 + NB * BNF_S);
+  const int64_t ws = wsl * (p.N / BNF_S) * (64 * 2 + NB * BNF_S * WB);
   const int smax = tb > 0 ? n - 1 : n;
   int lo = (int)((int64_t)n * ws / (wb + ws));
   lo = lo < 1 ? 1 : (lo > smax ? smax : lo);
@@ -907,47 +914,47 @@ __device__ __forceinline__ int mixed_small_wgs(const GemmParams& p, int G) {
 }
 
 // The fp32 partial slots of the small share follow the big share's.
-template <int NB, int BNF_B>
+template <int NB, int BNF_B, bool Q8>
 __device__ __forceinline__ float* mixed_small_partial(const GemmParams& p, int gb) {
-  return p.partial + (size_t)gb * 8 * Frag<256, BNF_B, NB, false>::NACC * 64;
+  return p.partial + (size_t)gb * 8 * Frag<256, BNF_B, NB, Q8>::NACC * 64;
 }
 
-template <int ACT, int NB, int BNF_B, int BNF_S, int BK_S, int STAGES_S, bool GA>
+template <int ACT, int NB, int BNF_B, int BK_B, int STAGES_B, int BNF_S, int BK_S, int STAGES_S, bool Q8, bool GA>
 __global__ __launch_bounds__(512, 1) void k_gemm_mixed(const GemmParams p) {
-  static_assert(2 * Frag<64, BNF_S, NB, false>::NACC <= Frag<256, BNF_B, NB, false>::NACC,
+  static_assert(2 * Frag<64, BNF_S, NB, Q8>::NACC <= Frag<256, BNF_B, NB, Q8>::NACC,
                 "two small-tile partial slots per big-tile slot");
-  constexpr int EL_B = Ring<256, BNF_B, NB, MOE_GEMM_BK, MOE_GEMM_STAGES, false, false>::EL;
-  constexpr int EL_S = Ring<64, BNF_S, NB, BK_S, STAGES_S, true, false>::EL;
+  constexpr int EL_B = Ring<256, BNF_B, NB, BK_B, STAGES_B, false, Q8>::EL;
+  constexpr int EL_S = Ring<64, BNF_S, NB, BK_S, STAGES_S, true, Q8>::EL;
   __shared__ __attribute__((aligned(1024))) bf16 ring[EL_B > EL_S ? EL_B : EL_S];
   const int G = gridDim.x;
-  const int gs = mixed_small_wgs<NB, BNF_B, BNF_S>(p, G);
+  const int gs = mixed_small_wgs<NB, BNF_B, BNF_S, Q8>(p, G);
   const int gb = G - gs;
   const int b = blockIdx.x;  // b % kXcds is the XCD in both shares (gb % kXcds == 0)
+  if (b == 0 && threadIdx.x < 64) {  // before the tiles, so none of it stays live across them
+    const bool big = gb > 0 && persistent_splits<256, BK_B>(mixed_view<NB, BNF_B, BNF_S>(p, gs > 0 ? 1 : 0), gb);
+    set_fixup(p, big || streamk_partials<64, BK_S>(mixed_view<NB, BNF_B, BNF_S>(p, 2), gs));
+  }
   if (b < gb) {
-    gemm_tiles<256, BNF_B, NB, ACT, MOE_GEMM_BK, MOE_GEMM_STAGES, false, false, GA>(
-        mixed_view<NB, BNF_B, BNF_S>(p, gs > 0 ? 1 : 0), ring, b, gb);
+    gemm_tiles<256, BNF_B, NB, ACT, BK_B, STAGES_B, false, Q8, GA>(mixed_view<NB, BNF_B, BNF_S>(p, gs > 0 ? 1 : 0),
+                                                                   ring, b, gb);
   } else {
     GemmParams q = mixed_view<NB, BNF_B, BNF_S>(p, 2);
-    q.partial = mixed_small_partial<NB, BNF_B>(p, gb);
-    gemm_tiles<64, BNF_S, NB, ACT, BK_S, STAGES_S, true, false, GA>(q, ring, b - gb, gs);
-  }
-  if (b == 0 && threadIdx.x < 64) {
-    const bool big = gb > 0 && persistent_splits<256, MOE_GEMM_BK>(mixed_view<NB, BNF_B, BNF_S>(p, gs > 0 ? 1 : 0), gb);
-    set_fixup(p, big || streamk_partials<64, BK_S>(mixed_view<NB, BNF_B, BNF_S>(p, 2), gs));
+    q.partial = mixed_small_partial<NB, BNF_B, Q8>(p, gb);
+    gemm_tiles<64, BNF_S, NB, ACT, BK_S, STAGES_S, true, Q8, GA>(q, ring, b - gb, gs);
   }
 }
 
 // Fix-up of a mixed launch of G workgroups: the big share's tail pieces, then the small
 // share's stream-K partials (disjoint rows and partial slots).
-template <int ACT, int NB, int BNF_B, int BNF_S, int BK_S>
+template <int ACT, int NB, int BNF_B, int BK_B, int BNF_S, int BK_S, bool Q8>
 __global__ __launch_bounds__(256) void k_gemm_mixed_reduce(const GemmParams p, int G) {
   if (fixup_idle(p)) return;
-  const int gs = mixed_small_wgs<NB, BNF_B, BNF_S>(p, G);
+  const int gs = mixed_small_wgs<NB, BNF_B, BNF_S, Q8>(p, G);
   const int gb = G - gs;
-  tail_reduce<256, BNF_B, NB, ACT, MOE_GEMM_BK, false>(mixed_view<NB, BNF_B, BNF_S>(p, gs > 0 ? 1 : 0), gb / kXcds);
+  tail_reduce<256, BNF_B, NB, ACT, BK_B, Q8>(mixed_view<NB, BNF_B, BNF_S>(p, gs > 0 ? 1 : 0), gb / kXcds);
   GemmParams q = mixed_view<NB, BNF_B, BNF_S>(p, 2);
-  q.partial = mixed_small_partial<NB, BNF_B>(p, gb);
-  streamk_reduce<64, BNF_S, NB, ACT, BK_S, false>(q, gs);
+  q.partial = mixed_small_partial<NB, BNF_B, Q8>(p, gb);
+  streamk_reduce<64, BNF_S, NB, ACT, BK_S, Q8>(q, gs);
 }
 
 // Compute units of the first device asked (a launch size only: every kernel is correct for
@@ -1067,26 +1074,44 @@ hipError_t launch_skinny_dual(const GemmParams& p, int act, int64_t bound, hipSt
 }
 
 // Mixed-height launch and its fix-up (one launch each).
-template <int ACT, int NB, int BNF_B, int BNF_S, int BK_S, int STAGES_S, bool GA>
+template <int ACT, int NB, int BNF_B, int BK_B, int STAGES_B, int BNF_S, int BK_S, int STAGES_S, bool Q8, bool GA>
 hipError_t launch_mixed_act(const GemmParams& p0, int64_t bound, hipStream_t s) {
   const GemmParams p = with_fixup(p0);
-  using FR = Frag<256, BNF_B, NB, false>;
+  using FR = Frag<256, BNF_B, NB, Q8>;
   const int grid = persistent_grid(1 << 30);
   const int64_t threads = (bound < grid ? bound : grid) * (int64_t)FR::ITEMS;
   const int64_t wg = (threads + 255) / 256;
-  hipLaunchKernelGGL((k_gemm_mixed<ACT, NB, BNF_B, BNF_S, BK_S, STAGES_S, GA>), dim3(grid), dim3(512), 0, s, p);
-  hipLaunchKernelGGL((k_gemm_mixed_reduce<ACT, NB, BNF_B, BNF_S, BK_S>), dim3((unsigned)(wg < 2048 ? wg : 2048)),
+  hipLaunchKernelGGL((k_gemm_mixed<ACT, NB, BNF_B, BK_B, STAGES_B, BNF_S, BK_S, STAGES_S, Q8, GA>), dim3(grid),
+                     dim3(512), 0, s, p);
+  hipLaunchKernelGGL((k_gemm_mixed_reduce<ACT, NB, BNF_B, BK_B, BNF_S, BK_S, Q8>), dim3((unsigned)(wg < 2048 ? wg : 2048)),
                      dim3(256), 0, s, p, grid);
   return hipGetLastError();
 }
 
-// Gated up-projection: 256 x (2 x 128) tiles beside 64 x (2 x 256) tiles (32-deep slices).
-template <bool GA>
+// Gated up-projection, bf16 weights: 256 x (2 x 128) tiles (the split ring) beside
+// 64 x (2 x 256) tiles (32-deep slices).
+template <int ACT, bool GA>
+hipError_t launch_mixed_up_bf16(const GemmParams& p, int64_t bound, hipStream_t s) {
+  return launch_mixed_act<ACT, 2, 128, MOE_GEMM_BK, MOE_GEMM_STAGES, 256, MOE_DUAL_BK, MOE_DUAL_STAGES, false, GA>(
+      p, bound, s);
+}
+// int8 weights: 256 x (2 x 128) tiles (three stages) beside 64 x (2 x 256) tiles, as their
+// launches without the small share.
+template <int ACT>
+hipError_t launch_mixed_up_q8(const GemmParams& p, int64_t bound, hipStream_t s) {
+  return launch_mixed_act<ACT, 2, 128, 64, 3, 256, 64, 4, true, false>(p, bound, s);
+}
+template <bool GA, bool Q8>
 hipError_t launch_mixed_up(const GemmParams& p, int act, int64_t bound, hipStream_t s) {
-  if (act == ACT_SILU) return launch_mixed_act<ACT_SILU, 2, 128, 256, MOE_DUAL_BK, MOE_DUAL_STAGES, GA>(p, bound, s);
-  if (act == ACT_GELU_ERF)
-    return launch_mixed_act<ACT_GELU_ERF, 2, 128, 256, MOE_DUAL_BK, MOE_DUAL_STAGES, GA>(p, bound, s);
-  return launch_mixed_act<ACT_GELU_TANH, 2, 128, 256, MOE_DUAL_BK, MOE_DUAL_STAGES, GA>(p, bound, s);
+  if constexpr (Q8) {
+    if (act == ACT_SILU) return launch_mixed_up_q8<ACT_SILU>(p, bound, s);
+    if (act == ACT_GELU_ERF) return launch_mixed_up_q8<ACT_GELU_ERF>(p, bound, s);
+    return launch_mixed_up_q8<ACT_GELU_TANH>(p, bound, s);
+  } else {
+    if (act == ACT_SILU) return launch_mixed_up_bf16<ACT_SILU, GA>(p, bound, s);
+    if (act == ACT_GELU_ERF) return launch_mixed_up_bf16<ACT_GELU_ERF, GA>(p, bound, s);
+    return launch_mixed_up_bf16<ACT_GELU_TANH, GA>(p, bound, s);
+  }
 }
 
 }  // namespace
@@ -1110,6 +1135,11 @@ hipError_t launch_expert_up(const FfnArgs& a, bool bf16_io, hipStream_t s) {
       }
       return launch_bf16<kSkinnyRows, 128, 2, 64, 6, true, true>(p, a.act, max_m_tiles(a, kSkinnyRows), s);
     }
+    if (a.F % 256 == 0 && a.partial != nullptr) {  // 64-row tiles for small remainders
+      const int64_t bound = max_m_tiles(a, 256) * p.n_tiles;
+      if (bound <= 0) return hipSuccess;
+      return launch_mixed_up<false, true>(p, a.act, bound, s);
+    }
     return launch_bf16<256, 128, 2, 64, 3, false, true>(p, a.act, max_m_tiles(a, 256), s);
   }
   if (skinny(a) && a.F % 256 == 0) {
@@ -1132,7 +1162,8 @@ hipError_t launch_expert_up(const FfnArgs& a, bool bf16_io, hipStream_t s) {
   if (a.F % 256 == 0 && a.partial != nullptr) {  // the small share's stream-K keeps partials
     const int64_t bound = max_m_tiles(a, BM) * p.n_tiles;
     if (bound <= 0) return hipSuccess;
-    return a.x_row_token != nullptr ? launch_mixed_up<true>(p, a.act, bound, s) : launch_mixed_up<false>(p, a.act, bound, s);
+    return a.x_row_token != nullptr ? launch_mixed_up<true, false>(p, a.act, bound, s)
+                                    : launch_mixed_up<false, false>(p, a.act, bound, s);
   }
   return launch_bf16<BM, BNF, 2>(p, a.act, max_m_tiles(a, BM), s);
 }
@@ -1162,6 +1193,8 @@ hipError_t launch_expert_down(const FfnArgs& a, bool bf16_io, hipStream_t s) {
   if (a.s3 != nullptr) {
     GemmParams p{a.h, a.w3, nullptr, a.y_perm, a.offsets, a.counts, a.E, a.F, a.D, a.D / 128, a.rows, a.partial,
                  kSplitMax, a.s3, nullptr};
+    // (no small share: its int8 64 x 256 tiles copy 24 KB per K slice, too little to keep
+    // pace; measured 1.6 against 1.15 ms on the int8 prefill)
     return launch_bf16<256, 128, 1, 64, 4, false, true>(p, a.act, max_m_tiles(a, 256), s);
   }
   constexpr int BM = 256;
@@ -1172,7 +1205,7 @@ hipError_t launch_expert_down(const FfnArgs& a, bool bf16_io, hipStream_t s) {
     // 256 x 256 tiles beside 64 x 256 tiles (64-deep slices, four stages)
     const int64_t bound = max_m_tiles(a, BM) * p.n_tiles;
     if (bound <= 0) return hipSuccess;
-    return launch_mixed_act<ACT_SILU, 1, 256, 256, 64, 4, false>(p, bound, s);
+    return launch_mixed_act<ACT_SILU, 1, 256, MOE_GEMM_BK, MOE_GEMM_STAGES, 256, 64, 4, false, false>(p, bound, s);
   }
   GemmParams p{a.h, a.w3, nullptr, a.y_perm, a.offsets, a.counts, a.E, a.F, a.D, a.D / 128, a.rows, a.partial,
                kSplitMax};
