@@ -800,3 +800,37 @@ def test_mixtral_shape_eight_times_the_batch(orc):
     # 0.5-1.9 GB): schedule, row offsets and scratch at the largest batch tested here.
     cfg = configs.scaled_config("mixtral_prefill", N=32768, D=4096, F=14336, name="mixtral_prefill_n32768")
     _check_layer(orc, cfg, sample=_spread(cfg["N"], 10, extra=(1, 32767)))
+
+
+# ---------------------------------------------------------------------------------------
+# Seeded random layers: routing recipe, sizes, expert counts and capacity drawn at random
+# (the grouped GEMMs then meet many remainder patterns and splits of the mixed-height
+# launch); each checked end to end as above
+# ---------------------------------------------------------------------------------------
+
+def _random_layers(n, seed=20261204, budget=1.2e8):
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        base = ["mixtral_prefill", "grok1_layer", "gshard_capacity", "switch_top1"][i % 4]
+        E = int(rng.choice([2, 4, 8, 16, 32, 64]))
+        k = int(rng.integers(1, min(E, 4) + 1))
+        if base == "gshard_capacity":
+            k = max(k, 2)  # the noisy second choice needs a second slot
+        D = int(rng.choice([128, 256, 384]))
+        F = int(rng.choice([256, 512, 768, 384]))
+        N = int(rng.integers(1, 1500))
+        N = max(1, min(N, int(budget // (k * D * F))))
+        over = dict(E=E, k=k, seed=70000 + i, name=f"random{i}_{base}_N{N}E{E}k{k}D{D}F{F}")
+        if base in ("gshard_capacity", "switch_top1"):
+            over["capacity_factor"] = float(rng.choice([0.5, 1.0, 1.25, 2.0]))
+            over["min_capacity"] = int(rng.choice([0, 4]))
+        if base != "switch_top1" and rng.random() < 0.25:
+            over["weight_dtype"] = "int8"
+        out.append(configs.scaled_config(base, N=N, D=D, F=F, **over))
+    return out
+
+
+@pytest.mark.parametrize("cfg", _random_layers(40), ids=lambda c: c["name"])
+def test_layer_random(orc, cfg):
+    _check_layer(orc, cfg)
