@@ -261,6 +261,9 @@ __device__ __forceinline__ f32x4* slot_base(const GemmParams& p, int64_t slot, i
   return reinterpret_cast<f32x4*>(p.partial) + (slot * 8 + wid) * (Frag<BM, BNF, NB, Q8>::NACC / 4) * 64;
 }
 
+// Threads per fix-up workgroup (the grid-stride loops below assume it).
+constexpr int kFixupThreads = 256;
+
 // Fix-up thread `it` of a tile: sums the 16-byte groups (one per matrix) of the slots that
 // next_slot() yields, in order, applies the epilogue and stores 4 bf16 of one row.
 template <int BM, int BNF, int NB, int ACT, bool Q8, typename Slots>
@@ -760,7 +763,7 @@ __device__ __forceinline__ void tail_reduce(const GemmParams& p, const int nslot
     if (sh.S > 1) total += sh.tail;
   }
   const int64_t items = (int64_t)total * FR::ITEMS;
-  for (int64_t gi = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; gi < items; gi += (int64_t)gridDim.x * blockDim.x) {
+  for (int64_t gi = (int64_t)blockIdx.x * kFixupThreads + threadIdx.x; gi < items; gi += (int64_t)gridDim.x * kFixupThreads) {
     int i = (int)(gi / FR::ITEMS);
     const int it = (int)(gi % FR::ITEMS);
     int x = 0;
@@ -783,7 +786,7 @@ __device__ __forceinline__ void tail_reduce(const GemmParams& p, const int nslot
   }
 }
 template <int BM, int BNF, int NB, int ACT, int BK, bool Q8>
-__global__ __launch_bounds__(256) void k_gemm_tail_reduce(const GemmParams p, int nslot) {
+__global__ __launch_bounds__(kFixupThreads) void k_gemm_tail_reduce(const GemmParams p, int nslot) {
   if (fixup_idle(p)) return;
   tail_reduce<BM, BNF, NB, ACT, BK, Q8>(p, nslot);
 }
@@ -799,7 +802,7 @@ __device__ __forceinline__ void streamk_reduce(const GemmParams& p, const int gr
   const TileScan ts = tile_scan<BM>(p);
   const SkPlan sk = sk_plan(ts.total, grid, nk);
   const int64_t items = (int64_t)(ts.total - sk.dp) * FR::ITEMS;
-  for (int64_t gi = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; gi < items; gi += (int64_t)gridDim.x * blockDim.x) {
+  for (int64_t gi = (int64_t)blockIdx.x * kFixupThreads + threadIdx.x; gi < items; gi += (int64_t)gridDim.x * kFixupThreads) {
     const int ls = (int)(gi / FR::ITEMS), it = (int)(gi % FR::ITEMS);
     const int64_t wa = sk_owner((int64_t)ls * nk, sk.W, grid), wb = sk_owner((int64_t)(ls + 1) * nk - 1, sk.W, grid);
     if (wa == wb) continue;  // stored directly by its only workgroup
@@ -819,7 +822,7 @@ __device__ __forceinline__ void streamk_reduce(const GemmParams& p, const int gr
   }
 }
 template <int BM, int BNF, int NB, int ACT, int BK, bool Q8>
-__global__ __launch_bounds__(256) void k_gemm_streamk_reduce(const GemmParams p, int grid) {
+__global__ __launch_bounds__(kFixupThreads) void k_gemm_streamk_reduce(const GemmParams p, int grid) {
   if (fixup_idle(p)) return;
   if (p.dual && skinny_wide(p, grid)) return;  // the dual skinny kernel ran whole wide tiles
   streamk_reduce<BM, BNF, NB, ACT, BK, Q8>(p, grid);
@@ -947,7 +950,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm_mixed(const GemmParams p) {
 // Fix-up of a mixed launch of G workgroups: the big share's tail pieces, then the small
 // share's stream-K partials (disjoint rows and partial slots).
 template <int ACT, int NB, int BNF_B, int BK_B, int BNF_S, int BK_S, bool Q8>
-__global__ __launch_bounds__(256) void k_gemm_mixed_reduce(const GemmParams p, int G) {
+__global__ __launch_bounds__(kFixupThreads) void k_gemm_mixed_reduce(const GemmParams p, int G) {
   if (fixup_idle(p)) return;
   const int gs = mixed_small_wgs<NB, BNF_B, BNF_S, Q8>(p, G);
   const int gb = G - gs;
@@ -998,14 +1001,14 @@ hipError_t launch_act(const GemmParams& p0, int64_t bound, hipStream_t s) {
   // Fix-up grid: at most `grid` split tiles (tail tiles < one round; stream-K tiles < G).
   auto fixup_grid = [&](int grid) {
     const int64_t threads = (bound < grid ? bound : grid) * (int64_t)FR::ITEMS;
-    const int64_t wg = (threads + 255) / 256;
+    const int64_t wg = (threads + kFixupThreads - 1) / kFixupThreads;
     return (unsigned)(wg < 2048 ? wg : 2048);
   };
   if constexpr (STREAMK) {
     // Every compute unit takes an equal share of the K slices.
     const int grid = persistent_grid(1 << 30);
     hipLaunchKernelGGL((k_gemm_bf16<BM, BNF, NB, ACT, BK, STAGES, true, Q8>), dim3(grid), dim3(512), 0, s, p);
-    hipLaunchKernelGGL((k_gemm_streamk_reduce<BM, BNF, NB, ACT, BK, Q8>), dim3(fixup_grid(grid)), dim3(256), 0, s, p,
+    hipLaunchKernelGGL((k_gemm_streamk_reduce<BM, BNF, NB, ACT, BK, Q8>), dim3(fixup_grid(grid)), dim3(kFixupThreads), 0, s, p,
                        grid);
   } else {
     const int grid = persistent_grid(bound);
@@ -1019,7 +1022,7 @@ hipError_t launch_act(const GemmParams& p0, int64_t bound, hipStream_t s) {
     if (!gathered)
       hipLaunchKernelGGL((k_gemm_bf16<BM, BNF, NB, ACT, BK, STAGES, false, Q8>), dim3(grid), dim3(512), 0, s, p);
     if (p.partial != nullptr)
-      hipLaunchKernelGGL((k_gemm_tail_reduce<BM, BNF, NB, ACT, BK, Q8>), dim3(fixup_grid(grid)), dim3(256), 0, s, p,
+      hipLaunchKernelGGL((k_gemm_tail_reduce<BM, BNF, NB, ACT, BK, Q8>), dim3(fixup_grid(grid)), dim3(kFixupThreads), 0, s, p,
                          grid / kXcds);
   }
   return hipGetLastError();
@@ -1060,10 +1063,10 @@ hipError_t launch_dual_act(const GemmParams& p0, int64_t bound, hipStream_t s) {
   using FR = Frag<64, 128, 2, false>;
   const int grid = persistent_grid(1 << 30);
   const int64_t threads = (bound < grid ? bound : grid) * (int64_t)FR::ITEMS;
-  const int64_t wg = (threads + 255) / 256;
+  const int64_t wg = (threads + kFixupThreads - 1) / kFixupThreads;
   hipLaunchKernelGGL(k_gemm_skinny_dual<ACT>, dim3(grid), dim3(512), 0, s, p);
   hipLaunchKernelGGL((k_gemm_streamk_reduce<64, 128, 2, ACT, 64, false>), dim3((unsigned)(wg < 2048 ? wg : 2048)),
-                     dim3(256), 0, s, p, grid);
+                     dim3(kFixupThreads), 0, s, p, grid);
   return hipGetLastError();
 }
 hipError_t launch_skinny_dual(const GemmParams& p, int act, int64_t bound, hipStream_t s) {
@@ -1080,11 +1083,11 @@ hipError_t launch_mixed_act(const GemmParams& p0, int64_t bound, hipStream_t s) 
   using FR = Frag<256, BNF_B, NB, Q8>;
   const int grid = persistent_grid(1 << 30);
   const int64_t threads = (bound < grid ? bound : grid) * (int64_t)FR::ITEMS;
-  const int64_t wg = (threads + 255) / 256;
+  const int64_t wg = (threads + kFixupThreads - 1) / kFixupThreads;
   hipLaunchKernelGGL((k_gemm_mixed<ACT, NB, BNF_B, BK_B, STAGES_B, BNF_S, BK_S, STAGES_S, Q8, GA>), dim3(grid),
                      dim3(512), 0, s, p);
   hipLaunchKernelGGL((k_gemm_mixed_reduce<ACT, NB, BNF_B, BK_B, BNF_S, BK_S, Q8>), dim3((unsigned)(wg < 2048 ? wg : 2048)),
-                     dim3(256), 0, s, p, grid);
+                     dim3(kFixupThreads), 0, s, p, grid);
   return hipGetLastError();
 }
 

@@ -56,6 +56,7 @@ struct TileScan {
   int incl;   // inclusive prefix (lanes >= E hold the total)
   int cnt;    // rows of expert `lane` this launch covers (0 for lanes >= E)
   int skip;   // rows of expert `lane` before the first covered row
+  int off;    // first buffer row of expert `lane` (offsets[lane])
   int total;  // number of tiles
 };
 
@@ -63,7 +64,12 @@ template <int BM>
 __device__ __forceinline__ TileScan tile_scan(const GemmParams& p) {
   const int lane = lane_id();
   TileScan s;
-  s.cnt = lane < p.E ? p.counts[lane] : 0;
+  s.cnt = 0;
+  s.off = 0;
+  if (lane < p.E) {  // both loads in flight together; tile_of needs no load of its own
+    s.cnt = p.counts[lane];
+    s.off = p.offsets[lane];
+  }
   if (s.cnt < 0) s.cnt = 0;
   s.skip = 0;
   if (p.part != 0) {
@@ -103,7 +109,7 @@ __device__ __forceinline__ bool tile_of(const GemmParams& p, const TileScan& s, 
   t.m0 = mt * BM;
   t.mcount = min(BM, cnt - t.m0);
   t.n0 = nt * BN;
-  t.row_base = (int64_t)p.offsets[e] + __shfl(s.skip, e) + t.m0;
+  t.row_base = (int64_t)__shfl(s.off, e) + __shfl(s.skip, e) + t.m0;
   if (t.row_base < 0 || t.row_base >= p.rows) return false;
   if (t.row_base + t.mcount > p.rows) t.mcount = (int)(p.rows - t.row_base);
   return true;
