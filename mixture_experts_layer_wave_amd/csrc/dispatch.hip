@@ -593,11 +593,23 @@ struct DevStats {
 __global__ __launch_bounds__(64) void k_stats(const StatsArgs a) {
   __shared__ double P_s[kMaxE];
   const int e = threadIdx.x;
-  const bool have_p = *a.psum_magic == kPsumMagic;
+  const uint32_t magic = *a.psum_magic;
+  const bool have_probs = magic == kProbsMagic && a.probs != nullptr;
+  const bool have_p = magic == kPsumMagic || have_probs;
   if (e < a.E) {
     // sum of the block sums in block order; 16 loads in flight ahead of the adds
     double s = 0.0;
-    if (have_p) {
+    if (have_probs) {
+      // token-parallel router: the 32-token block sums formed here, in token order
+      for (int64_t b = 0; b < a.nblk_r; ++b) {
+        float bs = 0.f;
+        for (int i = 0; i < kRouterTokens; ++i) {
+          const int64_t t = b * kRouterTokens + i;
+          if (t < a.N) bs += a.probs[t * a.E + e];
+        }
+        s += (double)bs;
+      }
+    } else if (have_p) {
       constexpr int U = 16;
       for (int b0 = 0; b0 < a.nblk_r; b0 += U) {
         float v[U];

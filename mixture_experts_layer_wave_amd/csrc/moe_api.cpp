@@ -131,8 +131,10 @@ int do_route_dispatch(const moe_desc* d, const void* x, const float* w_r, const 
   int rc = rows_of(d, &rows);
   if (rc) return rc;
   const RouterArgs ra = router_args(d, x, w_r, bias, noise, nullptr, nullptr, nullptr, idx, gate, scratch);
+  // (Batches the router takes token-parallel need one router launch already: then the
+  // router and the one-launch dispatch.)
   const bool fused = d->dtype == MOE_DT_BF16 && d->N <= kDispatchTokens && rows <= kSmallRows && d->E <= 16 &&
-                     d->D % kRouterChunk == 0 && ra.rpart != nullptr;
+                     d->D % kRouterChunk == 0 && ra.rpart != nullptr && !router_token_parallel(d->N, d->E);
   if (!fused) {
     rc = status_of(launch_router(ra, d->dtype == MOE_DT_BF16, st));
     if (rc) return rc;
@@ -558,6 +560,7 @@ int moe_read_stats(const moe_desc* d, const void* scratch, size_t scratch_bytes,
   StatsArgs a{};
   a.psum = at<float>(sc, s.psum);
   a.psum_magic = at<uint32_t>(sc, s.header + 64);
+  a.probs = d->dtype == MOE_DT_BF16 ? at<float>(sc, s.rpart) : nullptr;
   a.load = at<int32_t>(sc, s.load);
   a.tokdrop = at<int32_t>(sc, s.tokdrop);
   a.out = at<void>(sc, s.header);

@@ -16,6 +16,10 @@ constexpr int kSmallRows = 4096;       // most buffer rows of the fused one-laun
 constexpr int kMaxE = 64;
 constexpr int kMaxK = 8;
 constexpr uint32_t kPsumMagic = 0x5053554du;  // marks valid router partial sums
+// Marks token probabilities [N][E] left in the split-K partial region by the token-parallel
+// router (the statistics then form the 32-token block sums themselves).
+constexpr uint32_t kProbsMagic = 0x50524f42u;
+constexpr int kTokRouterTokens = 64;  // most tokens of the token-parallel router
 // Split-K partial tiles of the bf16 grouped GEMM: at most 256 workgroups, each holding
 // 8 waves x 128 fp32 accumulators x 64 lanes.
 constexpr size_t kGemmPartialUnits = 256;
@@ -97,6 +101,9 @@ struct RouterArgs {
   int noisy;  // MOE_SECOND_*: 1 = noise on slots >= 1, 2 = noise replaces the logits
 };
 hipError_t launch_router(const RouterArgs& a, bool bf16_x, hipStream_t s);
+// Whether launch_router takes the token-parallel path for bf16 x with split-K scratch (and
+// no given logits): batches of at most kTokRouterTokens tokens and at most 16 experts.
+inline bool router_token_parallel(int64_t N, int E) { return N <= kTokRouterTokens && E <= 16; }
 // Only the split-K logit kernel (bf16 x): partial logits [S][N][E] in a.rpart, S from
 // router_split(N, D); the epilogue is left to the caller.
 hipError_t launch_router_split(const RouterArgs& a, hipStream_t s);
@@ -144,6 +151,7 @@ hipError_t launch_route_dispatch_small(const RouterArgs& ra, const DispatchArgs&
 struct StatsArgs {
   const float* psum;
   const uint32_t* psum_magic;
+  const float* probs;       // [N][E] token probabilities (token-parallel router), or null
   const int32_t* load;      // scratch copy
   const int32_t* tokdrop;
   void* out;                // moe_stats in the scratch header

@@ -23,6 +23,10 @@
 //  * Single-pass path (fp32 x, routing given logits, or no scratch): a workgroup owns 32
 //    tokens, its 8 waves split D and accumulate with v_mfma_f32_32x32x2_f32; the 8
 //    partial blocks meet in LDS and are added in wave order before the epilogue.
+//  * Token-parallel path (bf16 x with scratch, at most kTokRouterTokens tokens, E <= 16):
+//    one workgroup per token forms the whole logit row with fp32 fused multiply-adds and a
+//    fixed reduction tree, then finishes the token, so a small batch needs one launch and
+//    no split-K partials (the decode regime).
 #include "moe_device.h"
 #include "moe_internal.h"
 #include "route_token.h"
@@ -388,9 +392,109 @@ __global__ __launch_bounds__(256) void k_router_epi(const RouterArgs a, RouterSp
   if (blockIdx.x == 0 && tid == 0 && a.psum_magic) *a.psum_magic = kPsumMagic;
 }
 
+// ---- token-parallel path (bf16 x, small batches) ------------------------------------
+
+// One workgroup per token. Thread i takes rows i, i + 512, ... of D (a wave reads 64
+// consecutive rows of W_r, so its loads are coalesced) and adds x[d] W_r[d][e] over them
+// with fp32 fused multiply-adds in row order; the 512 partial rows are then added in a
+// fixed tree (a xor butterfly over each wave's lanes, whose pairwise sums are equal on both
+// lanes, then the 8 waves in order), so the logits are bit-reproducible. Lanes 0..3 of
+// wave 0 finish the token with the quad epilogue and keep its probabilities in the split-K
+// partial region, from which the statistics form the 32-token block sums.
+template <int EP, int KM>
+__global__ __launch_bounds__(512) void k_router_tok(const RouterArgs a) {
+  __shared__ float red_s[kWaves][EP];
+  constexpr int U = 8;  // rows per thread whose loads are in flight together (D = 4096: all)
+  constexpr int EPL = EP / 4;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = uniform(tid >> 6);
+  const int E = a.E;
+  const int64_t t = blockIdx.x;
+  const uint16_t* xr = reinterpret_cast<const uint16_t*>(a.x) + t * a.D;
+  // the epilogue lanes' bias and noise values, requested before the logit loads (every
+  // lane loads, at a clamped index, so no wait is needed before those loads; only lanes
+  // 0..3 of wave 0 use them, for their experts below E)
+  float bz[EPL], nzl[EPL];
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) {
+    const int e = min(EPL * lane + i, E - 1);
+    bz[i] = a.bias != nullptr ? a.bias[e] : 0.f;
+    nzl[i] = a.noise != nullptr ? a.noise[t * E + e] : 0.f;
+  }
+  float acc[EP];
+#pragma unroll
+  for (int e = 0; e < EP; ++e) acc[e] = 0.f;
+  for (int d0 = tid; d0 < a.D; d0 += U * 512) {
+    float xf[U];
+    f32x4 wq[U][EP / 4];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {  // unconditional loads (rows past D re-read the last row, unused)
+      const int d = min(d0 + u * 512, a.D - 1);
+      xf[u] = __uint_as_float((uint32_t)xr[d] << 16);
+      if (E == EP) {
+#pragma unroll
+        for (int q = 0; q < EP / 4; ++q) wq[u][q] = reinterpret_cast<const f32x4*>(a.w_r + (int64_t)d * E)[q];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int d = d0 + u * 512;
+      if (d >= a.D) continue;
+      if (E == EP) {
+#pragma unroll
+        for (int e = 0; e < EP; ++e) acc[e] = fmaf(xf[u], wq[u][e / 4][e % 4], acc[e]);
+      } else {
+        const float* wrow = a.w_r + (int64_t)d * E;
+#pragma unroll
+        for (int e = 0; e < EP; ++e)
+          if (e < E) acc[e] = fmaf(xf[u], wrow[e], acc[e]);
+      }
+    }
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1)
+#pragma unroll
+    for (int e = 0; e < EP; ++e) acc[e] += __shfl_xor(acc[e], off);
+  if (lane == 0) {
+#pragma unroll
+    for (int e = 0; e < EP; ++e) red_s[w][e] = acc[e];
+  }
+  __syncthreads();
+  if (w != 0 || lane >= 4) return;
+  const int part = lane;
+  float l[EPL], p[EPL];
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) {
+    const int e = EPL * part + i;
+    float v = 0.f;
+    if (e < E) {
+      v = red_s[0][e];
+#pragma unroll
+      for (int ww = 1; ww < kWaves; ++ww) v += red_s[ww][e];
+      if (a.bias != nullptr) v += bz[i];
+    }
+    l[i] = v;
+  }
+  int sel[kMaxK];
+  float gt[kMaxK];
+  route_token_quad<EPL, KM>(a, t, part, true, nzl, l, p, sel, gt);
+  if (part == 0) store_topk<KM>(a, t, sel, gt);
+#pragma unroll
+  for (int i = 0; i < EPL; ++i)
+    if (EPL * part + i < E) a.rpart[t * E + EPL * part + i] = p[i];
+  if (t == 0 && part == 0 && a.psum_magic) *a.psum_magic = kProbsMagic;
+}
+
 // KM: compile-time bound on k for the token epilogue (2 covers the common top-1 / top-2).
 template <int NT, int EP, int KM>
 hipError_t launch_epk(const RouterArgs& a, bool bf16_x, hipStream_t s) {
+  if constexpr (EP <= 16) {
+    if (bf16_x && a.logits_in == nullptr && a.rpart != nullptr && router_token_parallel(a.N, a.E)) {
+      hipLaunchKernelGGL((k_router_tok<EP, KM>), dim3((unsigned)a.N), dim3(512), 0, s, a);
+      return hipGetLastError();
+    }
+  }
   if (bf16_x && a.logits_in == nullptr && a.rpart != nullptr && a.D % kRouterChunk == 0) {
     const RouterSplit rs = router_split(a.N, a.D);
     hipLaunchKernelGGL((k_router_split<NT>), dim3((unsigned)(rs.tiles * rs.S)), dim3(512), 0, s, a, rs);

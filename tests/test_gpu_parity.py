@@ -79,13 +79,16 @@ def test_route_from_identical_logits(orc, N, E, k, dist, mode, noisy):
 
 
 @pytest.mark.parametrize("N,E,k", [(300, 64, 2), (300, 40, 8), (97, 64, 1), (300, 33, 3), (1000, 16, 2),
-                                   (300, 8, 2), (65, 4, 3), (200, 5, 2), (129, 24, 4)])
+                                   (300, 8, 2), (65, 4, 3), (200, 5, 2), (129, 24, 4),
+                                   # at most 64 tokens and 16 experts: the token-parallel router
+                                   (64, 8, 2), (1, 8, 2), (37, 16, 8), (64, 5, 2), (50, 12, 3), (64, 16, 1)])
 @pytest.mark.parametrize("mode", ["softmax_topk", "topk_softmax"])
 @pytest.mark.parametrize("noisy", [False, "second", "all"])
 def test_route_split_epilogue(orc, N, E, k, mode, noisy):
-    """The split-K router's own epilogue (bf16 x with scratch; four lanes per token, each
-    with E / 4 experts) against the oracle routing the logits that router produced:
-    identical selection, gates and probabilities within fp32 rounding."""
+    """The bf16 router's own epilogue (x bf16 with scratch: the split-K router, or for at
+    most 64 tokens and 16 experts the token-parallel one; four lanes per token, each with
+    E / 4 experts) against the oracle routing the logits that router produced: identical
+    selection, gates and probabilities within fp32 rounding."""
     if noisy == "second" and k < 2:
         pytest.skip("noisy second choice needs k >= 2")
     cfg = _routing_cfg(N, E, k, mode, noisy, D=256)
@@ -117,11 +120,13 @@ def test_route_split_epilogue(orc, N, E, k, mode, noisy):
                                       ("grok1_layer", 129, 6144), ("gshard_capacity", 1000, 2048),
                                       ("mixtral_decode", 64, 4096), ("mixtral_decode", 1, 4096),
                                       ("gshard_capacity", 4097, 128), ("switch_top1", 257, 2048),
+                                      ("switch_top1", 33, 2048),
                                       ("mixtral_prefill", 70000, 256)])
 @pytest.mark.parametrize("scratch", [False, True], ids=["single_pass", "split_k"])
 def test_router_logits(orc, name, N, D, scratch):
     """fp32 router logits against the exact ones: the single-pass fp32 MFMA path (no
-    scratch) and, for bf16 x, the split-K path with W_r split into three bf16 pieces."""
+    scratch) and, for bf16 x, the split-K path with W_r split into three bf16 pieces, or for
+    at most 64 tokens and 16 experts the token-parallel path (fp32 fused multiply-adds)."""
     # clean logits (under noisy top-k gating logits_out would report logit + noise)
     cfg = configs.scaled_config(name, N=N, D=D, F=128, second_choice="topk")
     inp = inputs.make_inputs(cfg, weights=False)
@@ -696,7 +701,12 @@ def test_layer_bitwise_reproducible_and_equal_to_steps(orc, cfg):
                                  configs.scaled_config("gshard_capacity", N=200, D=256, F=384, E=16,
                                                        name="gshard_capacity_fused_dispatch"),
                                  configs.scaled_config("mixtral_prefill", N=333, D=256, F=512),
-                                 configs.scaled_config("switch_top1", N=1000, D=256, F=384)],
+                                 configs.scaled_config("switch_top1", N=1000, D=256, F=384),
+                                 # token-parallel router: the block sums formed from the
+                                 # probabilities it leaves in scratch
+                                 configs.scaled_config("mixtral_decode", N=64, D=256, F=384),
+                                 configs.scaled_config("gshard_capacity", N=48, D=256, F=384, E=16,
+                                                       name="gshard_capacity_n48")],
                          ids=lambda c: c["name"])
 def test_stats(orc, cfg):
     res = _check_layer(orc, cfg)
