@@ -80,7 +80,7 @@ def parse_kernel(name: str):
 
 def stage_of(name: str) -> str:
     base, args = parse_kernel(name)
-    if base in ("k_router", "k_router_split", "k_router_epi"):
+    if base in ("k_router", "k_router_split", "k_router_epi", "k_router_tok"):
         return "route"
     if base in ("k_dispatch_count", "k_dispatch_scan", "k_dispatch_assign", "k_gather", "k_dispatch_small"):
         return "dispatch"

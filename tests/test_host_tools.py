@@ -45,6 +45,7 @@ def test_bench_refuses_more_than_one_gpu():
     ("void moe::(anonymous namespace)::k_router_epi<8>(moe::RouterArgs, moe::RouterSplit)", "k_router_epi", [8],
      "route"),
     ("k_route_dispatch_small<8>", "k_route_dispatch_small", [8], "forward"),
+    ("void moe::(anonymous namespace)::k_router_tok<8, 2>(moe::RouterArgs)", "k_router_tok", [8, 2], "route"),
     ("k_dispatch_small", "k_dispatch_small", [], "dispatch"),
     ("void moe::(anonymous namespace)::k_combine<__bf16>(moe::CombineArgs, int)", "k_combine", [], "combine"),
     ("__amd_rocclr_copyBuffer", "__amd_rocclr_copyBuffer", [], "other"),
