@@ -210,8 +210,12 @@ MOE_API int moe_workspace_layout(const moe_desc* desc, moe_ws_layout* layout);
  *   probs_out  [N,E] fp32        optional output of softmax over all E
  *   topk_idx   [N,k] int32       required output, expert of each slot
  *   topk_gate  [N,k] fp32        required output, gate of each slot
- *   scratch    moe_scratch_size  optional (NULL = skip); receives per-block partial sums
- *                                of the probabilities for the balance statistic. */
+ *   scratch    moe_scratch_size  optional (NULL = skip); receives the probabilities'
+ *                                sums per 32-token block for the balance statistic (for
+ *                                bf16 x and at most 64 tokens and 16 experts, the
+ *                                probabilities themselves, which moe_read_stats adds up
+ *                                in the same blocks), and with bf16 x the working data of
+ *                                the logit GEMM. */
 MOE_API int moe_route(const moe_desc* desc, const void* x, const float* w_r, const float* logit_bias,
               const float* noise, const float* logits_in, float* logits_out, float* probs_out,
               int32_t* topk_idx, float* topk_gate, void* scratch, size_t scratch_bytes,
