@@ -844,3 +844,30 @@ def _random_layers(n, seed=20261204, budget=1.2e8):
 @pytest.mark.parametrize("cfg", _random_layers(40), ids=lambda c: c["name"])
 def test_layer_random(orc, cfg):
     _check_layer(orc, cfg)
+
+
+def _random_small_batches(n, seed=20261205):
+    """Seeded layers of at most 64 tokens (the decode regime: token-parallel router for
+    E <= 16, one-launch dispatch, skinny GEMM tiles), across the routing recipes."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        base = ["mixtral_decode", "gshard_capacity", "switch_top1", "grok1_layer"][i % 4]
+        E = int(rng.choice([2, 4, 5, 8, 12, 16, 16, 32]))
+        k = 1 if base == "switch_top1" else int(rng.integers(2 if base == "gshard_capacity" else 1, min(E, 4) + 1))
+        D = int(rng.choice([128, 256, 384]))
+        F = int(rng.choice([256, 384, 512]))
+        N = int(rng.integers(1, 65))
+        over = dict(E=E, k=k, seed=80000 + i, name=f"small{i}_{base}_N{N}E{E}k{k}D{D}F{F}")
+        if base in ("gshard_capacity", "switch_top1"):
+            over["capacity_factor"] = float(rng.choice([0.5, 1.0, 1.25, 2.0]))
+            over["min_capacity"] = int(rng.choice([0, 4]))
+        if base in ("mixtral_decode", "grok1_layer") and rng.random() < 0.3:
+            over["weight_dtype"] = "int8"
+        out.append(configs.scaled_config(base, N=N, D=D, F=F, **over))
+    return out
+
+
+@pytest.mark.parametrize("cfg", _random_small_batches(24), ids=lambda c: c["name"])
+def test_layer_random_small_batch(orc, cfg):
+    _check_layer(orc, cfg)
