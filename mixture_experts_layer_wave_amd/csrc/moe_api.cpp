@@ -117,7 +117,8 @@ int do_route(const moe_desc* d, const void* x, const float* w_r, const float* bi
 
 // Router of the forward pass followed by its dispatch. A batch of at most kDispatchTokens
 // tokens with bf16 x (E <= 16, buffer of at most kSmallRows rows) takes two launches: the
-// split-K logit kernel, then one kernel that finishes the routing and dispatches.
+// split-K logit kernel, then one kernel that finishes the routing and dispatches; or, for
+// at most kTokRouterTokens tokens, the token-parallel router, then the one-launch dispatch.
 int do_dispatch(const moe_desc* d, const void* x, const int32_t* idx, const float* gate, int32_t* load,
                 int32_t* counts, int32_t* offsets, int32_t* row_of, uint8_t* dropped, float* gate_eff,
                 int32_t* token_of_row, void* x_perm, void* scratch, hipStream_t st,
